@@ -19,7 +19,10 @@ Recipe (the same for every consumer):
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
+import os
+
 import numpy as np
 
 BF16_NAN_BITS = np.uint16(0x7FC0)
@@ -115,6 +118,25 @@ class DecodeCase:
     def seq_bits(self, tensor_id: int, b: int, n: int) -> np.ndarray:
         """[Hkv, n, D] rows of sequence b (n = that sequence's length)."""
         return normal_bf16_bits((self.Hkv, n, self.D), [self.wid, tensor_id, self.variant, b])
+
+    def iter_seqs(self, lens: np.ndarray | None = None, workers: int | None = None):
+        """Yield (b, n, k_bits [Hkv,n,D], v_bits [Hkv,n,D]) in order of b.
+
+        Sequences are drawn on a thread pool, a few at a time, so that only
+        a bounded number of them is held in memory.
+        """
+        lens = self.kv_lens() if lens is None else lens
+        workers = workers or min(16, os.cpu_count() or 1)
+
+        def one(b):
+            n = int(min(max(int(lens[b]), 0), self.Lmax))
+            if n == 0:
+                return b, 0, None, None
+            return b, n, self.seq_bits(K_ID, b, n), self.seq_bits(V_ID, b, n)
+
+        with ThreadPoolExecutor(workers) as ex:
+            for s0 in range(0, self.B, workers):
+                yield from ex.map(one, range(s0, min(self.B, s0 + workers)))
 
     def cache_bits(self, tensor_id: int, lens: np.ndarray | None = None) -> np.ndarray:
         """Full [B, Hkv, Lmax, D] cache; rows past each length are NaN."""

@@ -1,0 +1,265 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one causal prefill of a Qwen3-8B-shaped layer at 16,384 tokens
+(B=1, Hq=32, Hkv=8, D=128) followed by one ragged GQA decode over 64 cached
+sequences (lengths uniform in [1024, 32768], same heads).  Inputs are
+synthetic, seeded, and resident in HBM before timing starts.
+
+Printed: one JSON line.  `value` is the prefill's causal TFLOP/s (FLOPs =
+4*B*Hq*D*visible (query, key) pairs of the bottom-right mask, divided by the
+prefill kernel's mean duration from HIP events on its stream); the decode's
+KV-read GB/s (bytes = sum of lengths * Hkv * D * 2 tensors * 2 B over the
+split + combine duration, MALL flushed before each decode) is reported beside
+it with its own roofline.  `cpu_baseline` times the CPU oracle on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import attn_inputs as ai  # noqa: E402
+
+METRIC = "prefill causal TFLOP/s + decode KV GB/s (Qwen3-8B heads), % of roofline, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+FLUSH_BYTES = 512 << 20        # > the 256 MB Infinity Cache
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU seconds per oracle sample")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_attention_30_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, src_hash: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("#") or "=" not in line:
+            continue
+        k, v = (x.strip() for x in line.split("=", 1))
+        vals[k] = v
+    if vals.get("source_hash") != src_hash:
+        return None
+    try:
+        return float(vals[f"{kernel}.hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def to_dev(bits, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def build_decode_cache(case: ai.DecodeCase, lens, dev):
+    import torch
+    shape = (case.B, case.Hkv, case.Lmax, case.D)
+    kc = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    for b, n, kb, vb in case.iter_seqs(lens):
+        if n:
+            kc[b, :, :n] = to_dev(kb, dev)
+            vc[b, :, :n] = to_dev(vb, dev)
+    return kc, vc
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return os.cpu_count() or 1
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def cpu_prefill_baseline(case: ai.PrefillCase, qb, kb, vb, seconds: float):
+    """The oracle's row mode on sampled query rows of the same prefill.
+
+    Rows are drawn per head; the rate is (4*D*visible keys of the rows
+    computed) / CPU seconds, in TFLOP/s."""
+    import oracle
+    q = ai.bf16_bits_to_f64(qb)
+    k = ai.bf16_bits_to_f64(kb)
+    v = ai.bf16_bits_to_f64(vb)
+    off = case.Lk - case.Lq
+    R = 2
+    spent, flops, rows_done = 0.0, 0.0, 0
+    while spent < seconds:
+        rows = np.stack([np.stack([ai.sample_rows(case.Lq, R, [case.wid, 99, R, h]) for h in range(case.Hq)])])
+        t = time.perf_counter()
+        oracle.attention_rows(q, k, v, rows, True, case.scale)
+        dt = time.perf_counter() - t
+        spent += dt
+        flops += 4.0 * case.D * float(np.sum(rows + off + 1))
+        rows_done += rows.size
+        R = min(case.Lq, R * 2)
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{rows_done} query rows (sampled per head, all 32 heads) of the L=16384 causal prefill, "
+                      f"fp64 numpy row mode, {spent:.1f} s", "cpu": cpu_model()}
+
+
+def cpu_decode_baseline(case: ai.DecodeCase, lens, seconds: float):
+    import oracle
+    q = ai.bf16_bits_to_f64(case.q_bits())
+    spent, nbytes, seqs = 0.0, 0, 0
+    for b, n, kb, vb in case.iter_seqs(lens, workers=4):
+        if n == 0:
+            continue
+        k64, v64 = ai.bf16_bits_to_f64(kb)[None], ai.bf16_bits_to_f64(vb)[None]
+        t = time.perf_counter()
+        oracle.decode(q[b:b + 1], k64, v64, np.array([n]), case.scale)
+        spent += time.perf_counter() - t
+        nbytes += n * case.Hkv * case.D * 2 * 2
+        seqs += 1
+        if spent >= seconds:
+            break
+    return {"value": nbytes / spent / 1e9, "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"first {seqs} of the 64 ragged sequences, fp64 numpy, {spent:.1f} s (KV bytes counted as bf16)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU split is described in DESIGN.md, not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import exact_attention_30_amd as attn
+    from oracle import accounting as acc
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # ---- inputs (resident before timing) ------------------------------------
+    pc = ai.QWEN_16K
+    qb, kb, vb = pc.q_bits(), pc.k_bits(), pc.v_bits()
+    q, k, v = to_dev(qb, dev), to_dev(kb, dev), to_dev(vb, dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((pc.B, pc.Hq, pc.Lq), dtype=torch.float32, device=dev)
+    pflops = acc.prefill_flops(pc.B, pc.Hq, pc.D, pc.Lq, pc.Lk, True)
+
+    dc = ai.RAGGED_DECODE
+    lens = dc.kv_lens()
+    kc, vc = build_decode_cache(dc, lens, dev)
+    dq = to_dev(dc.q_bits(), dev)
+    dlens = torch.from_numpy(lens).to(dev)
+    dout = torch.empty_like(dq)
+    dbytes = acc.decode_kv_bytes(lens, dc.Hkv, dc.D, dc.Lmax)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i, evs=None):
+        if evs:
+            evs[0].record(stream)
+        attn.prefill(q, k, v, causal=True, scale=pc.scale, out=out, lse=lse)
+        if evs:
+            evs[1].record(stream)
+        flush.fill_(i & 0xFF)
+        if evs:
+            evs[2].record(stream)
+        attn.decode(dq, kc, vc, dlens, scale=dc.scale, out=dout)
+        if evs:
+            evs[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    dec_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    tflops = pflops / (pre_ms * 1e-3) / 1e12
+    gbps = dbytes / (dec_ms * 1e-3) / 1e9
+
+    src = kernel_source_hash()
+    ptraffic = read_traffic("prefill", src)
+    dtraffic = read_traffic("decode", src)
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "causal prefill L=16384 + ragged GQA decode B=64 (Qwen3-8B heads: Hq=32, Hkv=8, D=128)",
+            "prefill": {"B": pc.B, "Hq": pc.Hq, "Hkv": pc.Hkv, "Lq": pc.Lq, "Lk": pc.Lk, "D": pc.D,
+                        "causal": True, "flops": pflops, "ms": round(pre_ms, 4)},
+            "decode": {"B": dc.B, "Hq": dc.Hq, "Hkv": dc.Hkv, "Lmax": dc.Lmax, "D": dc.D,
+                       "lens": "uniform [1024, 32768] seeded", "sum_lens": int(lens.sum()),
+                       "kv_bytes": dbytes, "split_keys": attn.decode_split_keys(dc.B, dc.Hkv, dc.Lmax),
+                       "ms": round(dec_ms, 4), "mall_flushed": True},
+            "parallelism": "single GPU",
+        },
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel<128,64>", "achieved": round(tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": ptraffic},
+        "decode": {"value": round(gbps, 1), "unit": "GB/s",
+                   "roofline": {"bound": "hbm", "kernel": "decode_split_kernel<128,1> + decode_combine_kernel<128>",
+                                "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": dtraffic}},
+        "kernel_source_hash": src,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_prefill_baseline(pc, qb, kb, vb, args.cpu_seconds)
+        rec["decode"]["cpu_baseline"] = cpu_decode_baseline(dc, lens, args.cpu_seconds * 0.5)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,163 @@
+"""Exact GQA attention for MI355X: a thin ctypes binding over libattn.so.
+
+The functions here only check tensors and marshal pointers; every step of the
+computation runs in the HIP kernels of libattn.so (see include/attn.h for the
+contract).  PyTorch provides device memory and the current stream.  If the
+library has not been built, importing this package raises ImportError: there
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_OK = 0
+STATUS_NAMES = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_HEADDIM",
+                -4: "ATTN_ERR_GQA", -5: "ATTN_ERR_SCALE", -6: "ATTN_ERR_HIP", -7: "ATTN_ERR_SPLIT",
+                -8: "ATTN_ERR_WORKSPACE"}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "(python exact_attention_30_amd/build.py)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_prefill.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    lib.attn_prefill.restype = i
+    lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    lib.attn_decode.restype = i
+    lib.attn_decode_ex.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.attn_decode_ex.restype = i
+    lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.attn_decode_workspace_bytes.restype = sz
+    lib.attn_decode_split_keys.argtypes = [i, i, i]
+    lib.attn_decode_split_keys.restype = i
+    lib.attn_status_string.argtypes = [i]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {lib.attn_status_string(status).decode()}")
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        raise AttnError(status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, dim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def default_scale(D: int) -> float:
+    return float(torch.tensor(1.0 / math.sqrt(D), dtype=torch.float32).item())
+
+
+def prefill(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=None,
+            return_lse: bool = True):
+    """attn_prefill: q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D] bf16 -> (out bf16, lse fp32 or None)."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    if v.shape != k.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.bfloat16, 4)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 3)
+        if tuple(lse.shape) != (B, Hq, Lq):
+            raise ValueError("lse must be [B,Hq,Lq]")
+    scale = default_scale(D) if scale is None else float(scale)
+    _check(lib.attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Lq, Lk, D,
+                            1 if causal else 0, ctypes.c_float(scale), _stream(q.device)))
+    return out, lse
+
+
+def decode(q, kcache, vcache, kv_lens, scale: float | None = None, out=None):
+    """attn_decode: q [B,Hq,D], caches [B,Hkv,Lmax,D] bf16, kv_lens [B] int32 -> out [B,Hq,D] bf16."""
+    B, Hq, Hkv, Lmax, D = _decode_shapes(q, kcache, vcache, kv_lens)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.bfloat16, 3)
+    scale = default_scale(D) if scale is None else float(scale)
+    _check(lib.attn_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(kv_lens), _ptr(out), B, Hq, Hkv, Lmax, D,
+                           ctypes.c_float(scale), _stream(q.device)))
+    return out
+
+
+def decode_ex(q, kcache, vcache, kv_lens, scale: float | None = None, split_keys: int = 0, out=None,
+              return_lse: bool = True, workspace=None):
+    """attn_decode_ex: decode plus lse [B,Hq] fp32, a chunk-size override and an optional workspace."""
+    B, Hq, Hkv, Lmax, D = _decode_shapes(q, kcache, vcache, kv_lens)
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if return_lse else None
+    scale = default_scale(D) if scale is None else float(scale)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.attn_decode_ex(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(kv_lens), _ptr(out), _ptr(lse), B, Hq,
+                              Hkv, Lmax, D, ctypes.c_float(scale), int(split_keys), _ptr(workspace), ws_bytes,
+                              _stream(q.device)))
+    return out, lse
+
+
+def decode_workspace_bytes(B, Hq, Hkv, Lmax, D, split_keys=0) -> int:
+    return int(lib.attn_decode_workspace_bytes(B, Hq, Hkv, Lmax, D, split_keys))
+
+
+def decode_split_keys(B, Hkv, Lmax) -> int:
+    return int(lib.attn_decode_split_keys(B, Hkv, Lmax))
+
+
+def _decode_shapes(q, kcache, vcache, kv_lens):
+    _need(q, "q", torch.bfloat16, 3)
+    _need(kcache, "kcache", torch.bfloat16, 4)
+    _need(vcache, "vcache", torch.bfloat16, 4)
+    _need(kv_lens, "kv_lens", torch.int32, 1)
+    B, Hq, D = q.shape
+    Hkv, Lmax = kcache.shape[1], kcache.shape[2]
+    if vcache.shape != kcache.shape or kcache.shape[0] != B or kcache.shape[3] != D or kv_lens.shape[0] != B:
+        raise ValueError("shape mismatch between q, caches and kv_lens")
+    return B, Hq, Hkv, Lmax, D
+
+
+__all__ = ["prefill", "decode", "decode_ex", "decode_workspace_bytes", "decode_split_keys", "AttnError", "lib",
+           "LIB_PATH", "default_scale"]

@@ -1,0 +1,54 @@
+// Shared device helpers for the gfx950 attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define ATTN_DEV __device__ __forceinline__
+
+// log2(e) in fp32: exp(x) = exp2(x * log2(e)); ln(2) for the way back.
+#define ATTN_LOG2E 1.4426950408889634f
+#define ATTN_LN2 0.6931471805599453f
+
+// A row's running maximum is only raised when a tile's maximum exceeds it by
+// more than this many powers of two; until then the exponentials may reach
+// 2^ATTN_RESCALE_SLACK, which fp32 sums and bf16 weights hold without loss of
+// relative precision.  The final normalisation uses the same reference, so the
+// result is unchanged (up to rounding).
+#define ATTN_RESCALE_SLACK 8.0f
+
+ATTN_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Lane-pair exchange across the two halves of a wave64 (lane l <-> l ^ 32).
+ATTN_DEV float xor32(float x) { return __shfl_xor(x, 32); }
+ATTN_DEV float xor16(float x) { return __shfl_xor(x, 16); }
+
+ATTN_DEV bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// Pack two bf16 values held in the low halves (lo16) or high halves (hi16)
+// of two 32-bit words into one word: first operand in the low half.
+ATTN_DEV uint32_t pack_lo16(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+ATTN_DEV uint32_t pack_hi16(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+// 16-byte global load / store helpers.
+ATTN_DEV u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+ATTN_DEV void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+
+ATTN_DEV bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+ATTN_DEV bf16x8 pack8(float a0, float a1, float a2, float a3, float a4, float a5, float a6, float a7) {
+  bf16x8 r;
+  r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
+  r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
+  return r;
+}
+
+ATTN_DEV float fmax3(float a, float b, float c) { return __builtin_fmaxf(a, __builtin_fmaxf(b, c)); }
+ATTN_DEV float fmin3(float a, float b, float c) { return __builtin_fminf(a, __builtin_fminf(b, c)); }

@@ -1,0 +1,48 @@
+// Launch arguments shared by the kernel files and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct PrefillArgs {
+  const uint16_t *q;
+  const uint16_t *k;
+  const uint16_t *v;
+  uint16_t *out;
+  float *lse;
+  int B, Hq, Hkv, Lq, Lk;
+  int G;       // Hq / Hkv
+  int hpw;     // query heads per workgroup (divides G and the 4 waves)
+  int wph;     // waves per head = 4 / hpw
+  int Bq;      // query rows per head per workgroup = 32 * wph
+  int n_qblk;  // ceil(Lq / Bq)
+  int n_hg;    // head groups per KV head = G / hpw
+  int total;   // workgroups in the grid
+  int causal;
+  float c;     // scale * log2(e)
+};
+
+struct DecodeArgs {
+  const uint16_t *q;
+  const uint16_t *kc;
+  const uint16_t *vc;
+  const int32_t *lens;
+  uint16_t *out;
+  float *lse;
+  float *part_o;    // [B][Hq][nsplit][D] normalised partial outputs
+  float *part_lse;  // [B][Hq][nsplit]
+  int B, Hq, Hkv, Lmax;
+  int G;            // Hq / Hkv
+  int n_hg;         // groups of up to 64 query heads per KV head
+  int split;        // keys per chunk
+  int nsplit;       // ceil(Lmax / split)
+  float c;          // scale * log2(e)
+};
+
+hipError_t launch_prefill(const PrefillArgs &a, int D, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, int D, hipStream_t s);
+
+}  // namespace attn

@@ -1,0 +1,156 @@
+/*
+ * attn.h -- C ABI of libattn.so: exact grouped-query scaled-dot-product
+ * attention on AMD Instinct MI355X (gfx950), prefill and single-token decode.
+ *
+ * What is computed (all entry points):
+ *   for batch b, query head h (KV head h / G with G = Hq / Hkv, consecutive
+ *   query heads sharing one KV head), query row i:
+ *     s_ij  = scale * <q_i, k_j>                 over the visible keys j
+ *     lse_i = ln sum_j exp(s_ij)                 (natural log)
+ *     out_i = sum_j exp(s_ij - lse_i) * v_j
+ *   The Lq x Lk score table is never written to memory: keys are consumed in
+ *   tiles with a running row maximum and row sum (an online softmax), which
+ *   gives the same result up to rounding order.
+ *
+ * Sources (pages, by title):
+ *   "어텐션 구현 고르기, SDPA·FlashAttention 메모리와 GPU 비용"
+ *     (tool.smithlab.co.kr) -- section "어텐션 구현 종류와 차이 한눈에 보기"
+ *     (all implementations compute the same values; flash kernels take
+ *     fp16/bf16 and head dim up to 256), section "eager 어텐션 메모리, 길이에
+ *     따라 얼마나 커지나" (the tiled method keeps only per-row max and sum
+ *     statistics, memory linear in length, no approximation), section
+ *     "is_causal 마스크 정렬, KV 캐시와 쓸 때의 함정" (causal mask anchored at
+ *     the bottom-right corner when there are fewer queries than keys; a
+ *     single decode query attends to the whole cache with no mask);
+ *   "Как NVIDIA учит нейросети думать быстрее: оптимизация внимания для
+ *     длинных контекстов" (iphoneandroid24.ru) -- section "Параметр первый:
+ *     размер группы (group size)" (G query heads share one KV head), section
+ *     "Параметр второй: размерность головы" (head dims 64/128/256), section
+ *     "Параметр четвёртый: параллелизм…" (a long KV cache split into parts
+ *     whose partial results are merged).
+ *
+ * Conventions shared by every entry point:
+ *   - Element types: q, k, v, kcache, vcache and out are bfloat16 (passed as
+ *     void*); lse is float32; kv_lens is int32.  Arithmetic: fp32
+ *     accumulation and fp32 softmax statistics.
+ *   - Layouts are dense and row-major (last index fastest):
+ *       prefill q/out [B][Hq][Lq][D], k/v [B][Hkv][Lk][D], lse [B][Hq][Lq];
+ *       decode q/out [B][Hq][D], kcache/vcache [B][Hkv][Lmax][D],
+ *       kv_lens [B], lse [B][Hq].
+ *   - Every pointer is device memory owned by the caller, 16-byte aligned.
+ *     Inputs are read only; outputs are written only.  Inputs and outputs
+ *     must not overlap.
+ *   - D must be 64, 128 or 256; Hq must be a multiple of Hkv.
+ *   - scale multiplies q.k in fp32 (pass 1/sqrt(D) for the usual scaling);
+ *     it must be finite; 0 gives uniform weights.
+ *   - stream is a hipStream_t (NULL = the default stream).  Calls are
+ *     asynchronous: they enqueue work and return.  Argument errors are
+ *     reported before anything is enqueued; device faults show up at the
+ *     caller's next synchronisation.
+ *   - Errors are returned as negative attn_status codes; nothing is thrown
+ *     across the ABI; the library keeps no state between calls apart from
+ *     HIP's stream-ordered memory pool used by attn_decode.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,     /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = -2,    /* a negative size, Lk = 0 with Lq > 0, causal with Lq > Lk,
+                             Lmax < 1, or a size whose element count overflows */
+  ATTN_ERR_HEADDIM = -3,  /* D not in {64, 128, 256} */
+  ATTN_ERR_GQA = -4,      /* Hq < 1, Hkv < 1 or Hq % Hkv != 0 */
+  ATTN_ERR_SCALE = -5,    /* scale is NaN or infinite */
+  ATTN_ERR_HIP = -6,      /* a HIP call or kernel launch failed */
+  ATTN_ERR_SPLIT = -7,    /* split_keys not 0 and not a positive multiple of 128 */
+  ATTN_ERR_WORKSPACE = -8 /* workspace given but smaller than attn_decode_workspace_bytes() */
+} attn_status;
+
+/*
+ * attn_prefill -- causal or full attention of Lq query rows over Lk keys.
+ *
+ * Pages: the cost guide's sections on the tiled method and on is_causal
+ * alignment (above).  causal != 0 applies the bottom-right-aligned mask:
+ * query row i sees key j iff j <= i + (Lk - Lq).  That is the only causal
+ * alignment offered; with Lq == Lk it is the usual lower triangle, and with
+ * Lq < Lk (chunked prefill, several new rows over a cache) each row sees the
+ * cache plus the new rows up to itself.  causal with Lq > Lk is rejected
+ * (ATTN_ERR_SHAPE): such rows would see no key.
+ *
+ *   q   [B][Hq][Lq][D] bf16      k, v [B][Hkv][Lk][D] bf16
+ *   out [B][Hq][Lq][D] bf16      lse  [B][Hq][Lq] fp32, may be NULL
+ *
+ * B == 0 or Lq == 0 is an empty call: ATTN_OK, nothing is read, written or
+ * enqueued, and the pointers may be NULL (the other arguments are still
+ * checked).
+ * Returns ATTN_OK or a negative attn_status.
+ */
+int attn_prefill(const void *q, const void *k, const void *v, void *out, float *lse,
+                 int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, float scale,
+                 void *stream);
+
+/*
+ * attn_decode -- one new query row per sequence over a ragged KV cache.
+ *
+ * Pages: the cost guide's is_causal section (the new token's K/V are already
+ * in the cache and the single query attends to all cached keys with no mask)
+ * and the NVIDIA page's parallelism section (KV split into parts, partial
+ * results merged).  Sequence b uses keys [0, n_b) of its cache rows, with
+ * n_b = min(kv_lens[b], Lmax) (negative lengths count as 0); the rows past
+ * n_b are never read.  n_b == 0 gives out = 0.
+ *
+ *   q       [B][Hq][D] bf16           out [B][Hq][D] bf16
+ *   kcache, vcache [B][Hkv][Lmax][D] bf16
+ *   kv_lens [B] int32, device memory (read on the device only)
+ *
+ * The keys are split into chunks processed in parallel; each chunk yields a
+ * partial output and log-sum-exp, merged by a second kernel.  The partials
+ * live in a workspace taken from HIP's stream-ordered allocator on `stream`
+ * and released on it.  B == 0 is an empty call (ATTN_OK; pointers may be
+ * NULL).
+ */
+int attn_decode(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens,
+                void *out, int B, int Hq, int Hkv, int Lmax, int D, float scale, void *stream);
+
+/*
+ * attn_decode_ex -- attn_decode with three extra controls:
+ *   lse        [B][Hq] fp32 output (natural log; -inf where n_b == 0), may be NULL;
+ *   split_keys keys per chunk: 0 picks a size from B, Hkv and Lmax; otherwise a
+ *              positive multiple of 128 (else ATTN_ERR_SPLIT);
+ *   workspace  caller-owned device buffer of workspace_bytes for the partials;
+ *              NULL takes it from the stream-ordered allocator as attn_decode
+ *              does.  If non-NULL it must hold at least
+ *              attn_decode_workspace_bytes(...) bytes (else ATTN_ERR_WORKSPACE)
+ *              and must not be used by other work until this call's kernels
+ *              have finished on `stream`.
+ */
+int attn_decode_ex(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens,
+                   void *out, float *lse, int B, int Hq, int Hkv, int Lmax, int D, float scale,
+                   int split_keys, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * attn_decode_workspace_bytes -- bytes of workspace attn_decode_ex needs for
+ * these sizes and split_keys (0 = the automatic choice).  Returns 0 for an
+ * empty call and for invalid arguments.
+ */
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Lmax, int D, int split_keys);
+
+/* attn_decode_split_keys -- the chunk size attn_decode picks for these sizes. */
+int attn_decode_split_keys(int B, int Hkv, int Lmax);
+
+/* attn_status_string -- static, NUL-terminated text for a status code. */
+const char *attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

@@ -1,0 +1,113 @@
+"""Host-side checks of libattn.so: it loads, exports what include/attn.h
+declares, and rejects bad arguments before touching the GPU.  No kernel is
+launched here (these run without a GPU)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def attn():
+    import exact_attention_30_amd as m
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(attn):
+    names = declared_functions()
+    assert {"attn_prefill", "attn_decode", "attn_decode_ex", "attn_status_string"} <= set(names)
+    lib = ctypes.CDLL(attn.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(attn):
+    for code in range(0, -9, -1):
+        s = attn.lib.attn_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert attn.lib.attn_status_string(-99).decode() == "unknown status"
+
+
+P = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+N = None
+
+
+def prefill(attn, q=P, k=P, v=P, out=P, lse=N, B=1, Hq=4, Hkv=2, Lq=8, Lk=8, D=128, causal=1, scale=0.125):
+    return attn.lib.attn_prefill(q, k, v, out, lse, B, Hq, Hkv, Lq, Lk, D, causal, ctypes.c_float(scale), None)
+
+
+def test_prefill_validation(attn):
+    assert prefill(attn, q=N) == -1
+    assert prefill(attn, out=N) == -1
+    assert prefill(attn, Hq=6, Hkv=4) == -4
+    assert prefill(attn, Hkv=0) == -4
+    assert prefill(attn, D=96) == -3
+    assert prefill(attn, D=512) == -3
+    assert prefill(attn, scale=math.inf) == -5
+    assert prefill(attn, scale=math.nan) == -5
+    assert prefill(attn, B=-1) == -2
+    assert prefill(attn, Lq=9, Lk=8) == -2          # causal with a row that sees no key
+    assert prefill(attn, Lk=0) == -2
+    assert prefill(attn, B=1 << 20, Hq=1 << 10, Hkv=1, Lq=1 << 20, Lk=1 << 20) == -2
+    # empty calls succeed without enqueueing anything, and accept NULL pointers
+    assert prefill(attn, B=0) == 0
+    assert prefill(attn, Lq=0) == 0
+    assert prefill(attn, q=N, k=N, v=N, out=N, B=0) == 0
+    assert prefill(attn, q=N, k=N, v=N, out=N, Lq=0, Lk=0) == 0
+    assert prefill(attn, B=0, D=96) == -3          # the other arguments are still checked
+
+
+def decode(attn, split=0, ws=N, ws_bytes=0, lens=P, B=2, Hq=8, Hkv=2, Lmax=4096, D=128, scale=0.1):
+    return attn.lib.attn_decode_ex(P, P, P, lens, P, N, B, Hq, Hkv, Lmax, D, ctypes.c_float(scale), split, ws,
+                                   ws_bytes, None)
+
+
+def test_decode_validation(attn):
+    assert decode(attn, lens=N) == -1
+    assert decode(attn, Hq=7) == -4
+    assert decode(attn, D=80) == -3
+    assert decode(attn, scale=-math.inf) == -5
+    assert decode(attn, Lmax=0) == -2
+    assert decode(attn, B=-3) == -2
+    assert decode(attn, B=70000) == -2
+    assert decode(attn, split=100) == -7
+    assert decode(attn, split=-128) == -7
+    need = attn.decode_workspace_bytes(2, 8, 2, 4096, 128, 256)
+    assert need > 0
+    assert decode(attn, split=256, ws=P, ws_bytes=need - 1) == -8
+    assert decode(attn, B=0) == 0
+    assert attn.lib.attn_decode(N, N, N, N, N, 0, 8, 2, 64, 128, ctypes.c_float(0.1), None) == 0
+    assert attn.lib.attn_decode(P, P, P, N, P, 1, 8, 2, 64, 128, ctypes.c_float(0.1), None) == -1
+
+
+def test_decode_workspace_and_split_sizes(attn):
+    # one chunk: no partials needed
+    assert attn.decode_workspace_bytes(4, 32, 8, 256, 128, 256) == 0
+    # nsplit = 32768/1024 = 32 partials of D floats + 1 lse per (b, h), each array 256-B aligned
+    rows = 64 * 32 * 32
+    want = ((rows * 128 * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
+    assert attn.decode_workspace_bytes(64, 32, 8, 32768, 128, 1024) == want
+    assert attn.decode_workspace_bytes(1, 3, 2, 10, 128, 0) == 0          # invalid GQA -> 0
+    s = attn.decode_split_keys(64, 8, 32768)
+    assert s in (256, 512, 1024) and s % 128 == 0
+    assert attn.decode_split_keys(32, 1, 8192) == 256
+
+
+def test_binding_rejects_cpu_tensors(attn):
+    import torch
+    q = torch.zeros((1, 4, 8, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        attn.prefill(q, q[:, :1], q[:, :1])
+    with pytest.raises(TypeError):
+        attn.prefill(q.float(), q[:, :1], q[:, :1])

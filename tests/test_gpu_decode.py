@@ -1,0 +1,154 @@
+"""GPU parity of attn_decode / attn_decode_ex against the CPU oracle.
+
+Cache rows past each sequence's length hold NaN, so any read past the end
+shows up as a non-finite output.  Covers the ragged 64-sequence workload in
+full, the group-size sweep, edge lengths (0, 1, block and chunk boundaries,
+beyond Lmax), every head dim, group sizes that need several query-column
+blocks or head groups, and independence from the chunk size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs as ai
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+from gpu_util import DEV, check_lse, check_out, decode_cache_on_device, to_dev, to_np  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def attn():
+    import exact_attention_30_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+class OracleBySeq:
+    """The oracle one sequence at a time, fed while the caches are built."""
+
+    def __init__(self, case, qb):
+        self.case = case
+        self.q = ai.bf16_bits_to_f64(qb)
+        self.out = np.zeros((case.B, case.Hq, case.D))
+        self.lse = np.full((case.B, case.Hq), -np.inf)
+
+    def __call__(self, b, n, kb, vb):
+        o, l_ = oracle.decode(self.q[b:b + 1], ai.bf16_bits_to_f64(kb)[None], ai.bf16_bits_to_f64(vb)[None],
+                              np.array([n]), self.case.scale)
+        self.out[b], self.lse[b] = o[0], l_[0]
+
+
+def run_case(attn, case, split_keys=None, lens=None):
+    lens = case.kv_lens() if lens is None else np.asarray(lens, dtype=np.int32)
+    qb = case.q_bits()
+    ref = OracleBySeq(case, qb)
+    kc, vc = decode_cache_on_device(case, lens, per_seq=ref)
+    q = to_dev(qb)
+    lens_d = torch.from_numpy(lens).to(DEV)
+    if split_keys is None:
+        out = attn.decode(q, kc, vc, lens_d, scale=case.scale)
+        out2, lse = attn.decode_ex(q, kc, vc, lens_d, scale=case.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(out, out2)
+    else:
+        out, lse = attn.decode_ex(q, kc, vc, lens_d, scale=case.scale, split_keys=split_keys)
+        torch.cuda.synchronize()
+    check_out(to_np(out), ref.out, case.name)
+    check_lse(to_np(lse), ref.lse, case.name)
+    del kc, vc
+    return out
+
+
+@pytest.mark.timeout(900)
+def test_decode_ragged_64_sequences(attn):
+    run_case(attn, ai.RAGGED_DECODE)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("G", ai.G_SWEEP)
+def test_decode_gsweep(attn, G):
+    run_case(attn, ai.gsweep_decode(G))
+
+
+EDGE = ai.DecodeCase("edges_D128_G4", 41, B=12, Hq=8, Hkv=2, Lmax=1100, D=128, lens_lo=0, lens_hi=0,
+                     fixed_lens=[0, 1, 2, 31, 32, 33, 255, 256, 257, 1099, 1100, 5000])
+
+
+@pytest.mark.parametrize("split", [128, 256, 384, 1024, 2048])
+def test_decode_edge_lengths(attn, split):
+    run_case(attn, EDGE, split_keys=split)
+
+
+def test_decode_negative_length_is_empty(attn):
+    c = ai.DecodeCase("neg_len", 42, B=2, Hq=4, Hkv=4, Lmax=300, D=64, lens_lo=0, lens_hi=0, fixed_lens=[-5, 300])
+    lens = np.array([-5, 300], dtype=np.int32)
+    qb = c.q_bits()
+    ref = OracleBySeq(c, qb)
+    kc, vc = decode_cache_on_device(c, np.maximum(lens, 0), per_seq=ref)
+    out, lse = attn.decode_ex(to_dev(qb), kc, vc, torch.from_numpy(lens).to(DEV), scale=c.scale)
+    torch.cuda.synchronize()
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    check_out(to_np(out)[1], ref.out[1], "neg_len")
+
+
+@pytest.mark.parametrize("D,G,Hkv", [(64, 1, 3), (64, 8, 2), (256, 4, 2), (256, 1, 2), (128, 16, 2),
+                                     (128, 32, 1), (128, 48, 1), (128, 80, 1), (64, 64, 1), (256, 64, 1)])
+def test_decode_head_dims_and_groups(attn, D, G, Hkv):
+    c = ai.DecodeCase(f"D{D}_G{G}", 43, B=3, Hq=G * Hkv, Hkv=Hkv, Lmax=900, D=D, lens_lo=1, lens_hi=900,
+                      variant=D * 100 + G)
+    run_case(attn, c, split_keys=256)
+
+
+def test_decode_split_size_independence(attn):
+    c = ai.DecodeCase("split_indep", 44, B=4, Hq=16, Hkv=4, Lmax=5000, D=128, lens_lo=100, lens_hi=5000)
+    lens = c.kv_lens()
+    kc, vc = decode_cache_on_device(c, lens)
+    q = to_dev(c.q_bits())
+    ld = torch.from_numpy(lens).to(DEV)
+    res = [attn.decode_ex(q, kc, vc, ld, scale=c.scale, split_keys=s) for s in (128, 512, 1024, 8192)]
+    torch.cuda.synchronize()
+    for o, l_ in res[1:]:
+        np.testing.assert_allclose(to_np(o), to_np(res[0][0]), atol=1e-2, rtol=0)
+        np.testing.assert_allclose(to_np(l_), to_np(res[0][1]), atol=1e-5, rtol=0)
+
+
+def test_decode_equals_last_prefill_row(attn):
+    B, Hq, Hkv, L, D = 2, 8, 2, 777, 128
+    c = ai.PrefillCase("dec_vs_pre", 45, B=B, Hq=Hq, Hkv=Hkv, Lq=L, Lk=L, D=D)
+    q, k, v = to_dev(c.q_bits()), to_dev(c.k_bits()), to_dev(c.v_bits())
+    full, lf = attn.prefill(q, k, v, causal=True, scale=c.scale)
+    lens = torch.full((B,), L, dtype=torch.int32, device=DEV)
+    od, ld = attn.decode_ex(q[:, :, -1].contiguous(), k, v, lens, scale=c.scale, split_keys=256)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(to_np(od), to_np(full[:, :, -1]), atol=1e-2, rtol=0)
+    np.testing.assert_allclose(to_np(ld), to_np(lf[:, :, -1]), atol=1e-4, rtol=0)
+
+
+def test_decode_caller_workspace(attn):
+    c = ai.DecodeCase("ws", 46, B=3, Hq=8, Hkv=2, Lmax=3000, D=128, lens_lo=500, lens_hi=3000)
+    lens = c.kv_lens()
+    kc, vc = decode_cache_on_device(c, lens)
+    q = to_dev(c.q_bits())
+    ld = torch.from_numpy(lens).to(DEV)
+    need = attn.decode_workspace_bytes(c.B, c.Hq, c.Hkv, c.Lmax, c.D, 256)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    o1, l1 = attn.decode_ex(q, kc, vc, ld, scale=c.scale, split_keys=256, workspace=ws)
+    o2, l2 = attn.decode_ex(q, kc, vc, ld, scale=c.scale, split_keys=256)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    with pytest.raises(attn.AttnError):
+        attn.decode_ex(q, kc, vc, ld, scale=c.scale, split_keys=256, workspace=ws[:-1])
+
+
+def test_decode_deterministic(attn):
+    c = ai.DecodeCase("det", 47, B=8, Hq=32, Hkv=8, Lmax=4096, D=128, lens_lo=1, lens_hi=4096)
+    lens = c.kv_lens()
+    kc, vc = decode_cache_on_device(c, lens)
+    q = to_dev(c.q_bits())
+    ld = torch.from_numpy(lens).to(DEV)
+    a = attn.decode(q, kc, vc, ld, scale=c.scale)
+    b = attn.decode(q, kc, vc, ld, scale=c.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

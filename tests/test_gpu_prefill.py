@@ -1,0 +1,172 @@
+"""GPU parity of attn_prefill against the CPU oracle (element by element).
+
+Full-oracle cases cover every output; long sequences compare 64 seeded rows
+per (batch, head) (rows 0 and Lq-1 included), computed one by one by the
+oracle's row mode.  Shapes span several tiles and ragged tails, every head
+dim, several group sizes, causal and full attention, Lq < Lk (bottom-right
+mask) and the workloads used for measurement.
+"""
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs as ai
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+from gpu_util import DEV, PrefillData, check_lse, check_out, to_dev, to_np  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def attn():
+    import exact_attention_30_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+def run_full(attn, case, scale=None):
+    d = PrefillData(case)
+    sc = case.scale if scale is None else scale
+    out, lse = attn.prefill(d.q, d.k, d.v, causal=case.causal, scale=sc)
+    torch.cuda.synchronize()
+    q, k, v = d.f64()
+    ro, rl = oracle.attention(q, k, v, case.causal, sc)
+    e = check_out(to_np(out), ro, case.name)
+    check_lse(to_np(lse), rl, case.name)
+    return e
+
+
+def run_sampled(attn, case, nrows=64):
+    d = PrefillData(case)
+    out, lse = attn.prefill(d.q, d.k, d.v, causal=case.causal, scale=case.scale)
+    torch.cuda.synchronize()
+    rows = np.stack([np.stack([ai.rows_for_head(case.wid * 1000 + case.variant, b, h, case.Lq, nrows)
+                               for h in range(case.Hq)]) for b in range(case.B)])
+    q, k, v = d.f64()
+    ro, rl = oracle.attention_rows(q, k, v, rows, case.causal, case.scale)
+    go = to_np(out)
+    gl = to_np(lse)
+    bi = np.arange(case.B)[:, None, None]
+    hi = np.arange(case.Hq)[None, :, None]
+    check_out(go[bi, hi, rows], ro, case.name)
+    check_lse(gl[bi, hi, rows], rl, case.name)
+
+
+SMALL = [
+    ai.TINY,
+    ai.PrefillCase("ragged_G2_L100_D64", 11, B=2, Hq=4, Hkv=2, Lq=100, Lk=100, D=64),
+    ai.PrefillCase("chunk_G3_Lq77_Lk200_D128", 12, B=1, Hq=6, Hkv=2, Lq=77, Lk=200, D=128),
+    ai.PrefillCase("full_G1_Lq33_Lk129_D256", 13, B=1, Hq=2, Hkv=2, Lq=33, Lk=129, D=256, causal=False),
+    ai.PrefillCase("causal_G8_L130_D128", 14, B=1, Hq=8, Hkv=1, Lq=130, Lk=130, D=128),
+    ai.PrefillCase("one_row_Lk300_D128", 15, B=2, Hq=4, Hkv=1, Lq=1, Lk=300, D=128),
+    ai.PrefillCase("one_by_one_D64", 16, B=1, Hq=1, Hkv=1, Lq=1, Lk=1, D=64),
+    ai.PrefillCase("full_G4_Lq65_Lk65_D64", 17, B=3, Hq=8, Hkv=2, Lq=65, Lk=65, D=64, causal=False),
+    ai.PrefillCase("chunk_G2_Lq40_Lk1000_D256", 18, B=1, Hq=4, Hkv=2, Lq=40, Lk=1000, D=256),
+    ai.PrefillCase("causal_G16_L257_D128", 19, B=1, Hq=16, Hkv=1, Lq=257, Lk=257, D=128),
+    ai.PrefillCase("causal_G6_L300_D64", 20, B=1, Hq=12, Hkv=2, Lq=300, Lk=300, D=64),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: c.name)
+def test_prefill_small(attn, case):
+    run_full(attn, case)
+
+
+def test_prefill_qwen_4k_full(attn):
+    run_full(attn, ai.QWEN_4K)
+
+
+def test_prefill_d256_full(attn):
+    run_full(attn, ai.D256)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("case", [ai.QWEN_16K, ai.QWEN_32K, ai.QWEN_CHUNK], ids=lambda c: c.name)
+def test_prefill_long_sampled(attn, case):
+    run_sampled(attn, case)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("G", ai.G_SWEEP)
+def test_prefill_gsweep_sampled(attn, G):
+    run_sampled(attn, ai.gsweep_prefill(G))
+
+
+def test_prefill_scale_zero_closed_form(attn):
+    # zero scores: lse_i = ln(#visible keys) and out_i = mean of the visible V rows
+    c = ai.PrefillCase("scale0_chunk", 21, B=1, Hq=4, Hkv=2, Lq=96, Lk=300, D=128)
+    d = PrefillData(c)
+    out, lse = attn.prefill(d.q, d.k, d.v, causal=True, scale=0.0)
+    torch.cuda.synchronize()
+    _, _, v = d.f64()
+    cnt = np.arange(c.Lq) + 1 + (c.Lk - c.Lq)
+    np.testing.assert_allclose(to_np(lse)[0], np.broadcast_to(np.log(cnt), (4, c.Lq)), atol=1e-5)
+    csum = np.cumsum(v[0], axis=1)
+    want = np.stack([csum[h // 2][cnt - 1] / cnt[:, None] for h in range(4)])
+    check_out(to_np(out)[0], want, "scale0")
+
+
+def test_prefill_negative_scale(attn):
+    run_full(attn, ai.PrefillCase("neg_scale", 22, B=1, Hq=4, Hkv=1, Lq=70, Lk=150, D=64), scale=-0.2)
+
+
+def test_prefill_identical_v_rows(attn):
+    c = ai.PrefillCase("same_v", 23, B=1, Hq=4, Hkv=1, Lq=200, Lk=200, D=128)
+    d = PrefillData(c)
+    v = d.v[:, :, :1].expand_as(d.v).contiguous()
+    out, _ = attn.prefill(d.q, d.k, v, causal=True, scale=c.scale)
+    torch.cuda.synchronize()
+    want = np.broadcast_to(to_np(v[:, :, :1]), (1, 1, 200, 128))
+    np.testing.assert_allclose(to_np(out), np.broadcast_to(want, (1, 4, 200, 128)), atol=1e-2, rtol=0)
+
+
+def test_prefill_gqa_equals_replicated_mha(attn):
+    c = ai.PrefillCase("gqa_vs_mha", 24, B=2, Hq=8, Hkv=2, Lq=190, Lk=190, D=128)
+    d = PrefillData(c)
+    o1, l1 = attn.prefill(d.q, d.k, d.v, causal=True, scale=c.scale)
+    kr = d.k.repeat_interleave(4, dim=1).contiguous()
+    vr = d.v.repeat_interleave(4, dim=1).contiguous()
+    o2, l2 = attn.prefill(d.q, kr, vr, causal=True, scale=c.scale)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(to_np(o1), to_np(o2), atol=1e-2, rtol=0)
+    np.testing.assert_allclose(to_np(l1), to_np(l2), atol=1e-4, rtol=0)
+
+
+def test_prefill_chunk_equals_tail_of_full(attn):
+    c = ai.PrefillCase("tail", 25, B=1, Hq=8, Hkv=2, Lq=2048, Lk=2048, D=128)
+    d = PrefillData(c)
+    full, lf = attn.prefill(d.q, d.k, d.v, causal=True, scale=c.scale)
+    tail, lt = attn.prefill(d.q[:, :, -300:].contiguous(), d.k, d.v, causal=True, scale=c.scale)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(to_np(tail), to_np(full[:, :, -300:]), atol=1e-2, rtol=0)
+    np.testing.assert_allclose(to_np(lt), to_np(lf[:, :, -300:]), atol=1e-4, rtol=0)
+
+
+def test_prefill_deterministic(attn):
+    d = PrefillData(ai.QWEN_4K)
+    o1, l1 = attn.prefill(d.q, d.k, d.v, causal=True, scale=ai.QWEN_4K.scale)
+    o2, l2 = attn.prefill(d.q, d.k, d.v, causal=True, scale=ai.QWEN_4K.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_prefill_empty_calls(attn):
+    q = torch.empty((0, 4, 8, 64), dtype=torch.bfloat16, device=DEV)
+    k = torch.empty((0, 1, 8, 64), dtype=torch.bfloat16, device=DEV)
+    out, lse = attn.prefill(q, k, k)
+    assert out.shape == q.shape
+    q = torch.empty((1, 4, 0, 64), dtype=torch.bfloat16, device=DEV)
+    k = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16, device=DEV)
+    out, lse = attn.prefill(q, k, k)
+    assert out.numel() == 0
+
+
+def test_prefill_lse_optional(attn):
+    d = PrefillData(ai.TINY)
+    out, lse = attn.prefill(d.q, d.k, d.v, causal=True, scale=ai.TINY.scale, return_lse=False)
+    torch.cuda.synchronize()
+    assert lse is None
+    q, k, v = d.f64()
+    ro, _ = oracle.attention(q, k, v, True, ai.TINY.scale)
+    check_out(to_np(out), ro, "no-lse")
