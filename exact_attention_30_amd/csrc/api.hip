@@ -172,8 +172,9 @@ int attn_prefill(const void *q, const void *k, const void *v, void *out, float *
   a.Lq = Lq;
   a.Lk = Lk;
   a.G = Hq / Hkv;
-  a.hpw = gcd_int(a.G, 4);
-  a.wph = 4 / a.hpw;
+  const int nw = attn::prefill_waves();
+  a.hpw = gcd_int(a.G, nw);
+  a.wph = nw / a.hpw;
   a.Bq = 32 * a.wph;
   a.n_qblk = (Lq + a.Bq - 1) / a.Bq;
   a.n_hg = a.G / a.hpw;

@@ -15,8 +15,8 @@ struct PrefillArgs {
   float *lse;
   int B, Hq, Hkv, Lq, Lk;
   int G;       // Hq / Hkv
-  int hpw;     // query heads per workgroup (divides G and the 4 waves)
-  int wph;     // waves per head = 4 / hpw
+  int hpw;     // query heads per workgroup (divides G and the wave count)
+  int wph;     // waves per head = waves / hpw
   int Bq;      // query rows per head per workgroup = 32 * wph
   int n_qblk;  // ceil(Lq / Bq)
   int n_hg;    // head groups per KV head = G / hpw
@@ -43,6 +43,7 @@ struct DecodeArgs {
 };
 
 hipError_t launch_prefill(const PrefillArgs &a, int D, hipStream_t s);
+int prefill_waves();  // waves per prefill workgroup (32 query rows each)
 hipError_t launch_decode(const DecodeArgs &a, int D, hipStream_t s);
 
 }  // namespace attn

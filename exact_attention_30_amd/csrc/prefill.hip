@@ -10,21 +10,27 @@
 // быстрее…", section on group size (G query heads read one KV head).
 //
 // gfx950 design
-//  * One workgroup = 4 wave64s = 128 query rows of up to 4 query heads that
-//    share one KV head; every K/V tile it stages in LDS serves all of them.
+//  * One workgroup = 8 wave64s (two per SIMD) = 256 query rows of up to 8
+//    query heads that share one KV head; every K/V tile it stages in LDS
+//    serves all of them (256 FLOP per byte staged).
 //  * Each wave owns 32 query rows and computes the transposed score block
 //    S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys on the M side, queries on
 //    the N side).  In the accumulator layout a lane holds one query column and
-//    16 keys per 32-key block, so row max / row sum are lane-local plus one
-//    exchange between the two wave halves.
-//  * P^T (bf16) is fed to O^T += V^T P^T straight from those registers: the
-//    16 keys a lane holds for one P.V step are the same keys its V^T operand
-//    reads, because V^T is written to LDS with the matching key order.
-//  * V is transposed once per tile on its way into LDS (4 keys x 8 dims per
-//    thread, byte permutes), K is copied as is; both double-buffered.
+//    16 keys per 32-key block, so the row max and row sum are lane-local plus
+//    one v_permlane32_swap between the two wave halves.
+//  * P^T (bf16, round to nearest even) feeds O^T += V^T P^T straight from
+//    those registers.  V stays row-major in LDS; its V^T operand is read with
+//    ds_read_b64_tr_b16 (a 4 x 16 transpose per 16-lane group), two reads per
+//    MFMA, in the key order the P^T registers hold.
+//  * LDS rows are padded (K: 16 B, V: 64 B) so that the b128 K reads and the
+//    transposing V reads hit all 64 banks without conflicts.  Tiles are
+//    staged through registers and double-buffered: the next tile's global
+//    loads are in flight while the current tile is computed.
 //  * Softmax in the log2 domain: p = exp2(s*c - m) with c = scale*log2(e);
 //    the running maximum is raised lazily (ATTN_RESCALE_SLACK), so the O
-//    rescale is skipped on almost every tile.
+//    rescale is skipped on almost every tile.  The row sum adds the fp32
+//    exponentials (before their rounding to bf16), so that the log-sum-exp
+//    is that of the true normaliser.
 //  * Causal: tiles past a wave's last visible key are skipped, the mask is
 //    evaluated only on tiles that cross the diagonal or the end of the keys.
 //    Workgroups are issued heaviest first, and consecutive workgroup ids are
@@ -37,27 +43,42 @@ namespace attn {
 
 template <int D, int BK>
 struct PrefillCfg {
-  static constexpr int NW = 4;
+  static constexpr int NW = 8;
   static constexpr int NT = NW * 64;
-  static constexpr int KS = D + 8;       // K row stride in LDS (bf16 elements)
-  static constexpr int VS = BK + 8;      // V^T row stride in LDS
+  static constexpr int KS = D + 8;       // K row stride in LDS (bf16 elements): +16 B
+  static constexpr int VS = D + 32;      // V row stride in LDS: +64 B
   static constexpr int K_ELEMS = BK * KS;
-  static constexpr int V_ELEMS = D * VS;
+  static constexpr int V_ELEMS = BK * VS;
   static constexpr int BUF = K_ELEMS + V_ELEMS;
-  static constexpr int K_CHUNKS = BK * D / 8;          // 16-byte pieces of a K tile
-  static constexpr int K_PER_T = (K_CHUNKS + NT - 1) / NT;
-  static constexpr int V_UNITS = (BK / 4) * (D / 8);    // 4 keys x 8 dims each
-  static constexpr int V_PER_T = (V_UNITS + NT - 1) / NT;
+  static constexpr int CHUNKS = BK * D / 8;   // 16-byte pieces per tile and tensor
+  static constexpr int PER_T = CHUNKS / NT;
+  static_assert(CHUNKS % NT == 0, "tile must split evenly over the threads");
   static_assert(BK % 32 == 0 && D % 32 == 0, "tile shape");
 };
 
-// Position of key k (0..15 inside a 16-key group) in the V^T row: the lane
-// half hh reads positions 8*hh..8*hh+7, which must be keys
-// {4hh..4hh+3, 8+4hh..8+4hh+3}, the keys the S^T accumulator gives that half.
-ATTN_DEV int vt_pos16(int k16) { return 8 * ((k16 >> 2) & 1) + 4 * (k16 >> 3) + (k16 & 3); }
+ATTN_DEV float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+ATTN_DEV float pair_min(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+ATTN_DEV float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+ATTN_DEV bf16x4 lds_tr16(const uint16_t *p) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4 *)(reinterpret_cast<uintptr_t>(p)));
+  return __builtin_bit_cast(bf16x4, r);
+}
 
 template <int D, int BK>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
   using C = PrefillCfg<D, BK>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF];
 
@@ -101,63 +122,30 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const uint16_t *kg = a.k + kvoff;
   const uint16_t *vg = a.v + kvoff;
 
-  u32x4 kreg[C::K_PER_T];
-  u32x4 vreg[C::V_PER_T][4];
+  u32x4 kreg[C::PER_T], vreg[C::PER_T];
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
   auto load_tile = [&](int j) {
     const int k0 = j * BK;
 #pragma unroll
-    for (int i = 0; i < C::K_PER_T; ++i) {
+    for (int i = 0; i < C::PER_T; ++i) {
       const int c = tid + i * C::NT;
-      if (C::K_CHUNKS % C::NT == 0 || c < C::K_CHUNKS) {
-        const int key = c / (D / 8), dc = c % (D / 8);
-        const int gk = k0 + key;
-        kreg[i] = gk < a.Lk ? ld16(kg + (size_t)gk * D + dc * 8) : zero4;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < C::V_PER_T; ++i) {
-      const int u = tid + i * C::NT;
-      if (C::V_UNITS % C::NT == 0 || u < C::V_UNITS) {
-        const int quad = u / (D / 8), dc = u % (D / 8);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int gk = k0 + 4 * quad + e;
-          vreg[i][e] = gk < a.Lk ? ld16(vg + (size_t)gk * D + dc * 8) : zero4;
-        }
-      }
+      const int key = c / (D / 8), dc = c % (D / 8);
+      const int gk = k0 + key;
+      const bool ok = gk < a.Lk;
+      kreg[i] = ok ? ld16(kg + (size_t)gk * D + dc * 8) : zero4;
+      vreg[i] = ok ? ld16(vg + (size_t)gk * D + dc * 8) : zero4;
     }
   };
-
   auto store_tile = [&](int buf) {
     uint16_t *ks_ = smem + buf * C::BUF;
-    uint16_t *vt = ks_ + C::K_ELEMS;
+    uint16_t *vs_ = ks_ + C::K_ELEMS;
 #pragma unroll
-    for (int i = 0; i < C::K_PER_T; ++i) {
+    for (int i = 0; i < C::PER_T; ++i) {
       const int c = tid + i * C::NT;
-      if (C::K_CHUNKS % C::NT == 0 || c < C::K_CHUNKS) {
-        const int key = c / (D / 8), dc = c % (D / 8);
-        st16(ks_ + key * C::KS + dc * 8, kreg[i]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < C::V_PER_T; ++i) {
-      const int u = tid + i * C::NT;
-      if (C::V_UNITS % C::NT == 0 || u < C::V_UNITS) {
-        const int quad = u / (D / 8), dc = u % (D / 8);
-        const int k = 4 * quad;
-        const int pos = (k & ~15) + vt_pos16(k & 15);
-#pragma unroll
-        for (int w4 = 0; w4 < 4; ++w4) {
-          const uint32_t a0 = vreg[i][0][w4], a1 = vreg[i][1][w4], a2 = vreg[i][2][w4], a3 = vreg[i][3][w4];
-          u32x2 lo, hi;
-          lo[0] = pack_lo16(a0, a1); lo[1] = pack_lo16(a2, a3);
-          hi[0] = pack_hi16(a0, a1); hi[1] = pack_hi16(a2, a3);
-          *reinterpret_cast<u32x2 *>(vt + (dc * 8 + 2 * w4) * C::VS + pos) = lo;
-          *reinterpret_cast<u32x2 *>(vt + (dc * 8 + 2 * w4 + 1) * C::VS + pos) = hi;
-        }
-      }
+      const int key = c / (D / 8), dc = c % (D / 8);
+      st16(ks_ + key * C::KS + dc * 8, kreg[i]);
+      st16(vs_ + key * C::VS + dc * 8, vreg[i]);
     }
   };
 
@@ -170,6 +158,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const bool cpos = cexp >= 0.f;
   const float maskval = cpos ? -__builtin_inff() : __builtin_inff();
 
+  // per-lane LDS offsets of the MFMA operands
+  const int koff = ql * C::KS + 8 * hh;                             // + 32 rb rows, + 16 ks
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int voff = (4 * hh + (j16 >> 2)) * C::VS + 16 * (g16 & 1) + 4 * (j16 & 3);  // + 16 kb rows, + 32 db
+
   load_tile(0);
   store_tile(0);
   __syncthreads();
@@ -177,7 +170,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   for (int j = 0; j < nt; ++j) {
     if (j + 1 < nt) load_tile(j + 1);
     const uint16_t *ks_ = smem + (j & 1) * C::BUF;
-    const uint16_t *vt = ks_ + C::K_ELEMS;
+    const uint16_t *vs_ = ks_ + C::K_ELEMS;
     const int k0 = j * BK;
     if (k0 < kend_w) {
       // S^T = K Q^T for BK keys x 32 queries
@@ -185,27 +178,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int rb = 0; rb < BK / 32; ++rb) {
         s[rb] = f32x16{};
-        const uint16_t *kr = ks_ + (32 * rb + ql) * C::KS + 8 * hh;
+        const uint16_t *kr = ks_ + 32 * rb * C::KS + koff;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks)
           s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(kr + 16 * ks)), qf[ks], s[rb], 0, 0, 0);
       }
       const bool need_mask = (k0 + BK > kmask_from);
-      uint32_t vis[BK / 32];
       if (need_mask) {
         const int lim = a.causal ? min(a.Lk - 1, qrow + off) : a.Lk - 1;
 #pragma unroll
-        for (int rb = 0; rb < BK / 32; ++rb) {
-          uint32_t bits = 0;
+        for (int rb = 0; rb < BK / 32; ++rb)
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) {
             const int key = k0 + 32 * rb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-            const bool vv = key <= lim;
-            bits |= (vv ? 1u : 0u) << rr;
-            s[rb][rr] = vv ? s[rb][rr] : maskval;
+            s[rb][rr] = key <= lim ? s[rb][rr] : maskval;
           }
-          vis[rb] = bits;
-        }
       }
       // tile maximum of s*c for this lane's query
       float red = s[0][0];
@@ -215,14 +202,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
           for (int rr = (rb == 0 ? 1 : 0); rr < 16; rr += 2)
             red = (rr + 1 < 16) ? fmax3(red, s[rb][rr], s[rb][rr + 1]) : __builtin_fmaxf(red, s[rb][rr]);
-        red = __builtin_fmaxf(red, xor32(red));
+        red = pair_max(red);
       } else {
 #pragma unroll
         for (int rb = 0; rb < BK / 32; ++rb)
 #pragma unroll
           for (int rr = (rb == 0 ? 1 : 0); rr < 16; rr += 2)
             red = (rr + 1 < 16) ? fmin3(red, s[rb][rr], s[rb][rr + 1]) : __builtin_fminf(red, s[rb][rr]);
-        red = __builtin_fminf(red, xor32(red));
+        red = pair_min(red);
       }
       const float mt = red * cexp;
       const bool need = mt > m_run + ATTN_RESCALE_SLACK;
@@ -236,28 +223,34 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       }
       const float nm = -m_run;
       bf16x8 pb[BK / 16];
-      float lsum = 0.f;
 #pragma unroll
       for (int rb = 0; rb < BK / 32; ++rb) {
         float p[16];
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
-          float e = fast_exp2(__builtin_fmaf(s[rb][rr], cexp, nm));
-          if (need_mask) e = ((vis[rb] >> rr) & 1u) ? e : 0.f;
-          p[rr] = e;
-          lsum += e;
+          // a hidden score is +-inf here; with c == 0 the product would be NaN, so select
+          const float e = fast_exp2(__builtin_fmaf(s[rb][rr], cexp, nm));
+          p[rr] = (need_mask && s[rb][rr] == maskval) ? 0.f : e;
         }
         pb[2 * rb] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
         pb[2 * rb + 1] = pack8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
+        // row sum of the fp32 exponentials (the lse needs the unrounded normaliser)
+        float t8[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t8[i] = p[i] + p[i + 8];
+        l_run += ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
       }
-      l_run += lsum;
-      // O^T += V^T P^T
+      // O^T += V^T P^T; the V^T operand comes from row-major V by transposing reads
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const uint16_t *vr = vt + (32 * db + ql) * C::VS + 8 * hh;
 #pragma unroll
-        for (int kb = 0; kb < BK / 16; ++kb)
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(vr + 16 * kb)), pb[kb], o[db], 0, 0, 0);
+        for (int kb = 0; kb < BK / 16; ++kb) {
+          const uint16_t *vp = vs_ + 16 * kb * C::VS + 32 * db + voff;
+          const bf16x4 lo = lds_tr16(vp);
+          const bf16x4 hi = lds_tr16(vp + 8 * C::VS);
+          const bf16x8 vop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[kb], o[db], 0, 0, 0);
+        }
       }
     }
     if (j + 1 < nt) store_tile((j + 1) & 1);
@@ -265,7 +258,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   }
 
   // ---- epilogue: out = O / l, lse = m ln2 + ln l -------------------------
-  const float lt = l_run + xor32(l_run);
+  const float lt = pair_sum(l_run);
   if (qrow < a.Lq && kend_w > 0) {
     const float inv = 1.f / lt;
     uint16_t *op = a.out + (((size_t)b * a.Hq + head) * a.Lq + qrow) * D;
@@ -288,7 +281,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 
 template <int D, int BK>
 static hipError_t launch_t(const PrefillArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((prefill_kernel<D, BK>), dim3(a.total), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((prefill_kernel<D, BK>), dim3(a.total), dim3(PrefillCfg<D, BK>::NT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -300,5 +293,7 @@ hipError_t launch_prefill(const PrefillArgs &a, int D, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
 }
+
+int prefill_waves() { return PrefillCfg<128, 64>::NW; }
 
 }  // namespace attn
