@@ -36,6 +36,8 @@
 //    Workgroups are issued heaviest first, and consecutive workgroup ids are
 //    spread over the 8 XCDs so that each XCD works on one KV head at a time
 //    (its K/V stay in that XCD's L2).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -49,7 +51,9 @@ struct PrefillCfg {
   static constexpr int VS = D + 32;      // V row stride in LDS: +64 B
   static constexpr int K_ELEMS = BK * KS;
   static constexpr int V_ELEMS = BK * VS;
-  static constexpr int BUF = K_ELEMS + V_ELEMS;
+  static constexpr int KBUFS = 2;        // K tiles in LDS (current, next)
+  static constexpr int VBUFS = 3;        // V tiles (previous, current, next)
+  static constexpr int LDS_ELEMS = KBUFS * K_ELEMS + VBUFS * V_ELEMS;
   static constexpr int CHUNKS = BK * D / 8;   // 16-byte pieces per tile and tensor
   static constexpr int PER_T = CHUNKS / NT;
   static_assert(CHUNKS % NT == 0, "tile must split evenly over the threads");
@@ -80,7 +84,9 @@ ATTN_DEV bf16x4 lds_tr16(const uint16_t *p) {
 template <int D, int BK>
 __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
   using C = PrefillCfg<D, BK>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
+  uint16_t *const kbuf = smem;
+  uint16_t *const vbuf = smem + C::KBUFS * C::K_ELEMS;
 
   // ---- which tile: XCD-grouped, heaviest q-block first -------------------
   const int bid = blockIdx.x;
@@ -137,9 +143,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
       vreg[i] = ok ? ld16(vg + (size_t)gk * D + dc * 8) : zero4;
     }
   };
-  auto store_tile = [&](int buf) {
-    uint16_t *ks_ = smem + buf * C::BUF;
-    uint16_t *vs_ = ks_ + C::K_ELEMS;
+  auto store_tile = [&](int j) {
+    uint16_t *ks_ = kbuf + (j % C::KBUFS) * C::K_ELEMS;
+    uint16_t *vs_ = vbuf + (j % C::VBUFS) * C::V_ELEMS;
 #pragma unroll
     for (int i = 0; i < C::PER_T; ++i) {
       const int c = tid + i * C::NT;
@@ -163,14 +169,114 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
   const int g16 = lane >> 4, j16 = lane & 15;
   const int voff = (4 * hh + (j16 >> 2)) * C::VS + 16 * (g16 & 1) + 4 * (j16 & 3);  // + 16 kb rows, + 32 db
 
+  bf16x8 pb[BK / 16];
+  // O^T += V^T P^T for one tile; the V^T operand comes from row-major V by
+  // transposing reads
+  auto pv = [&](const uint16_t *vs_) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int kb = 0; kb < BK / 16; ++kb) {
+        const uint16_t *vp = vs_ + 16 * kb * C::VS + 32 * db + voff;
+        const bf16x4 lo = lds_tr16(vp);
+        const bf16x4 hi = lds_tr16(vp + 8 * C::VS);
+        const bf16x8 vop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[kb], o[db], 0, 0, 0);
+      }
+    }
+    // keep the transposing reads three MFMAs ahead of their use
+    constexpr int N = (D / 32) * (BK / 16);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < N - 3; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+  };
+
+  // Online-softmax update for one tile of S^T (this lane: one query, BK/2
+  // keys): raise the running max if needed, P = exp2(s*c - m) into pb,
+  // row sum into l_run.  MASKED: the tile crosses the diagonal or the end of
+  // the keys and hidden scores hold maskval.
+  auto softmax = [&](f32x16(&s)[BK / 32], auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
+    float red;
+    if (cpos) {
+      float mx[BK / 32][4];
+#pragma unroll
+      for (int rb = 0; rb < BK / 32; ++rb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          mx[rb][g] = fmax3(s[rb][4 * g], s[rb][4 * g + 1], __builtin_fmaxf(s[rb][4 * g + 2], s[rb][4 * g + 3]));
+      red = mx[0][0];
+#pragma unroll
+      for (int rb = 0; rb < BK / 32; ++rb)
+#pragma unroll
+        for (int g = (rb == 0 ? 1 : 0); g < 4; g += 2)
+          red = (g + 1 < 4) ? fmax3(red, mx[rb][g], mx[rb][g + 1]) : __builtin_fmaxf(red, mx[rb][g]);
+      red = pair_max(red);
+    } else {
+      float mn[BK / 32][4];
+#pragma unroll
+      for (int rb = 0; rb < BK / 32; ++rb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          mn[rb][g] = fmin3(s[rb][4 * g], s[rb][4 * g + 1], __builtin_fminf(s[rb][4 * g + 2], s[rb][4 * g + 3]));
+      red = mn[0][0];
+#pragma unroll
+      for (int rb = 0; rb < BK / 32; ++rb)
+#pragma unroll
+        for (int g = (rb == 0 ? 1 : 0); g < 4; g += 2)
+          red = (g + 1 < 4) ? fmin3(red, mn[rb][g], mn[rb][g + 1]) : __builtin_fminf(red, mn[rb][g]);
+      red = pair_min(red);
+    }
+    const float mt = red * cexp;
+    const bool need = mt > m_run + ATTN_RESCALE_SLACK;
+    if (wave_any(need)) {
+      const float mnew = need ? mt : m_run;
+      const float alpha = need ? fast_exp2(m_run - mnew) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+      m_run = mnew;
+    }
+    const float nm = -m_run;
+#pragma unroll
+    for (int rb = 0; rb < BK / 32; ++rb) {
+      float p[16];
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const float e = fast_exp2(__builtin_fmaf(s[rb][rr], cexp, nm));
+        // a hidden score is +-inf; with c == 0 the product would be NaN, so select
+        p[rr] = (MASKED && s[rb][rr] == maskval) ? 0.f : e;
+      }
+      pb[2 * rb] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+      pb[2 * rb + 1] = pack8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
+      // row sum of the fp32 exponentials (the lse needs the unrounded normaliser)
+      float t8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t8[i] = p[i] + p[i + 8];
+      l_run += ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
+    }
+  };
+
+  // Waves 0-3 run QK, softmax, PV of tile j between two barriers; waves 4-7
+  // (one per SIMD, next to one of the first group) run PV of tile j-1 first,
+  // then QK and softmax of tile j, so that on each SIMD one wave's softmax
+  // overlaps the other's matrix work.
+  const bool lag = w >= C::NW / 2;
+  bool pending = false;
   load_tile(0);
   store_tile(0);
   __syncthreads();
 
   for (int j = 0; j < nt; ++j) {
     if (j + 1 < nt) load_tile(j + 1);
-    const uint16_t *ks_ = smem + (j & 1) * C::BUF;
-    const uint16_t *vs_ = ks_ + C::K_ELEMS;
+    const uint16_t *ks_ = kbuf + (j % C::KBUFS) * C::K_ELEMS;
+    const uint16_t *vs_ = vbuf + (j % C::VBUFS) * C::V_ELEMS;
+    if (pending) pv(vbuf + ((j + C::VBUFS - 1) % C::VBUFS) * C::V_ELEMS);
+    pending = false;
     const int k0 = j * BK;
     if (k0 < kend_w) {
       // S^T = K Q^T for BK keys x 32 queries
@@ -183,6 +289,17 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
         for (int ks = 0; ks < D / 16; ++ks)
           s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(kr + 16 * ks)), qf[ks], s[rb], 0, 0, 0);
       }
+      {
+        // keep the K operand reads four MFMAs ahead of their use
+        constexpr int N = (BK / 32) * (D / 16);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < N - 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      }
       const bool need_mask = (k0 + BK > kmask_from);
       if (need_mask) {
         const int lim = a.causal ? min(a.Lk - 1, qrow + off) : a.Lk - 1;
@@ -193,69 +310,17 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
             const int key = k0 + 32 * rb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
             s[rb][rr] = key <= lim ? s[rb][rr] : maskval;
           }
-      }
-      // tile maximum of s*c for this lane's query
-      float red = s[0][0];
-      if (cpos) {
-#pragma unroll
-        for (int rb = 0; rb < BK / 32; ++rb)
-#pragma unroll
-          for (int rr = (rb == 0 ? 1 : 0); rr < 16; rr += 2)
-            red = (rr + 1 < 16) ? fmax3(red, s[rb][rr], s[rb][rr + 1]) : __builtin_fmaxf(red, s[rb][rr]);
-        red = pair_max(red);
+        softmax(s, std::true_type{});
       } else {
-#pragma unroll
-        for (int rb = 0; rb < BK / 32; ++rb)
-#pragma unroll
-          for (int rr = (rb == 0 ? 1 : 0); rr < 16; rr += 2)
-            red = (rr + 1 < 16) ? fmin3(red, s[rb][rr], s[rb][rr + 1]) : __builtin_fminf(red, s[rb][rr]);
-        red = pair_min(red);
+        softmax(s, std::false_type{});
       }
-      const float mt = red * cexp;
-      const bool need = mt > m_run + ATTN_RESCALE_SLACK;
-      if (wave_any(need)) {
-        const float mnew = need ? mt : m_run;
-        const float alpha = need ? fast_exp2(m_run - mnew) : 1.f;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-        m_run = mnew;
-      }
-      const float nm = -m_run;
-      bf16x8 pb[BK / 16];
-#pragma unroll
-      for (int rb = 0; rb < BK / 32; ++rb) {
-        float p[16];
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          // a hidden score is +-inf here; with c == 0 the product would be NaN, so select
-          const float e = fast_exp2(__builtin_fmaf(s[rb][rr], cexp, nm));
-          p[rr] = (need_mask && s[rb][rr] == maskval) ? 0.f : e;
-        }
-        pb[2 * rb] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-        pb[2 * rb + 1] = pack8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
-        // row sum of the fp32 exponentials (the lse needs the unrounded normaliser)
-        float t8[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) t8[i] = p[i] + p[i + 8];
-        l_run += ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
-      }
-      // O^T += V^T P^T; the V^T operand comes from row-major V by transposing reads
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-        for (int kb = 0; kb < BK / 16; ++kb) {
-          const uint16_t *vp = vs_ + 16 * kb * C::VS + 32 * db + voff;
-          const bf16x4 lo = lds_tr16(vp);
-          const bf16x4 hi = lds_tr16(vp + 8 * C::VS);
-          const bf16x8 vop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[kb], o[db], 0, 0, 0);
-        }
-      }
+      if (lag) pending = true;
+      else pv(vs_);
     }
-    if (j + 1 < nt) store_tile((j + 1) & 1);
+    if (j + 1 < nt) store_tile(j + 1);
     __syncthreads();
   }
+  if (pending) pv(vbuf + ((nt - 1) % C::VBUFS) * C::V_ELEMS);
 
   // ---- epilogue: out = O / l, lse = m ln2 + ln l -------------------------
   const float lt = pair_sum(l_run);
