@@ -23,11 +23,11 @@ STATUS_NAMES = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "AT
                 -8: "ATTN_ERR_WORKSPACE"}
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+def _load(path: str = LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with __graft_entry__.build() "
                           "(python exact_attention_30_amd/build.py)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.attn_prefill.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
     lib.attn_prefill.restype = i

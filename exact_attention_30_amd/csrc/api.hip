@@ -15,15 +15,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 bool head_dim_ok(int D) { return D == 64 || D == 128 || D == 256; }
 
-int gcd_int(int x, int y) {
-  while (y) {
-    const int t = x % y;
-    x = y;
-    y = t;
-  }
-  return x;
-}
-
 // The memory pool attn_decode takes its partials from: one per device, kept
 // (release threshold at its maximum) so that repeated calls reuse memory.
 std::mutex g_pool_mu;
@@ -172,15 +163,7 @@ int attn_prefill(const void *q, const void *k, const void *v, void *out, float *
   a.Lq = Lq;
   a.Lk = Lk;
   a.G = Hq / Hkv;
-  const int nw = attn::prefill_waves();
-  a.hpw = gcd_int(a.G, nw);
-  a.wph = nw / a.hpw;
-  a.Bq = 32 * a.wph;
-  a.n_qblk = (Lq + a.Bq - 1) / a.Bq;
-  a.n_hg = a.G / a.hpw;
-  const long long total = (long long)a.n_qblk * Hkv * a.n_hg * B;
-  if (total > 0x7fffffffLL) return ATTN_ERR_SHAPE;
-  a.total = (int)total;
+  if (!attn::prefill_plan(a, D)) return ATTN_ERR_SHAPE;
   a.causal = causal ? 1 : 0;
   a.c = scale * kLog2e;
   hipError_t e = attn::launch_prefill(a, D, reinterpret_cast<hipStream_t>(stream));

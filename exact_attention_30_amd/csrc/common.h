@@ -10,6 +10,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 #define ATTN_DEV __device__ __forceinline__
 
@@ -52,3 +53,30 @@ ATTN_DEV bf16x8 pack8(float a0, float a1, float a2, float a3, float a4, float a5
 
 ATTN_DEV float fmax3(float a, float b, float c) { return __builtin_fmaxf(a, __builtin_fmaxf(b, c)); }
 ATTN_DEV float fmin3(float a, float b, float c) { return __builtin_fminf(a, __builtin_fminf(b, c)); }
+
+// Row reductions across the two halves of a wave64 (lane l with lane l ^ 32):
+// v_permlane32_swap(v, v) returns {v[l], v[l ^ 32]} as a pair in every lane.
+ATTN_DEV float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+ATTN_DEV float pair_min(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+ATTN_DEV float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane
+// 4r + c supplies the address of 4 consecutive bf16 of row r; lane i receives
+// element i % 4 of the chunk of lane 4r + i / 4 for r = 0..3, i.e. column i of
+// the 4 x 16 block.
+ATTN_DEV bf16x4 lds_tr16(const uint16_t *p) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4 *)(reinterpret_cast<uintptr_t>(p)));
+  return __builtin_bit_cast(bf16x4, r);
+}
+

@@ -17,7 +17,7 @@ struct PrefillArgs {
   int G;       // Hq / Hkv
   int hpw;     // query heads per workgroup (divides G and the wave count)
   int wph;     // waves per head = waves / hpw
-  int Bq;      // query rows per head per workgroup = 32 * wph
+  int Bq;      // query rows per head per workgroup = rows per wave * wph
   int n_qblk;  // ceil(Lq / Bq)
   int n_hg;    // head groups per KV head = G / hpw
   int total;   // workgroups in the grid
@@ -42,8 +42,10 @@ struct DecodeArgs {
   float c;          // scale * log2(e)
 };
 
+// Fill in the query-row packing (hpw, wph, Bq, n_qblk, n_hg, total) for the
+// kernel that serves head dim D; false if the grid would be too large.
+bool prefill_plan(PrefillArgs &a, int D);
 hipError_t launch_prefill(const PrefillArgs &a, int D, hipStream_t s);
-int prefill_waves();  // waves per prefill workgroup (32 query rows each)
 hipError_t launch_decode(const DecodeArgs &a, int D, hipStream_t s);
 
 }  // namespace attn

@@ -41,6 +41,12 @@
 #include "common.h"
 #include "kernels.h"
 
+// Scheduling choices (compile-time):
+//  ATTN_PF_PRIO         raise the wave priority around the MFMA sections
+#ifndef ATTN_PF_PRIO
+#define ATTN_PF_PRIO 1
+#endif
+
 namespace attn {
 
 template <int D, int BK>
@@ -51,35 +57,14 @@ struct PrefillCfg {
   static constexpr int VS = D + 32;      // V row stride in LDS: +64 B
   static constexpr int K_ELEMS = BK * KS;
   static constexpr int V_ELEMS = BK * VS;
-  static constexpr int KBUFS = 2;        // K tiles in LDS (current, next)
-  static constexpr int VBUFS = 3;        // V tiles (previous, current, next)
+  static constexpr int KBUFS = 2;        // K tiles in LDS
+  static constexpr int VBUFS = 2;        // V tiles
   static constexpr int LDS_ELEMS = KBUFS * K_ELEMS + VBUFS * V_ELEMS;
   static constexpr int CHUNKS = BK * D / 8;   // 16-byte pieces per tile and tensor
   static constexpr int PER_T = CHUNKS / NT;
   static_assert(CHUNKS % NT == 0, "tile must split evenly over the threads");
   static_assert(BK % 32 == 0 && D % 32 == 0, "tile shape");
 };
-
-ATTN_DEV float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-ATTN_DEV float pair_min(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __builtin_fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-ATTN_DEV float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
-ATTN_DEV bf16x4 lds_tr16(const uint16_t *p) {
-  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4 *)(reinterpret_cast<uintptr_t>(p)));
-  return __builtin_bit_cast(bf16x4, r);
-}
 
 template <int D, int BK>
 __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
@@ -129,29 +114,31 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
   const uint16_t *vg = a.v + kvoff;
 
   u32x4 kreg[C::PER_T], vreg[C::PER_T];
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
-  auto load_tile = [&](int j) {
-    const int k0 = j * BK;
+  // K of tile jk and V of tile jv, staged through registers.  Rows past the
+  // end of the keys are read from the last row instead (the loads stay
+  // unconditional): such keys are masked, so their K only meets -inf scores
+  // and their V only zero weights.
+  auto load_tile = [&](int jk, int jv) {
 #pragma unroll
     for (int i = 0; i < C::PER_T; ++i) {
       const int c = tid + i * C::NT;
       const int key = c / (D / 8), dc = c % (D / 8);
-      const int gk = k0 + key;
-      const bool ok = gk < a.Lk;
-      kreg[i] = ok ? ld16(kg + (size_t)gk * D + dc * 8) : zero4;
-      vreg[i] = ok ? ld16(vg + (size_t)gk * D + dc * 8) : zero4;
+      const int gk = min(jk * BK + key, a.Lk - 1);
+      const int gv = min(jv * BK + key, a.Lk - 1);
+      kreg[i] = ld16(kg + (size_t)gk * D + dc * 8);
+      vreg[i] = ld16(vg + (size_t)gv * D + dc * 8);
     }
   };
-  auto store_tile = [&](int j) {
-    uint16_t *ks_ = kbuf + (j % C::KBUFS) * C::K_ELEMS;
-    uint16_t *vs_ = vbuf + (j % C::VBUFS) * C::V_ELEMS;
+  auto store_tile = [&](int jk, int jv, bool sk, bool sv) {
+    uint16_t *ks_ = kbuf + (jk % C::KBUFS) * C::K_ELEMS;
+    uint16_t *vs_ = vbuf + (jv % C::VBUFS) * C::V_ELEMS;
 #pragma unroll
     for (int i = 0; i < C::PER_T; ++i) {
       const int c = tid + i * C::NT;
       const int key = c / (D / 8), dc = c % (D / 8);
-      st16(ks_ + key * C::KS + dc * 8, kreg[i]);
-      st16(vs_ + key * C::VS + dc * 8, vreg[i]);
+      if (sk) st16(ks_ + key * C::KS + dc * 8, kreg[i]);
+      if (sv) st16(vs_ + key * C::VS + dc * 8, vreg[i]);
     }
   };
 
@@ -261,26 +248,24 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  // Waves 0-3 run QK, softmax, PV of tile j between two barriers; waves 4-7
-  // (one per SIMD, next to one of the first group) run PV of tile j-1 first,
-  // then QK and softmax of tile j, so that on each SIMD one wave's softmax
-  // overlaps the other's matrix work.
-  const bool lag = w >= C::NW / 2;
-  bool pending = false;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < nt; ++j) {
-    if (j + 1 < nt) load_tile(j + 1);
-    const uint16_t *ks_ = kbuf + (j % C::KBUFS) * C::K_ELEMS;
-    const uint16_t *vs_ = vbuf + (j % C::VBUFS) * C::V_ELEMS;
-    if (pending) pv(vbuf + ((j + C::VBUFS - 1) % C::VBUFS) * C::V_ELEMS);
-    pending = false;
-    const int k0 = j * BK;
-    if (k0 < kend_w) {
-      // S^T = K Q^T for BK keys x 32 queries
-      f32x16 s[BK / 32];
+  // Two-group ping-pong.  Waves 0-3 (group A) and 4-7 (group B) share the
+  // SIMDs pairwise (wave w and w + 4 run on the same SIMD).  Each tile takes
+  // two phases separated by workgroup barriers; in every phase one group runs
+  // its matrix work G(j) = [P.V of tile j-1, QK of tile j] while the other runs
+  // its softmax of the tile it has just multiplied, so the exponentials of one
+  // wave execute next to the MFMAs of its SIMD neighbour:
+  //     phase 2j   : A G(j)      B softmax(j-1)
+  //     phase 2j+1 : A softmax(j) B G(j)
+  // K(j+1) and V(j) are fetched at the start of phase 2j and written to LDS at
+  // the end of phase 2j+1 (double-buffered: K(j) and V(j-1) are read during
+  // phases 2j and 2j+1).
+  const bool grpA = w < C::NW / 2;
+  f32x16 s[BK / 32];
+  auto active = [&](int jj) { return jj >= 0 && jj < nt && jj * BK < kend_w; };
+  auto gemm = [&](int jj) {
+    if (active(jj - 1)) pv(vbuf + ((jj - 1) % C::VBUFS) * C::V_ELEMS);
+    if (active(jj)) {
+      const uint16_t *ks_ = kbuf + (jj % C::KBUFS) * C::K_ELEMS;
 #pragma unroll
       for (int rb = 0; rb < BK / 32; ++rb) {
         s[rb] = f32x16{};
@@ -289,38 +274,61 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
         for (int ks = 0; ks < D / 16; ++ks)
           s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(kr + 16 * ks)), qf[ks], s[rb], 0, 0, 0);
       }
-      {
-        // keep the K operand reads four MFMAs ahead of their use
-        constexpr int N = (BK / 32) * (D / 16);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      // K operand reads four MFMAs ahead of their use
+      constexpr int N = (BK / 32) * (D / 16);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-        for (int i = 0; i < N - 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      for (int i = 0; i < N - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      const bool need_mask = (k0 + BK > kmask_from);
-      if (need_mask) {
-        const int lim = a.causal ? min(a.Lk - 1, qrow + off) : a.Lk - 1;
-#pragma unroll
-        for (int rb = 0; rb < BK / 32; ++rb)
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int key = k0 + 32 * rb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-            s[rb][rr] = key <= lim ? s[rb][rr] : maskval;
-          }
-        softmax(s, std::true_type{});
-      } else {
-        softmax(s, std::false_type{});
-      }
-      if (lag) pending = true;
-      else pv(vs_);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
-    if (j + 1 < nt) store_tile(j + 1);
+  };
+  auto soft = [&](int jj) {
+    if (!active(jj)) return;
+    const int k0 = jj * BK;
+    if (k0 + BK > kmask_from) {
+      const int lim = a.causal ? min(a.Lk - 1, qrow + off) : a.Lk - 1;
+#pragma unroll
+      for (int rb = 0; rb < BK / 32; ++rb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int key = k0 + 32 * rb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+          s[rb][rr] = key <= lim ? s[rb][rr] : maskval;
+        }
+      softmax(s, std::true_type{});
+    } else {
+      softmax(s, std::false_type{});
+    }
+  };
+
+  load_tile(0, 0);
+  store_tile(0, 0, true, false);
+  __syncthreads();
+  for (int j = 0; j <= nt; ++j) {
+    const bool ldk = j + 1 < nt, ldv = j < nt;
+    if (ldk || ldv) load_tile(min(j + 1, nt - 1), min(j, nt - 1));
+    // phase 2j
+    if (grpA) {
+      if (ATTN_PF_PRIO) __builtin_amdgcn_s_setprio(1);
+      gemm(j);
+      if (ATTN_PF_PRIO) __builtin_amdgcn_s_setprio(0);
+    } else {
+      soft(j - 1);
+    }
+    __syncthreads();
+    // phase 2j+1
+    if (grpA) {
+      soft(j);
+    } else {
+      if (ATTN_PF_PRIO) __builtin_amdgcn_s_setprio(1);
+      gemm(j);
+      if (ATTN_PF_PRIO) __builtin_amdgcn_s_setprio(0);
+    }
+    if (ldk || ldv) store_tile(j + 1, j, ldk, ldv);
     __syncthreads();
   }
-  if (pending) pv(vbuf + ((nt - 1) % C::VBUFS) * C::V_ELEMS);
 
   // ---- epilogue: out = O / l, lse = m ln2 + ln l -------------------------
   const float lt = pair_sum(l_run);
@@ -350,6 +358,28 @@ static hipError_t launch_t(const PrefillArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Query-row packing of the kernel above: 8 waves x 32 rows per workgroup.
+bool prefill_plan(PrefillArgs &a, int D) {
+  (void)D;
+  const int nw = 8;
+  const int rows = 32;
+  int g = a.G, x = nw;
+  while (x) {
+    const int t = g % x;
+    g = x;
+    x = t;
+  }
+  a.hpw = g;                       // query heads per workgroup: gcd(G, waves)
+  a.wph = nw / a.hpw;              // waves per head
+  a.Bq = rows * a.wph;             // query rows per head per workgroup
+  a.n_qblk = (a.Lq + a.Bq - 1) / a.Bq;
+  a.n_hg = a.G / a.hpw;
+  const long long total = (long long)a.n_qblk * a.Hkv * a.n_hg * a.B;
+  if (total > 0x7fffffffLL) return false;
+  a.total = (int)total;
+  return true;
+}
+
 hipError_t launch_prefill(const PrefillArgs &a, int D, hipStream_t s) {
   switch (D) {
     case 64: return launch_t<64, 64>(a, s);
@@ -358,7 +388,5 @@ hipError_t launch_prefill(const PrefillArgs &a, int D, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
 }
-
-int prefill_waves() { return PrefillCfg<128, 64>::NW; }
 
 }  // namespace attn
