@@ -37,8 +37,8 @@ def _load(path: str = LIB_PATH):
     lib.attn_decode_ex.restype = i
     lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.attn_decode_workspace_bytes.restype = sz
-    lib.attn_decode_split_keys.argtypes = [i, i, i]
-    lib.attn_decode_split_keys.restype = i
+    lib.attn_decode_waves.argtypes = [i, i, i, i, i, i]
+    lib.attn_decode_waves.restype = i
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
     return lib
@@ -126,7 +126,7 @@ def decode(q, kcache, vcache, kv_lens, scale: float | None = None, out=None):
 
 def decode_ex(q, kcache, vcache, kv_lens, scale: float | None = None, split_keys: int = 0, out=None,
               return_lse: bool = True, workspace=None):
-    """attn_decode_ex: decode plus lse [B,Hq] fp32, a chunk-size override and an optional workspace."""
+    """attn_decode_ex: decode plus lse [B,Hq] fp32, a key-range size override and an optional workspace."""
     B, Hq, Hkv, Lmax, D = _decode_shapes(q, kcache, vcache, kv_lens)
     if out is None:
         out = torch.empty_like(q)
@@ -143,8 +143,8 @@ def decode_workspace_bytes(B, Hq, Hkv, Lmax, D, split_keys=0) -> int:
     return int(lib.attn_decode_workspace_bytes(B, Hq, Hkv, Lmax, D, split_keys))
 
 
-def decode_split_keys(B, Hkv, Lmax) -> int:
-    return int(lib.attn_decode_split_keys(B, Hkv, Lmax))
+def decode_waves(B, Hq, Hkv, Lmax, D, split_keys=0) -> int:
+    return int(lib.attn_decode_waves(B, Hq, Hkv, Lmax, D, split_keys))
 
 
 def _decode_shapes(q, kcache, vcache, kv_lens):
@@ -159,5 +159,5 @@ def _decode_shapes(q, kcache, vcache, kv_lens):
     return B, Hq, Hkv, Lmax, D
 
 
-__all__ = ["prefill", "decode", "decode_ex", "decode_workspace_bytes", "decode_split_keys", "AttnError", "lib",
+__all__ = ["prefill", "decode", "decode_ex", "decode_workspace_bytes", "decode_waves", "AttnError", "lib",
            "LIB_PATH", "default_scale"]

@@ -44,34 +44,57 @@ hipError_t device_pool(hipMemPool_t *pool) {
   return hipSuccess;
 }
 
-int decode_split_auto(int B, int Hkv, int Lmax) {
-  // Aim for about 16K chunk-workgroups over the allocated cache extent (the
-  // lengths are on the device), in powers of two between 256 and 1024 keys.
-  const double work = (double)B * Hkv * Lmax;
-  int s = 1024;
-  while (s > 256 && work / s < 16384.0) s >>= 1;
-  return s;
-}
-
 struct DecodeShape {
-  int split, nsplit;
-  size_t part_o_bytes, part_lse_bytes, total;
+  int waves;        // main-kernel waves (ranges of the flat key-block space)
+  size_t pre_bytes, part_lse_bytes, part_o_bytes, total;
 };
 
-int decode_shape(int B, int Hq, int Hkv, int Lmax, int D, int split_keys, DecodeShape *ds) {
-  if (split_keys != 0 && (split_keys < 0 || split_keys % 128 != 0)) return ATTN_ERR_SPLIT;
-  const int split = split_keys ? split_keys : decode_split_auto(B, Hkv, Lmax);
-  const int nsplit = (int)(((long long)Lmax + split - 1) / split);
-  ds->split = split;
-  ds->nsplit = nsplit;
-  if (nsplit <= 1) {
-    ds->part_o_bytes = ds->part_lse_bytes = ds->total = 0;
-    return ATTN_OK;
-  }
-  const size_t rows = (size_t)B * Hq * nsplit;
-  ds->part_o_bytes = (rows * D * sizeof(float) + 255) & ~(size_t)255;
-  ds->part_lse_bytes = (rows * sizeof(float) + 255) & ~(size_t)255;
-  ds->total = ds->part_o_bytes + ds->part_lse_bytes;
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace layout: pre [B + 1] int64 | part_lse [slots][GW] | part_o [slots][GW][D],
+// slots = kDecodeMaxWaves + B * Hkv * n_hg (independent of the device).
+void decode_workspace(int B, int Hq, int Hkv, int D, DecodeShape *ds) {
+  const int G = Hq / Hkv;
+  const long long hh = (long long)Hkv * ((G + 63) / 64);
+  const long long gw = G < 64 ? G : 64;
+  const size_t slots = (size_t)attn::kDecodeMaxWaves + (size_t)B * hh;
+  ds->pre_bytes = align256((size_t)(B + 1) * sizeof(long long));
+  ds->part_lse_bytes = align256(slots * gw * sizeof(float));
+  ds->part_o_bytes = align256(slots * gw * D * sizeof(float));
+  ds->total = ds->pre_bytes + ds->part_lse_bytes + ds->part_o_bytes;
+}
+
+// Waves of the main kernel: all resident wave slots of the device by default;
+// with split_keys, enough waves that no wave gets more than split_keys keys
+// when every sequence has Lmax keys (capped at kDecodeMaxWaves).
+std::mutex g_occ_mu;
+int g_occ_cache[64][3][3];
+
+int device_waves(int D, int G, int *waves) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return ATTN_ERR_HIP;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return ATTN_ERR_HIP;
+  const int gw = G < 64 ? G : 64;
+  const int ci = (gw + 15) / 16 >= 3 ? 2 : (gw + 15) / 16 - 1;
+  const int di = D == 64 ? 0 : (D == 128 ? 1 : 2);
+  std::lock_guard<std::mutex> lk(g_occ_mu);
+  int &occ = g_occ_cache[dev][di][ci];
+  if (occ == 0 && attn::decode_waves_per_cu(D, G, &occ) != hipSuccess) return ATTN_ERR_HIP;
+  const long long w = (long long)cus * (occ > 0 ? occ : 1);
+  *waves = (int)(w < attn::kDecodeMaxWaves ? w : attn::kDecodeMaxWaves);
+  return ATTN_OK;
+}
+
+int decode_waves(int B, int Hq, int Hkv, int Lmax, int D, int split_keys, int *waves) {
+  if (split_keys == 0) return device_waves(D, Hq / Hkv, waves);
+  const int G = Hq / Hkv;
+  const double keys = (double)B * Hkv * ((G + 63) / 64) * (double)((Lmax + 31) / 32) * 32.0;
+  double w = keys / split_keys;
+  if (w < 1) w = 1;
+  if (w > attn::kDecodeMaxWaves) w = attn::kDecodeMaxWaves;
+  *waves = (int)w;
+  if (*waves < w) ++*waves;
+  if (*waves > attn::kDecodeMaxWaves) *waves = attn::kDecodeMaxWaves;
   return ATTN_OK;
 }
 
@@ -82,8 +105,7 @@ int decode_check(const void *q, const void *kc, const void *vc, const int32_t *l
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
   if (B < 0 || Lmax < 1 || B > 65535) return ATTN_ERR_SHAPE;
   if (B > 0 && (!q || !kc || !vc || !lens || !out)) return ATTN_ERR_NULL;
-  const int n_hg = (Hq / Hkv + 63) / 64;
-  if ((long long)Hkv * n_hg > 65535) return ATTN_ERR_SHAPE;
+  if ((long long)B * Hq > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   // element counts must fit comfortably in 64-bit offsets
   if ((double)B * Hkv * (double)Lmax * D > 9.0e18) return ATTN_ERR_SHAPE;
   return ATTN_OK;
@@ -94,21 +116,24 @@ int run_decode(const void *q, const void *kc, const void *vc, const int32_t *len
                void *stream) {
   int st = decode_check(q, kc, vc, lens, out, B, Hq, Hkv, Lmax, D, scale);
   if (st != ATTN_OK) return st;
+  if (split_keys != 0 && (split_keys < 0 || split_keys % 128 != 0)) return ATTN_ERR_SPLIT;
   DecodeShape ds;
-  st = decode_shape(B, Hq, Hkv, Lmax, D, split_keys, &ds);
-  if (st != ATTN_OK) return st;
+  decode_workspace(B, Hq, Hkv, D, &ds);
   if (ws != nullptr && ws_bytes < ds.total) return ATTN_ERR_WORKSPACE;
   if (B == 0) return ATTN_OK;
+  st = decode_waves(B, Hq, Hkv, Lmax, D, split_keys, &ds.waves);
+  if (st != ATTN_OK) return st;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   void *mem = ws;
   bool owned = false;
-  if (ds.total > 0 && mem == nullptr) {
+  if (mem == nullptr) {
     hipMemPool_t pool;
     if (device_pool(&pool) != hipSuccess) return ATTN_ERR_HIP;
     if (hipMallocFromPoolAsync(&mem, ds.total, pool, s) != hipSuccess) return ATTN_ERR_HIP;
     owned = true;
   }
+  char *base = static_cast<char *>(mem);
   DecodeArgs a;
   a.q = static_cast<const uint16_t *>(q);
   a.kc = static_cast<const uint16_t *>(kc);
@@ -116,18 +141,17 @@ int run_decode(const void *q, const void *kc, const void *vc, const int32_t *len
   a.lens = lens;
   a.out = static_cast<uint16_t *>(out);
   a.lse = lse;
-  a.part_o = ds.total ? static_cast<float *>(mem) : nullptr;
-  a.part_lse = ds.total ? reinterpret_cast<float *>(static_cast<char *>(mem) + ds.part_o_bytes) : nullptr;
+  a.pre = reinterpret_cast<long long *>(base);
+  a.part_lse = reinterpret_cast<float *>(base + ds.pre_bytes);
+  a.part_o = reinterpret_cast<float *>(base + ds.pre_bytes + ds.part_lse_bytes);
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.Lmax = Lmax;
   a.G = Hq / Hkv;
   a.n_hg = (a.G + 63) / 64;
-  a.split = ds.split;
-  a.nsplit = ds.nsplit;
   a.c = scale * kLog2e;
-  hipError_t e = attn::launch_decode(a, D, s);
+  hipError_t e = attn::launch_decode(a, D, ds.waves, s);
   if (owned) {
     hipError_t f = hipFreeAsync(mem, s);
     if (e == hipSuccess) e = f;
@@ -184,14 +208,17 @@ int attn_decode_ex(const void *q, const void *kcache, const void *vcache, const 
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Lmax, int D, int split_keys) {
   if (B <= 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || !head_dim_ok(D) || Lmax < 1) return 0;
+  if (split_keys != 0 && (split_keys < 0 || split_keys % 128 != 0)) return 0;
   DecodeShape ds;
-  if (decode_shape(B, Hq, Hkv, Lmax, D, split_keys, &ds) != ATTN_OK) return 0;
+  decode_workspace(B, Hq, Hkv, D, &ds);
   return ds.total;
 }
 
-int attn_decode_split_keys(int B, int Hkv, int Lmax) {
-  if (B < 1 || Hkv < 1 || Lmax < 1) return 0;
-  return decode_split_auto(B, Hkv, Lmax);
+int attn_decode_waves(int B, int Hq, int Hkv, int Lmax, int D, int split_keys) {
+  if (B <= 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || !head_dim_ok(D) || Lmax < 1) return 0;
+  if (split_keys != 0 && (split_keys < 0 || split_keys % 128 != 0)) return 0;
+  int w = 0;
+  return decode_waves(B, Hq, Hkv, Lmax, D, split_keys, &w) == ATTN_OK ? w : 0;
 }
 
 const char *attn_status_string(int status) {

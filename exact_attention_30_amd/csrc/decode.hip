@@ -16,10 +16,16 @@
 // exp(l_c - lse) o_c (it follows from splitting the softmax sum).
 //
 // gfx950 design
-//  * One wave64 workgroup per (sequence, KV head, chunk of `split` keys); it
-//    streams its K and V rows once, for all G query heads together.
-//    Workgroups whose chunk lies past the sequence's length exit at once (the
-//    lengths stay on the device).
+//  * Balanced flat split.  A one-workgroup planner kernel turns the device-side
+//    lengths into a prefix sum of 32-key blocks per sequence.  The main kernel
+//    runs exactly W persistent wave64 workgroups (one per resident wave slot);
+//    the key blocks of all (sequence, KV head) segments, laid end to end, are
+//    cut into W equal ranges, one per wave.  A wave streams its range once, for
+//    all G query heads of each segment together, and writes one partial
+//    (normalised O, lse) per segment piece it covers -- or the final output
+//    when its piece is the whole segment.  Every wave does the same amount of
+//    work whatever the length mix, nothing is launched for empty chunks, and
+//    there are at most W + (number of segments) partials.
 //  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: keys on the M side (16 per
 //    block, two blocks per 32-key step), up to 16 query heads on the N side per
 //    column block.  K rows are loaded straight from HBM into the A-operand
@@ -30,15 +36,53 @@
 //  * The next 32-key block's K and V loads are issued before the current
 //    block is computed (two register sets), keeping 16 KiB per wave in flight.
 //  * Lazy max update as in the prefill kernel.
-//  * A chunk that is a sequence's only chunk writes the final bf16 output; the
-//    others write fp32 partials that the combine kernel merges.
+//  * The combine kernel (one wave per query row) merges the partials of the
+//    segments that were split between waves.
 #include "common.h"
 #include "kernels.h"
 
 namespace attn {
 
+// Which wave's range contains flat block x, for the balanced split of `total`
+// blocks over W waves (the first total % W waves take one block more).
+ATTN_DEV long long wave_of(long long x, long long total, long long W) {
+  const long long q = total / W, rem = total % W;
+  const long long big = (q + 1) * rem;
+  if (x < big) return x / (q + 1);
+  return rem + (x - big) / q;
+}
+
+// Planner: pre[b] = sum over b' < b of ceil(min(max(lens[b'], 0), Lmax) / 32),
+// pre[B] = the total.  One workgroup of 1024 threads; each thread owns a
+// contiguous slice of sequences.
+__global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a) {
+  __shared__ long long part[1024];
+  const int t = threadIdx.x;
+  const int per = (a.B + 1023) / 1024;
+  const int b0 = min(a.B, t * per), b1 = min(a.B, b0 + per);
+  long long sum = 0;
+  for (int b = b0; b < b1; ++b) sum += (max(0, min(a.lens[b], a.Lmax)) + 31) / 32;
+  part[t] = sum;
+  __syncthreads();
+  // inclusive scan of the 1024 slice sums (Hillis-Steele)
+  for (int sh = 1; sh < 1024; sh <<= 1) {
+    const long long v = t >= sh ? part[t - sh] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  long long run = part[t] - sum;  // exclusive prefix of this slice
+  for (int b = b0; b < b1; ++b) {
+    a.pre[b] = run;
+    run += (max(0, min(a.lens[b], a.Lmax)) + 31) / 32;
+  }
+  if (t == 1023) a.pre[a.B] = part[1023];
+}
+
+// One query-column block: two waves per SIMD (256 registers each); more
+// column blocks need the whole register file.
 template <int D, int NCB>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2 : 1))) void decode_main_kernel(DecodeArgs a) {
   constexpr int KST = D / 32;            // 32-dim MFMA steps over the head dim
   constexpr int NKR = 2 * KST;           // K registers (16 B each) per 32-key block
   constexpr int VUN = D / 2;             // (8 keys x 8 dims) units per 32-key block
@@ -47,295 +91,366 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t vt[D * VTS];
 
   const int lane = threadIdx.x;
-  const int b = blockIdx.z;
-  const int hkv = blockIdx.y / a.n_hg;
-  const int hg = blockIdx.y - hkv * a.n_hg;
-  const int chunk = blockIdx.x;
   const int ql = lane & 15, g = lane >> 4;
-  const int gq0 = hg * 64;
-  const int gcnt = min(64, a.G - gq0);
-  const int n = max(0, min(a.lens[b], a.Lmax));
-  const int nch = (n + a.split - 1) / a.split;
+  const long long W = gridDim.x, w = blockIdx.x;
+  const long long HH = (long long)a.Hkv * a.n_hg;
+  const long long total = a.pre[a.B] * HH;  // key blocks of all segments
+  const long long q = total / W, rem = total % W;
+  long long r = q * w + min(w, rem);
+  const long long r1 = r + q + (w < rem ? 1 : 0);
+  if (r >= r1) return;
 
-  if (n == 0) {
-    // empty sequence: out = 0, lse = -inf (written once, by chunk 0)
-    if (chunk == 0) {
-      for (int qi = 0; qi < gcnt; ++qi) {
-        const size_t row = (size_t)b * a.Hq + hkv * a.G + gq0 + qi;
-        for (int d = lane; d < D; d += 64) a.out[row * D + d] = 0;
-        if (a.lse != nullptr && lane == 0) a.lse[row] = -__builtin_inff();
-      }
+  // segment holding block r: the largest b with HH * pre[b] <= r
+  int b;
+  {
+    int lo = 0, hi = a.B;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (HH * a.pre[mid] <= r) lo = mid;
+      else hi = mid;
     }
-    return;
+    b = lo;
   }
-  if (chunk >= nch) return;
-  const int k0 = chunk * a.split;
-  const int k1 = min(n, k0 + a.split);
+  long long nb = a.pre[b + 1] - a.pre[b];
+  long long off = r - HH * a.pre[b];
+  int hh = (int)(off / nb);
+  long long blk = off - hh * nb;
 
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  bf16x8 qf[NCB][KST];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    const int qi = 16 * cb + ql;
-    const uint16_t *qp = a.q + ((size_t)b * a.Hq + hkv * a.G + gq0 + min(qi, gcnt - 1)) * D + (D / 4) * g;
-#pragma unroll
-    for (int ks = 0; ks < KST; ++ks) qf[cb][ks] = as_bf16x8(qi < gcnt ? ld16(qp + 8 * ks) : zero4);
-  }
-
-  const size_t base = ((size_t)b * a.Hkv + hkv) * (size_t)a.Lmax * D;
-  const uint16_t *kg = a.kc + base;
-  const uint16_t *vg = a.vc + base;
-
-  f32x4 o[NCB][D / 16];
-  float m_run[NCB], l_run[NCB];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    m_run[cb] = -__builtin_inff();
-    l_run[cb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) o[cb][db] = f32x4{};
-  }
   const float cexp = a.c;
   const bool cpos = cexp >= 0.f;
   const float maskval = cpos ? -__builtin_inff() : __builtin_inff();
+  const int GW = min(a.G, 64);
 
-  auto load = [&](u32x4(&kr)[NKR], u32x4(&vr)[VU][8], int kb) {
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int key = kb + 16 * rb + ql;
-      const uint16_t *p = kg + (size_t)key * D + (D / 4) * g;
-#pragma unroll
-      for (int ks = 0; ks < KST; ++ks) kr[rb * KST + ks] = key < k1 ? ld16(p + 8 * ks) : zero4;
-    }
-#pragma unroll
-    for (int iu = 0; iu < VU; ++iu) {
-      const int u = lane + 64 * iu;
-      if (VUN % 64 == 0 || u < VUN) {
-        const int c = u % (D / 8), gg = u / (D / 8);
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const int key = kb + (kk < 4 ? 4 * gg + kk : 16 + 4 * gg + kk - 4);
-          vr[iu][kk] = key < k1 ? ld16(vg + (size_t)key * D + 8 * c) : zero4;
-        }
-      }
-    }
-  };
+  while (r < r1) {
+    const long long take = min(nb - blk, r1 - r);
+    const int hkv = hh / a.n_hg, hg = hh - hkv * a.n_hg;
+    const int gq0 = hg * 64;
+    const int gcnt = min(64, a.G - gq0);
+    const int n = max(0, min(a.lens[b], a.Lmax));
+    const int k0 = (int)(blk * 32);
+    const int k1 = min(n, (int)((blk + take) * 32));
+    const bool whole = (blk == 0) && (take == nb);
+    const long long slot = (long long)b * HH + hh + w;
 
-  auto compute = [&](const u32x4(&kr)[NKR], const u32x4(&vr)[VU][8], int kb) {
-    // V block -> V^T in LDS, keys in the order the P^T operand holds them
-#pragma unroll
-    for (int iu = 0; iu < VU; ++iu) {
-      const int u = lane + 64 * iu;
-      if (VUN % 64 == 0 || u < VUN) {
-        const int c = u % (D / 8), gg = u / (D / 8);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int w4 = i >> 1;
-          u32x4 t;
-          if (i & 1) {
-            t[0] = pack_hi16(vr[iu][0][w4], vr[iu][1][w4]);
-            t[1] = pack_hi16(vr[iu][2][w4], vr[iu][3][w4]);
-            t[2] = pack_hi16(vr[iu][4][w4], vr[iu][5][w4]);
-            t[3] = pack_hi16(vr[iu][6][w4], vr[iu][7][w4]);
-          } else {
-            t[0] = pack_lo16(vr[iu][0][w4], vr[iu][1][w4]);
-            t[1] = pack_lo16(vr[iu][2][w4], vr[iu][3][w4]);
-            t[2] = pack_lo16(vr[iu][4][w4], vr[iu][5][w4]);
-            t[3] = pack_lo16(vr[iu][6][w4], vr[iu][7][w4]);
-          }
-          st16(vt + (8 * c + i) * VTS + 8 * gg, t);
-        }
-      }
-    }
-    // S^T = K Q^T: 32 keys x 16 queries per column block
-    f32x4 s[NCB][2];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        s[cb][rb] = f32x4{};
-#pragma unroll
-        for (int ks = 0; ks < KST; ++ks)
-          s[cb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[rb * KST + ks]), qf[cb][ks], s[cb][rb], 0, 0, 0);
-      }
-    __syncthreads();
-    const bool partial = kb + 32 > k1;
-    bf16x8 pb[NCB];
+    bf16x8 qf[NCB][KST];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-      uint32_t vis = 0xffu;
-      if (partial) {
-        vis = 0;
+      const int qi = 16 * cb + ql;
+      const uint16_t *qp = a.q + ((size_t)b * a.Hq + hkv * a.G + gq0 + min(qi, gcnt - 1)) * D + (D / 4) * g;
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+      for (int ks = 0; ks < KST; ++ks) qf[cb][ks] = as_bf16x8(qi < gcnt ? ld16(qp + 8 * ks) : zero4);
+    }
+    const size_t base = ((size_t)b * a.Hkv + hkv) * (size_t)a.Lmax * D;
+    const uint16_t *kg = a.kc + base;
+    const uint16_t *vg = a.vc + base;
+
+    f32x4 o[NCB][D / 16];
+    float m_run[NCB], l_run[NCB];
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const bool vv = kb + 16 * rb + 4 * g + rr < k1;
-            vis |= (vv ? 1u : 0u) << (4 * rb + rr);
-            s[cb][rb][rr] = vv ? s[cb][rb][rr] : maskval;
+    for (int cb = 0; cb < NCB; ++cb) {
+      m_run[cb] = -__builtin_inff();
+      l_run[cb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) o[cb][db] = f32x4{};
+    }
+
+    auto load = [&](u32x4(&kr)[NKR], u32x4(&vr)[VU][8], int kb) {
+  #pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int key = kb + 16 * rb + ql;
+        const uint16_t *p = kg + (size_t)key * D + (D / 4) * g;
+  #pragma unroll
+        for (int ks = 0; ks < KST; ++ks) kr[rb * KST + ks] = key < k1 ? ld16(p + 8 * ks) : zero4;
+      }
+  #pragma unroll
+      for (int iu = 0; iu < VU; ++iu) {
+        const int u = lane + 64 * iu;
+        if (VUN % 64 == 0 || u < VUN) {
+          const int c = u % (D / 8), gg = u / (D / 8);
+  #pragma unroll
+          for (int kk = 0; kk < 8; ++kk) {
+            const int key = kb + (kk < 4 ? 4 * gg + kk : 16 + 4 * gg + kk - 4);
+            vr[iu][kk] = key < k1 ? ld16(vg + (size_t)key * D + 8 * c) : zero4;
           }
-      }
-      float red;
-      if (cpos) {
-        red = fmax3(s[cb][0][0], s[cb][0][1], s[cb][0][2]);
-        red = fmax3(red, s[cb][0][3], s[cb][1][0]);
-        red = fmax3(red, s[cb][1][1], s[cb][1][2]);
-        red = __builtin_fmaxf(red, s[cb][1][3]);
-        red = __builtin_fmaxf(red, xor16(red));
-        red = __builtin_fmaxf(red, xor32(red));
-      } else {
-        red = fmin3(s[cb][0][0], s[cb][0][1], s[cb][0][2]);
-        red = fmin3(red, s[cb][0][3], s[cb][1][0]);
-        red = fmin3(red, s[cb][1][1], s[cb][1][2]);
-        red = __builtin_fminf(red, s[cb][1][3]);
-        red = __builtin_fminf(red, xor16(red));
-        red = __builtin_fminf(red, xor32(red));
-      }
-      const float mt = red * cexp;
-      const bool need = mt > m_run[cb] + ATTN_RESCALE_SLACK;
-      if (wave_any(need)) {
-        const float mnew = need ? mt : m_run[cb];
-        const float alpha = need ? fast_exp2(m_run[cb] - mnew) : 1.f;
-        l_run[cb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 16; ++db) o[cb][db] *= alpha;
-        m_run[cb] = mnew;
-      }
-      const float nm = -m_run[cb];
-      float p[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float e = fast_exp2(__builtin_fmaf(s[cb][i >> 2][i & 3], cexp, nm));
-        if (partial) e = ((vis >> i) & 1u) ? e : 0.f;
-        p[i] = e;
-      }
-      l_run[cb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-      pb[cb] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-    }
-    // O^T += V^T P^T
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-      const bf16x8 vop = as_bf16x8(ld16(vt + (16 * db + ql) * VTS + 8 * g));
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-        o[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[cb], o[cb][db], 0, 0, 0);
-    }
-    __syncthreads();
-  };
-
-  const int nblk = (k1 - k0 + 31) / 32;
-  if constexpr (D <= 128) {
-    // two register sets: block i+1 is in flight while block i is computed
-    u32x4 kA[NKR], kB[NKR];
-    u32x4 vA[VU][8], vB[VU][8];
-    load(kA, vA, k0);
-    for (int bi = 0; bi < nblk; bi += 2) {
-      if (bi + 1 < nblk) load(kB, vB, k0 + 32 * (bi + 1));
-      compute(kA, vA, k0 + 32 * bi);
-      if (bi + 1 >= nblk) break;
-      if (bi + 2 < nblk) load(kA, vA, k0 + 32 * (bi + 2));
-      compute(kB, vB, k0 + 32 * (bi + 1));
-    }
-  } else {
-    // D = 256: one register set (a second would not fit next to the accumulators)
-    u32x4 kA[NKR];
-    u32x4 vA[VU][8];
-    for (int bi = 0; bi < nblk; ++bi) {
-      load(kA, vA, k0 + 32 * bi);
-      compute(kA, vA, k0 + 32 * bi);
-    }
-  }
-
-  // ---- write this chunk's result -----------------------------------------
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    float lt = l_run[cb];
-    lt += xor16(lt);
-    lt += xor32(lt);
-    const float inv = 1.f / lt;
-    const int qi = 16 * cb + ql;
-    if (qi < gcnt) {
-      const size_t row = (size_t)b * a.Hq + hkv * a.G + gq0 + qi;
-      const float lse_c = m_run[cb] * ATTN_LN2 + __logf(lt);
-      if (nch == 1) {
-#pragma unroll
-        for (int db = 0; db < D / 16; ++db) {
-          bf16x4 v4;
-          v4[0] = (__bf16)(o[cb][db][0] * inv);
-          v4[1] = (__bf16)(o[cb][db][1] * inv);
-          v4[2] = (__bf16)(o[cb][db][2] * inv);
-          v4[3] = (__bf16)(o[cb][db][3] * inv);
-          *reinterpret_cast<bf16x4 *>(a.out + row * D + 16 * db + 4 * g) = v4;
         }
-        if (a.lse != nullptr && g == 0) a.lse[row] = lse_c;
-      } else {
-        float *po = a.part_o + (row * a.nsplit + chunk) * D;
-#pragma unroll
-        for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4 *>(po + 16 * db + 4 * g) = o[cb][db] * inv;
-        if (g == 0) a.part_lse[row * a.nsplit + chunk] = lse_c;
       }
+    };
+
+    auto compute = [&](const u32x4(&kr)[NKR], const u32x4(&vr)[VU][8], int kb) {
+      // V block -> V^T in LDS, keys in the order the P^T operand holds them
+  #pragma unroll
+      for (int iu = 0; iu < VU; ++iu) {
+        const int u = lane + 64 * iu;
+        if (VUN % 64 == 0 || u < VUN) {
+          const int c = u % (D / 8), gg = u / (D / 8);
+  #pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int w4 = i >> 1;
+            u32x4 t;
+            if (i & 1) {
+              t[0] = pack_hi16(vr[iu][0][w4], vr[iu][1][w4]);
+              t[1] = pack_hi16(vr[iu][2][w4], vr[iu][3][w4]);
+              t[2] = pack_hi16(vr[iu][4][w4], vr[iu][5][w4]);
+              t[3] = pack_hi16(vr[iu][6][w4], vr[iu][7][w4]);
+            } else {
+              t[0] = pack_lo16(vr[iu][0][w4], vr[iu][1][w4]);
+              t[1] = pack_lo16(vr[iu][2][w4], vr[iu][3][w4]);
+              t[2] = pack_lo16(vr[iu][4][w4], vr[iu][5][w4]);
+              t[3] = pack_lo16(vr[iu][6][w4], vr[iu][7][w4]);
+            }
+            st16(vt + (8 * c + i) * VTS + 8 * gg, t);
+          }
+        }
+      }
+      // S^T = K Q^T: 32 keys x 16 queries per column block
+      f32x4 s[NCB][2];
+  #pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+  #pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          s[cb][rb] = f32x4{};
+  #pragma unroll
+          for (int ks = 0; ks < KST; ++ks)
+            s[cb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[rb * KST + ks]), qf[cb][ks], s[cb][rb], 0, 0, 0);
+        }
+      __syncthreads();
+      const bool partial = kb + 32 > k1;
+      bf16x8 pb[NCB];
+  #pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        uint32_t vis = 0xffu;
+        if (partial) {
+          vis = 0;
+  #pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+  #pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const bool vv = kb + 16 * rb + 4 * g + rr < k1;
+              vis |= (vv ? 1u : 0u) << (4 * rb + rr);
+              s[cb][rb][rr] = vv ? s[cb][rb][rr] : maskval;
+            }
+        }
+        float red;
+        if (cpos) {
+          red = fmax3(s[cb][0][0], s[cb][0][1], s[cb][0][2]);
+          red = fmax3(red, s[cb][0][3], s[cb][1][0]);
+          red = fmax3(red, s[cb][1][1], s[cb][1][2]);
+          red = __builtin_fmaxf(red, s[cb][1][3]);
+          red = __builtin_fmaxf(red, xor16(red));
+          red = __builtin_fmaxf(red, xor32(red));
+        } else {
+          red = fmin3(s[cb][0][0], s[cb][0][1], s[cb][0][2]);
+          red = fmin3(red, s[cb][0][3], s[cb][1][0]);
+          red = fmin3(red, s[cb][1][1], s[cb][1][2]);
+          red = __builtin_fminf(red, s[cb][1][3]);
+          red = __builtin_fminf(red, xor16(red));
+          red = __builtin_fminf(red, xor32(red));
+        }
+        const float mt = red * cexp;
+        const bool need = mt > m_run[cb] + ATTN_RESCALE_SLACK;
+        if (wave_any(need)) {
+          const float mnew = need ? mt : m_run[cb];
+          const float alpha = need ? fast_exp2(m_run[cb] - mnew) : 1.f;
+          l_run[cb] *= alpha;
+  #pragma unroll
+          for (int db = 0; db < D / 16; ++db) o[cb][db] *= alpha;
+          m_run[cb] = mnew;
+        }
+        const float nm = -m_run[cb];
+        float p[8];
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float e = fast_exp2(__builtin_fmaf(s[cb][i >> 2][i & 3], cexp, nm));
+          if (partial) e = ((vis >> i) & 1u) ? e : 0.f;
+          p[i] = e;
+        }
+        l_run[cb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        pb[cb] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+      }
+      // O^T += V^T P^T
+  #pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const bf16x8 vop = as_bf16x8(ld16(vt + (16 * db + ql) * VTS + 8 * g));
+  #pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          o[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[cb], o[cb][db], 0, 0, 0);
+      }
+      __syncthreads();
+    };
+
+    const int nblk = (k1 - k0 + 31) / 32;
+    if constexpr (D <= 128) {
+      // two register sets: block i+1 is in flight while block i is computed
+      u32x4 kA[NKR], kB[NKR];
+      u32x4 vA[VU][8], vB[VU][8];
+      load(kA, vA, k0);
+      for (int bi = 0; bi < nblk; bi += 2) {
+        if (bi + 1 < nblk) load(kB, vB, k0 + 32 * (bi + 1));
+        compute(kA, vA, k0 + 32 * bi);
+        if (bi + 1 >= nblk) break;
+        if (bi + 2 < nblk) load(kA, vA, k0 + 32 * (bi + 2));
+        compute(kB, vB, k0 + 32 * (bi + 1));
+      }
+    } else {
+      // D = 256: one register set (a second would not fit next to the accumulators)
+      u32x4 kA[NKR];
+      u32x4 vA[VU][8];
+      for (int bi = 0; bi < nblk; ++bi) {
+        load(kA, vA, k0 + 32 * bi);
+        compute(kA, vA, k0 + 32 * bi);
+      }
+    }
+
+    // ---- this piece's result ---------------------------------------------
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      float lt = l_run[cb];
+      lt += xor16(lt);
+      lt += xor32(lt);
+      const float inv = 1.f / lt;
+      const int qi = 16 * cb + ql;
+      if (qi < gcnt) {
+        const size_t row = (size_t)b * a.Hq + hkv * a.G + gq0 + qi;
+        const float lse_c = m_run[cb] * ATTN_LN2 + __logf(lt);
+        if (whole) {
+#pragma unroll
+          for (int db = 0; db < D / 16; ++db) {
+            bf16x4 v4;
+            v4[0] = (__bf16)(o[cb][db][0] * inv);
+            v4[1] = (__bf16)(o[cb][db][1] * inv);
+            v4[2] = (__bf16)(o[cb][db][2] * inv);
+            v4[3] = (__bf16)(o[cb][db][3] * inv);
+            *reinterpret_cast<bf16x4 *>(a.out + row * D + 16 * db + 4 * g) = v4;
+          }
+          if (a.lse != nullptr && g == 0) a.lse[row] = lse_c;
+        } else {
+          const size_t pr = (size_t)slot * GW + qi;
+          float *po = a.part_o + pr * D;
+#pragma unroll
+          for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4 *>(po + 16 * db + 4 * g) = o[cb][db] * inv;
+          if (g == 0) a.part_lse[pr] = lse_c;
+        }
+      }
+    }
+
+    // ---- next segment (skipping empty sequences) --------------------------
+    r += take;
+    if (r >= r1) break;
+    blk = 0;
+    if (++hh == HH) {
+      hh = 0;
+      do {
+        ++b;
+      } while (b < a.B && a.pre[b + 1] == a.pre[b]);
+      if (b >= a.B) break;  // not reached: r < r1 <= total implies a later block
+      nb = a.pre[b + 1] - a.pre[b];
     }
   }
 }
 
-// Merge the chunks of every (sequence, query head) that has more than one.
+// Merge the pieces of every (sequence, query head) whose segment was split
+// between waves; also writes out = 0 / lse = -inf for empty sequences.  One
+// wave per row: piece lse values are read one per lane (64 per round) and
+// reduced across the wave; each lane accumulates D/64 output elements.
 template <int D>
-__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a, int W) {
   const int row = blockIdx.x;  // b * Hq + h
-  const int b = row / a.Hq;
+  const int b = row / a.Hq, h = row - b * a.Hq;
   const int lane = threadIdx.x;
-  const int n = max(0, min(a.lens[b], a.Lmax));
-  const int nch = (n + a.split - 1) / a.split;
-  if (nch <= 1) return;
-  const float *pl = a.part_lse + (size_t)row * a.nsplit;
-  const float *po = a.part_o + (size_t)row * a.nsplit * D;
+  const int hkv = h / a.G, gfull = h - hkv * a.G;
+  const int hg = gfull / 64, qi = gfull - hg * 64;
+  const long long HH = (long long)a.Hkv * a.n_hg;
+  const long long hh = (long long)hkv * a.n_hg + hg;
+  const long long nb = a.pre[b + 1] - a.pre[b];
+  uint16_t *op = a.out + (size_t)row * D;
+  if (nb == 0) {
+    for (int d = lane; d < D; d += 64) op[d] = 0;
+    if (a.lse != nullptr && lane == 0) a.lse[row] = -__builtin_inff();
+    return;
+  }
+  const long long total = a.pre[a.B] * HH;
+  const long long s0 = HH * a.pre[b] + hh * nb;       // first flat block of the segment
+  const long long w0 = wave_of(s0, total, W), w1 = wave_of(s0 + nb - 1, total, W);
+  if (w0 == w1) return;  // one wave covered it and wrote the result
+  const int GW = min(a.G, 64);
+  const long long seg = (long long)b * HH + hh;
+  const int np = (int)(w1 - w0 + 1);
+  auto prow = [&](int c) { return ((size_t)(seg + w0 + c) * GW + qi); };
   float M = -__builtin_inff();
-  for (int c = 0; c < nch; ++c) M = __builtin_fmaxf(M, pl[c]);
+  for (int c0 = 0; c0 < np; c0 += 64) {
+    const float x = (c0 + lane < np) ? a.part_lse[prow(c0 + lane)] : -__builtin_inff();
+    M = __builtin_fmaxf(M, x);
+  }
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) M = __builtin_fmaxf(M, __shfl_xor(M, sh));
   float Z = 0.f;
   float acc[D / 64];
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) acc[i] = 0.f;
-  for (int c = 0; c < nch; ++c) {
-    const float wgt = __expf(pl[c] - M);
-    Z += wgt;
+  for (int c0 = 0; c0 < np; c0 += 64) {
+    const float wl = (c0 + lane < np) ? __expf(a.part_lse[prow(c0 + lane)] - M) : 0.f;
+    Z += wl;
+    const int cn = min(64, np - c0);
+    for (int c = 0; c < cn; ++c) {
+      const float wgt = __shfl(wl, c);
+      const float *po = a.part_o + prow(c0 + c) * D;
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) acc[i] = __builtin_fmaf(wgt, po[(size_t)c * D + lane + 64 * i], acc[i]);
+      for (int i = 0; i < D / 64; ++i) acc[i] = __builtin_fmaf(wgt, po[lane + 64 * i], acc[i]);
+    }
   }
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) Z += __shfl_xor(Z, sh);
   const float inv = 1.f / Z;
-  uint16_t *op = a.out + (size_t)row * D;
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) {
-    const __bf16 h = (__bf16)(acc[i] * inv);
-    op[lane + 64 * i] = __builtin_bit_cast(uint16_t, h);
+    const __bf16 hv = (__bf16)(acc[i] * inv);
+    op[lane + 64 * i] = __builtin_bit_cast(uint16_t, hv);
   }
   if (a.lse != nullptr && lane == 0) a.lse[row] = M + __logf(Z);
 }
 
 template <int D, int NCB>
-static hipError_t launch_t(const DecodeArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((decode_split_kernel<D, NCB>), dim3(a.nsplit, a.Hkv * a.n_hg, a.B), dim3(64), 0, s, a);
+static hipError_t launch_t(const DecodeArgs &a, int W, hipStream_t s) {
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, s, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.nsplit <= 1) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.Hq), dim3(64), 0, s, a);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_main_kernel<D, NCB>), dim3(W), dim3(64), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.Hq), dim3(64), 0, s, a, W);
   return hipGetLastError();
 }
 
 template <int D>
-static hipError_t launch_d(const DecodeArgs &a, hipStream_t s) {
+static hipError_t launch_d(const DecodeArgs &a, int W, hipStream_t s) {
   const int gw = a.G < 64 ? a.G : 64;
   const int ncb = (gw + 15) / 16;
-  if (ncb == 1) return launch_t<D, 1>(a, s);
-  if (ncb == 2) return launch_t<D, 2>(a, s);
-  return launch_t<D, 4>(a, s);
+  if (ncb == 1) return launch_t<D, 1>(a, W, s);
+  if (ncb == 2) return launch_t<D, 2>(a, W, s);
+  return launch_t<D, 4>(a, W, s);
 }
 
-hipError_t launch_decode(const DecodeArgs &a, int D, hipStream_t s) {
+hipError_t launch_decode(const DecodeArgs &a, int D, int W, hipStream_t s) {
   switch (D) {
-    case 64: return launch_d<64>(a, s);
-    case 128: return launch_d<128>(a, s);
-    case 256: return launch_d<256>(a, s);
+    case 64: return launch_d<64>(a, W, s);
+    case 128: return launch_d<128>(a, W, s);
+    case 256: return launch_d<256>(a, W, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Resident 64-thread workgroups of the main kernel per CU for this shape.
+hipError_t decode_waves_per_cu(int D, int G, int *out) {
+  const int gw = G < 64 ? G : 64;
+  const int ncb = (gw + 15) / 16;
+  const void *f = nullptr;
+#define ATTN_PICK(DD, NN) f = reinterpret_cast<const void *>(&decode_main_kernel<DD, NN>)
+  if (D == 64) { if (ncb == 1) ATTN_PICK(64, 1); else if (ncb == 2) ATTN_PICK(64, 2); else ATTN_PICK(64, 4); }
+  else if (D == 128) { if (ncb == 1) ATTN_PICK(128, 1); else if (ncb == 2) ATTN_PICK(128, 2); else ATTN_PICK(128, 4); }
+  else { if (ncb == 1) ATTN_PICK(256, 1); else if (ncb == 2) ATTN_PICK(256, 2); else ATTN_PICK(256, 4); }
+#undef ATTN_PICK
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, f, 64, 0);
 }
 
 }  // namespace attn

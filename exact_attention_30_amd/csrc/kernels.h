@@ -32,20 +32,23 @@ struct DecodeArgs {
   const int32_t *lens;
   uint16_t *out;
   float *lse;
-  float *part_o;    // [B][Hq][nsplit][D] normalised partial outputs
-  float *part_lse;  // [B][Hq][nsplit]
+  long long *pre;   // [B + 1] prefix sums of 32-key blocks per sequence (planner output)
+  float *part_o;    // [slots][GW][D] normalised piece outputs, slots = waves + B * Hkv * n_hg
+  float *part_lse;  // [slots][GW] piece log-sum-exps
   int B, Hq, Hkv, Lmax;
   int G;            // Hq / Hkv
-  int n_hg;         // groups of up to 64 query heads per KV head
-  int split;        // keys per chunk
-  int nsplit;       // ceil(Lmax / split)
+  int n_hg;         // groups of up to 64 query heads per KV head (GW = min(G, 64))
   float c;          // scale * log2(e)
 };
+
+// Upper bound on the waves of the decode main kernel (sizes the workspace).
+constexpr int kDecodeMaxWaves = 4096;
 
 // Fill in the query-row packing (hpw, wph, Bq, n_qblk, n_hg, total) for the
 // kernel that serves head dim D; false if the grid would be too large.
 bool prefill_plan(PrefillArgs &a, int D);
 hipError_t launch_prefill(const PrefillArgs &a, int D, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs &a, int D, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, int D, int waves, hipStream_t s);
+hipError_t decode_waves_per_cu(int D, int G, int *out);
 
 }  // namespace attn

@@ -111,11 +111,13 @@ int attn_prefill(const void *q, const void *k, const void *v, void *out, float *
  *   kcache, vcache [B][Hkv][Lmax][D] bf16
  *   kv_lens [B] int32, device memory (read on the device only)
  *
- * The keys are split into chunks processed in parallel; each chunk yields a
- * partial output and log-sum-exp, merged by a second kernel.  The partials
- * live in a workspace taken from HIP's stream-ordered allocator on `stream`
- * and released on it.  B == 0 is an empty call (ATTN_OK; pointers may be
- * NULL).
+ * The cached keys of all (sequence, KV head) pairs are laid end to end and cut
+ * into equal ranges, one per wave of the device (a balanced split that does
+ * not depend on the length mix); a pair split between waves gets its partial
+ * outputs and log-sum-exps merged by a final kernel.  A small planner kernel
+ * turns kv_lens into block counts on the device first.  The partials live in
+ * a workspace taken from HIP's stream-ordered allocator on `stream` and
+ * released on it.  B == 0 is an empty call (ATTN_OK; pointers may be NULL).
  */
 int attn_decode(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens,
                 void *out, int B, int Hq, int Hkv, int Lmax, int D, float scale, void *stream);
@@ -123,8 +125,10 @@ int attn_decode(const void *q, const void *kcache, const void *vcache, const int
 /*
  * attn_decode_ex -- attn_decode with three extra controls:
  *   lse        [B][Hq] fp32 output (natural log; -inf where n_b == 0), may be NULL;
- *   split_keys keys per chunk: 0 picks a size from B, Hkv and Lmax; otherwise a
- *              positive multiple of 128 (else ATTN_ERR_SPLIT);
+ *   split_keys 0: one key range per resident wave of the device; otherwise a
+ *              positive multiple of 128 (else ATTN_ERR_SPLIT): enough ranges
+ *              that none would exceed split_keys keys if every sequence had
+ *              Lmax keys (at most 4096 ranges);
  *   workspace  caller-owned device buffer of workspace_bytes for the partials;
  *              NULL takes it from the stream-ordered allocator as attn_decode
  *              does.  If non-NULL it must hold at least
@@ -138,13 +142,17 @@ int attn_decode_ex(const void *q, const void *kcache, const void *vcache, const 
 
 /*
  * attn_decode_workspace_bytes -- bytes of workspace attn_decode_ex needs for
- * these sizes and split_keys (0 = the automatic choice).  Returns 0 for an
+ * these sizes (the same for every split_keys and device).  Returns 0 for an
  * empty call and for invalid arguments.
  */
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Lmax, int D, int split_keys);
 
-/* attn_decode_split_keys -- the chunk size attn_decode picks for these sizes. */
-int attn_decode_split_keys(int B, int Hkv, int Lmax);
+/*
+ * attn_decode_waves -- the number of key ranges (waves) attn_decode_ex uses
+ * for these sizes and split_keys on the current device; 0 for invalid
+ * arguments or when no device is available.
+ */
+int attn_decode_waves(int B, int Hq, int Hkv, int Lmax, int D, int split_keys);
 
 /* attn_status_string -- static, NUL-terminated text for a status code. */
 const char *attn_status_string(int status);

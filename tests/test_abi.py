@@ -91,17 +91,25 @@ def test_decode_validation(attn):
     assert attn.lib.attn_decode(P, P, P, N, P, 1, 8, 2, 64, 128, ctypes.c_float(0.1), None) == -1
 
 
-def test_decode_workspace_and_split_sizes(attn):
-    # one chunk: no partials needed
-    assert attn.decode_workspace_bytes(4, 32, 8, 256, 128, 256) == 0
-    # nsplit = 32768/1024 = 32 partials of D floats + 1 lse per (b, h), each array 256-B aligned
-    rows = 64 * 32 * 32
-    want = ((rows * 128 * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
-    assert attn.decode_workspace_bytes(64, 32, 8, 32768, 128, 1024) == want
+def test_decode_workspace_sizes(attn):
+    # pre [B+1] int64 | lse [slots][GW] | O [slots][GW][D], slots = 4096 + B*Hkv*n_hg, each 256-B aligned
+    def al(x):
+        return (x + 255) // 256 * 256
+    B, Hq, Hkv, D = 64, 32, 8, 128
+    slots = 4096 + B * Hkv
+    want = al((B + 1) * 8) + al(slots * 4 * 4) + al(slots * 4 * D * 4)
+    assert attn.decode_workspace_bytes(B, Hq, Hkv, 32768, D, 0) == want
+    assert attn.decode_workspace_bytes(B, Hq, Hkv, 32768, D, 1024) == want     # independent of the split
+    assert attn.decode_workspace_bytes(B, Hq, Hkv, 10, D, 0) == want           # and of Lmax
+    # G = 80: two head groups of up to 64 heads per KV head
+    slots = 4096 + 3 * 1 * 2
+    assert attn.decode_workspace_bytes(3, 80, 1, 100, 64, 0) == al(4 * 8) + al(slots * 64 * 4) + al(slots * 64 * 64 * 4)
     assert attn.decode_workspace_bytes(1, 3, 2, 10, 128, 0) == 0          # invalid GQA -> 0
-    s = attn.decode_split_keys(64, 8, 32768)
-    assert s in (256, 512, 1024) and s % 128 == 0
-    assert attn.decode_split_keys(32, 1, 8192) == 256
+    assert attn.decode_workspace_bytes(1, 4, 2, 10, 128, 100) == 0        # invalid split -> 0
+    # explicit split: enough ranges that none exceeds split_keys at full length (no device needed)
+    assert attn.decode_waves(4, 32, 8, 32768, 128, 1024) == 4 * 8 * 32
+    assert attn.decode_waves(2, 8, 2, 1000, 128, 256) == 2 * 2 * 4          # ceil(1000/32)*32 = 1024 keys
+    assert attn.decode_waves(64, 32, 8, 32768, 128, 128) == 4096            # capped
 
 
 def test_binding_rejects_cpu_tensors(attn):
