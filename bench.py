@@ -43,7 +43,26 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU seconds per oracle sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy three times (scale for HBM byte counters)")
     return p.parse_args()
+
+
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration():
+    """A copy kernel of known size: reads and writes COPY_BYTES per launch."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(7)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "launches": 3}), flush=True)
 
 
 def kernel_source_hash() -> str:
@@ -161,6 +180,9 @@ def cpu_decode_baseline(case: ai.DecodeCase, lens, seconds: float):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the multi-GPU split is described in DESIGN.md, not built)", file=sys.stderr)
@@ -242,7 +264,7 @@ def main():
                         "causal": True, "flops": pflops, "ms": round(pre_ms, 4)},
             "decode": {"B": dc.B, "Hq": dc.Hq, "Hkv": dc.Hkv, "Lmax": dc.Lmax, "D": dc.D,
                        "lens": "uniform [1024, 32768] seeded", "sum_lens": int(lens.sum()),
-                       "kv_bytes": dbytes, "split_keys": attn.decode_split_keys(dc.B, dc.Hkv, dc.Lmax),
+                       "kv_bytes": dbytes, "waves": attn.decode_waves(dc.B, dc.Hq, dc.Hkv, dc.Lmax, dc.D),
                        "ms": round(dec_ms, 4), "mall_flushed": True},
             "parallelism": "single GPU",
         },
@@ -250,7 +272,7 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": ptraffic},
         "decode": {"value": round(gbps, 1), "unit": "GB/s",
-                   "roofline": {"bound": "hbm", "kernel": "decode_split_kernel<128,1> + decode_combine_kernel<128>",
+                   "roofline": {"bound": "hbm", "kernel": "decode_plan_kernel + decode_main_kernel<128,1> + decode_combine_kernel<128>",
                                 "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                 "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": dtraffic}},
         "kernel_source_hash": src,
