@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU seconds per oracle sample")
+    p.add_argument("--all-configs", action="store_true",
+                   help="time every prefill and decode configuration (one JSON line each) instead of the step")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy three times (scale for HBM byte counters)")
     return p.parse_args()
@@ -178,6 +180,81 @@ def cpu_decode_baseline(case: ai.DecodeCase, lens, seconds: float):
             "sample": f"first {seqs} of the 64 ragged sequences, fp64 numpy, {spent:.1f} s (KV bytes counted as bf16)"}
 
 
+def _time_ms(fn, iters: int, stream, between=None) -> float:
+    """Mean duration of fn() from HIP events recorded on `stream`; `between`
+    runs outside the timed window before each call (the MALL flush)."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for i, (a, b) in enumerate(evs):
+        if between is not None:
+            between(i)
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def all_configs(iters: int):
+    """Every prefill and decode shape of the workload list, timed on the GPU.
+
+    Prefill inputs come from the seeded host generators; the G-sweep decode
+    caches (up to 8.6 GB) are filled on the device from a seeded torch
+    generator with the same N(0,1)-rounded-to-bf16 distribution, since only
+    their timing is taken here (their values are checked in the GPU tests)."""
+    import torch
+    import exact_attention_30_amd as attn
+    from oracle import accounting as acc
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+
+    prefills = [ai.TINY, ai.QWEN_4K, ai.QWEN_16K, ai.QWEN_32K, ai.QWEN_CHUNK, ai.D256]
+    prefills += [ai.gsweep_prefill(G) for G in ai.G_SWEEP]
+    for pc in prefills:
+        q, k, v = to_dev(pc.q_bits(), dev), to_dev(pc.k_bits(), dev), to_dev(pc.v_bits(), dev)
+        out = torch.empty_like(q)
+        lse = torch.empty((pc.B, pc.Hq, pc.Lq), dtype=torch.float32, device=dev)
+        fn = lambda: attn.prefill(q, k, v, causal=True, scale=pc.scale, out=out, lse=lse)  # noqa: E731
+        for _ in range(2):
+            fn()
+        ms = _time_ms(fn, iters, stream)
+        fl = acc.prefill_flops(pc.B, pc.Hq, pc.D, pc.Lq, pc.Lk, True)
+        tf = fl / (ms * 1e-3) / 1e12
+        print(json.dumps({"config": pc.name, "kind": "prefill", "B": pc.B, "Hq": pc.Hq, "Hkv": pc.Hkv, "Lq": pc.Lq,
+                          "Lk": pc.Lk, "D": pc.D, "ms": round(ms, 4), "flops": fl, "TFLOP/s": round(tf, 1),
+                          "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}), flush=True)
+        del q, k, v, out, lse
+
+    decodes = [ai.RAGGED_DECODE] + [ai.gsweep_decode(G) for G in ai.G_SWEEP]
+    gen = torch.Generator(device=dev)
+    for dc in decodes:
+        lens = dc.kv_lens()
+        if dc is ai.RAGGED_DECODE:
+            kc, vc = build_decode_cache(dc, lens, dev)
+        else:
+            shape = (dc.B, dc.Hkv, dc.Lmax, dc.D)
+            gen.manual_seed(dc.wid * 1000 + dc.Hkv)
+            kc = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            vc = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        dq = to_dev(dc.q_bits(), dev)
+        dl = torch.from_numpy(lens).to(dev)
+        dout = torch.empty_like(dq)
+        fn = lambda: attn.decode(dq, kc, vc, dl, scale=dc.scale, out=dout)  # noqa: E731
+        for _ in range(2):
+            fn()
+        ms = _time_ms(fn, iters, stream, between=lambda i: flush.fill_(i & 0xFF))
+        nb = acc.decode_kv_bytes(lens, dc.Hkv, dc.D, dc.Lmax)
+        gbps = nb / (ms * 1e-3) / 1e9
+        print(json.dumps({"config": dc.name, "kind": "decode", "B": dc.B, "Hq": dc.Hq, "Hkv": dc.Hkv,
+                          "Lmax": dc.Lmax, "D": dc.D, "sum_lens": int(lens.sum()), "ms": round(ms, 4),
+                          "kv_bytes": nb, "GB/s": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                          "waves": attn.decode_waves(dc.B, dc.Hq, dc.Hkv, dc.Lmax, dc.D)}), flush=True)
+        del kc, vc
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -187,6 +264,9 @@ def main():
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the multi-GPU split is described in DESIGN.md, not built)", file=sys.stderr)
         sys.exit(2)
+    if args.all_configs:
+        all_configs(max(args.steps, 5))
+        return
     import torch
     import exact_attention_30_amd as attn
     from oracle import accounting as acc
