@@ -75,8 +75,10 @@ ATTN_DEV float pair_sum(float x) {
 // element i % 4 of the chunk of lane 4r + i / 4 for r = 0..3, i.e. column i of
 // the 4 x 16 block.
 ATTN_DEV bf16x4 lds_tr16(const uint16_t *p) {
+  // an address-space cast (not a round trip through an integer) keeps the
+  // pointer's provenance, so the compiler can tell which LDS array is read
   const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4 *)(reinterpret_cast<uintptr_t>(p)));
+      (__attribute__((address_space(3))) i16x4 *)(const_cast<uint16_t *>(p)));
   return __builtin_bit_cast(bf16x4, r);
 }
 

@@ -46,6 +46,10 @@
 #ifndef ATTN_PF_PRIO
 #define ATTN_PF_PRIO 1
 #endif
+//  ATTN_PF_BK128        key-tile size for D = 128
+#ifndef ATTN_PF_BK128
+#define ATTN_PF_BK128 64
+#endif
 
 namespace attn {
 
@@ -53,25 +57,39 @@ template <int D, int BK>
 struct PrefillCfg {
   static constexpr int NW = 8;
   static constexpr int NT = NW * 64;
-  static constexpr int KS = D + 8;       // K row stride in LDS (bf16 elements): +16 B
-  static constexpr int VS = D + 32;      // V row stride in LDS: +64 B
-  static constexpr int K_ELEMS = BK * KS;
-  static constexpr int V_ELEMS = BK * VS;
-  static constexpr int KBUFS = 2;        // K tiles in LDS
-  static constexpr int VBUFS = 2;        // V tiles
-  static constexpr int LDS_ELEMS = KBUFS * K_ELEMS + VBUFS * V_ELEMS;
-  static constexpr int CHUNKS = BK * D / 8;   // 16-byte pieces per tile and tensor
-  static constexpr int PER_T = CHUNKS / NT;
-  static_assert(CHUNKS % NT == 0, "tile must split evenly over the threads");
+  static constexpr int CPR = D / 8;                   // 16-byte chunks per K/V row
+  static constexpr int RPD = 512 / D;                 // rows per 1 KiB direct-to-LDS load
+  static constexpr int TILE = BK * D;                 // elements per K or V tile
+  static constexpr int DPW = TILE * 2 / 1024 / NW;    // (direct loads per tile and tensor) / waves
+  static_assert(DPW * NW * 1024 == TILE * 2, "tile must split evenly over the waves");
   static_assert(BK % 32 == 0 && D % 32 == 0, "tile shape");
 };
+
+// LDS row swizzles.  A tile row is stored unpadded; its 16-byte chunk c sits
+// at chunk c ^ swz(row).  K: the b128 operand reads (16 rows, one chunk) then
+// hit 16 distinct bank groups.  V: the swizzle moves whole 64-byte groups, so
+// each transposing read still finds its 4 chunks together, and 4 consecutive
+// rows land in 4 distinct bank quarters.
+template <int D>
+ATTN_DEV int kswz(int r) { return D == 64 ? ((r >> 1) & 7) : (r & 15); }
+template <int D>
+ATTN_DEV int vswz(int r) { return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3); }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// s_waitcnt vmcnt(0), other counters left alone (expcnt 7, lgkmcnt 15)
+#define ATTN_WAIT_VMEM() __builtin_amdgcn_s_waitcnt(0x0F70)
 
 template <int D, int BK>
 __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
   using C = PrefillCfg<D, BK>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
-  uint16_t *const kbuf = smem;
-  uint16_t *const vbuf = smem + C::KBUFS * C::K_ELEMS;
+  // four separate arrays, so that reads of one buffer never wait for the
+  // direct loads still filling another
+  __shared__ __attribute__((aligned(1024))) uint16_t kb0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t kb1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t vb0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t vb1[C::TILE];
 
   // ---- which tile: XCD-grouped, heaviest q-block first -------------------
   const int bid = blockIdx.x;
@@ -88,6 +106,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int ql = lane & 31, hh = lane >> 5;
   const int head = hkv * a.G + hg * a.hpw + w / a.wph;
   const int q0w = qblk * a.Bq + (w % a.wph) * 32;
@@ -113,32 +132,22 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
   const uint16_t *kg = a.k + kvoff;
   const uint16_t *vg = a.v + kvoff;
 
-  u32x4 kreg[C::PER_T], vreg[C::PER_T];
-
-  // K of tile jk and V of tile jv, staged through registers.  Rows past the
-  // end of the keys are read from the last row instead (the loads stay
-  // unconditional): such keys are masked, so their K only meets -inf scores
-  // and their V only zero weights.
-  auto load_tile = [&](int jk, int jv) {
+  // Tile j of K or V straight from global memory into LDS, moved by the four
+  // waves of one group: each wave moves 2 DPW blocks of 1 KiB; lane i fills
+  // bytes [16 i, 16 i + 16) of a block, so it fetches the logical chunk that
+  // the swizzle puts there.  Rows past the end of the keys are read from the
+  // last row instead (the loads stay unconditional): such keys are masked,
+  // so their K only meets -inf scores and their V only zero weights.
+  auto dma = [&](const uint16_t *g, uint16_t *dst, int j, auto is_v) __attribute__((always_inline)) {
+    constexpr bool V = decltype(is_v)::value;
 #pragma unroll
-    for (int i = 0; i < C::PER_T; ++i) {
-      const int c = tid + i * C::NT;
-      const int key = c / (D / 8), dc = c % (D / 8);
-      const int gk = min(jk * BK + key, a.Lk - 1);
-      const int gv = min(jv * BK + key, a.Lk - 1);
-      kreg[i] = ld16(kg + (size_t)gk * D + dc * 8);
-      vreg[i] = ld16(vg + (size_t)gv * D + dc * 8);
-    }
-  };
-  auto store_tile = [&](int jk, int jv, bool sk, bool sv) {
-    uint16_t *ks_ = kbuf + (jk % C::KBUFS) * C::K_ELEMS;
-    uint16_t *vs_ = vbuf + (jv % C::VBUFS) * C::V_ELEMS;
-#pragma unroll
-    for (int i = 0; i < C::PER_T; ++i) {
-      const int c = tid + i * C::NT;
-      const int key = c / (D / 8), dc = c % (D / 8);
-      if (sk) st16(ks_ + key * C::KS + dc * 8, kreg[i]);
-      if (sv) st16(vs_ + key * C::VS + dc * 8, vreg[i]);
+    for (int i = 0; i < 2 * C::DPW; ++i) {
+      const int blk = (wu & 3) * 2 * C::DPW + i;
+      const int row = blk * C::RPD + lane / C::CPR;
+      const int c = (lane % C::CPR) ^ (V ? vswz<D>(row) : kswz<D>(row));
+      const int grow = min(j * BK + row, a.Lk - 1);
+      __builtin_amdgcn_global_load_lds((glb_void_t *)(g + (size_t)grow * D + 8 * c),
+                                       (lds_void_t *)(dst + blk * 512), 16, 0, 0);
     }
   };
 
@@ -151,22 +160,34 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
   const bool cpos = cexp >= 0.f;
   const float maskval = cpos ? -__builtin_inff() : __builtin_inff();
 
-  // per-lane LDS offsets of the MFMA operands
-  const int koff = ql * C::KS + 8 * hh;                             // + 32 rb rows, + 16 ks
+  // per-lane LDS offsets (elements) of the MFMA operands.  K: row ql of the
+  // 32-key block, logical chunk 2 ks + hh (+ 32 rb rows).  V^T: row
+  // 4 hh + (j16 >> 2) of the 16-key block (+ 16 kb rows, + 8 for the upper
+  // half), 4 columns starting at 32 db + 16 (g16 & 1) + 4 (j16 & 3).
   const int g16 = lane >> 4, j16 = lane & 15;
-  const int voff = (4 * hh + (j16 >> 2)) * C::VS + 16 * (g16 & 1) + 4 * (j16 & 3);  // + 16 kb rows, + 32 db
+  int koffs[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) koffs[ks] = ql * D + 8 * ((2 * ks + hh) ^ kswz<D>(ql));
+  int voffs[D / 32];
+  {
+    const int vr = 4 * hh + (j16 >> 2);
+    const int tv = vswz<D>(vr) >> 2;
+    const int cin = 2 * (g16 & 1) + ((j16 & 3) >> 1);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) voffs[db] = vr * D + 8 * (4 * (db ^ tv) + cin) + 4 * (j16 & 1);
+  }
 
   bf16x8 pb[BK / 16];
   // O^T += V^T P^T for one tile; the V^T operand comes from row-major V by
   // transposing reads
-  auto pv = [&](const uint16_t *vs_) {
+  auto pv = [&](const uint16_t *vs_) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
       for (int kb = 0; kb < BK / 16; ++kb) {
-        const uint16_t *vp = vs_ + 16 * kb * C::VS + 32 * db + voff;
+        const uint16_t *vp = vs_ + 16 * kb * D + voffs[db];
         const bf16x4 lo = lds_tr16(vp);
-        const bf16x4 hi = lds_tr16(vp + 8 * C::VS);
+        const bf16x4 hi = lds_tr16(vp + 8 * D);
         const bf16x8 vop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[kb], o[db], 0, 0, 0);
       }
@@ -261,18 +282,17 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
   // phases 2j and 2j+1).
   const bool grpA = w < C::NW / 2;
   f32x16 s[BK / 32];
-  auto active = [&](int jj) { return jj >= 0 && jj < nt && jj * BK < kend_w; };
-  auto gemm = [&](int jj) {
-    if (active(jj - 1)) pv(vbuf + ((jj - 1) % C::VBUFS) * C::V_ELEMS);
+  auto active = [&](int jj) __attribute__((always_inline)) { return jj >= 0 && jj < nt && jj * BK < kend_w; };
+  auto gemm = [&](int jj, const uint16_t *ks_, const uint16_t *vs_) __attribute__((always_inline)) {
+    if (active(jj - 1)) pv(vs_);
     if (active(jj)) {
-      const uint16_t *ks_ = kbuf + (jj % C::KBUFS) * C::K_ELEMS;
 #pragma unroll
       for (int rb = 0; rb < BK / 32; ++rb) {
         s[rb] = f32x16{};
-        const uint16_t *kr = ks_ + 32 * rb * C::KS + koff;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks)
-          s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(kr + 16 * ks)), qf[ks], s[rb], 0, 0, 0);
+          s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(ks_ + 32 * rb * D + koffs[ks])), qf[ks],
+                                                          s[rb], 0, 0, 0);
       }
       // K operand reads four MFMAs ahead of their use
       constexpr int N = (BK / 32) * (D / 16);
@@ -285,7 +305,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
   };
-  auto soft = [&](int jj) {
+  auto soft = [&](int jj) __attribute__((always_inline)) {
     if (!active(jj)) return;
     const int k0 = jj * BK;
     if (k0 + BK > kmask_from) {
@@ -303,31 +323,46 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  load_tile(0, 0);
-  store_tile(0, 0, true, false);
-  __syncthreads();
-  for (int j = 0; j <= nt; ++j) {
-    const bool ldk = j + 1 < nt, ldv = j < nt;
-    if (ldk || ldv) load_tile(min(j + 1, nt - 1), min(j, nt - 1));
-    // phase 2j
+  // One tile step j (P = j % 2): K(j) is in kb[P], V(j-1) in vb[1-P].
+  // Group A runs its matrix work G(j) = [P.V of tile j-1, QK of tile j], then
+  // fetches K(j+1) into kb[1-P] and runs the softmax of tile j.  Group B
+  // fetches V(j) into vb[P], runs the softmax of tile j-1, then G(j).  So the
+  // exponentials of one wave execute next to the MFMAs of its SIMD
+  // neighbour.  Both target buffers were last read in step j-1.  A group's
+  // direct loads are complete before its next LDS reads (those loads and the
+  // LDS reads would otherwise share one wait counter), and the step ends with
+  // every wave's loads complete and a workgroup barrier, which publishes them.
+  auto step = [&](int j, auto parity) __attribute__((always_inline)) {
+    constexpr int P = decltype(parity)::value;
+    uint16_t *kcur = P ? kb1 : kb0;
+    uint16_t *knext = P ? kb0 : kb1;
+    uint16_t *vprev = P ? vb0 : vb1;
+    uint16_t *vcur = P ? vb1 : vb0;
     if (grpA) {
       if (ATTN_PF_PRIO) __builtin_amdgcn_s_setprio(1);
-      gemm(j);
+      gemm(j, kcur, vprev);
       if (ATTN_PF_PRIO) __builtin_amdgcn_s_setprio(0);
-    } else {
-      soft(j - 1);
-    }
-    __syncthreads();
-    // phase 2j+1
-    if (grpA) {
+      if (j + 1 < nt) dma(kg, knext, j + 1, std::false_type{});
       soft(j);
     } else {
+      if (j < nt) dma(vg, vcur, j, std::true_type{});
+      soft(j - 1);
+      ATTN_WAIT_VMEM();
       if (ATTN_PF_PRIO) __builtin_amdgcn_s_setprio(1);
-      gemm(j);
+      gemm(j, kcur, vprev);
       if (ATTN_PF_PRIO) __builtin_amdgcn_s_setprio(0);
     }
-    if (ldk || ldv) store_tile(j + 1, j, ldk, ldv);
+    ATTN_WAIT_VMEM();
     __syncthreads();
+  };
+
+  if (nt > 0 && grpA) dma(kg, kb0, 0, std::false_type{});
+  ATTN_WAIT_VMEM();
+  __syncthreads();
+  for (int j = 0; j <= nt; j += 2) {
+    step(j, std::integral_constant<int, 0>{});
+    if (j + 1 > nt) break;
+    step(j + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: out = O / l, lse = m ln2 + ln l -------------------------
@@ -383,7 +418,7 @@ bool prefill_plan(PrefillArgs &a, int D) {
 hipError_t launch_prefill(const PrefillArgs &a, int D, hipStream_t s) {
   switch (D) {
     case 64: return launch_t<64, 64>(a, s);
-    case 128: return launch_t<128, 64>(a, s);
+    case 128: return launch_t<128, ATTN_PF_BK128>(a, s);
     case 256: return launch_t<256, 32>(a, s);
     default: return hipErrorInvalidValue;
   }
