@@ -31,6 +31,12 @@ def _load(path: str = LIB_PATH):
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.attn_prefill.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
     lib.attn_prefill.restype = i
+    lib.attn_prefill_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.attn_prefill_ex.restype = i
+    lib.attn_prefill_splits.argtypes = [i, i, i, i, i, i, i, i]
+    lib.attn_prefill_splits.restype = i
+    lib.attn_prefill_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
+    lib.attn_prefill_workspace_bytes.restype = sz
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
     lib.attn_decode.restype = i
     lib.attn_decode_ex.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
@@ -83,9 +89,7 @@ def default_scale(D: int) -> float:
     return float(torch.tensor(1.0 / math.sqrt(D), dtype=torch.float32).item())
 
 
-def prefill(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=None,
-            return_lse: bool = True):
-    """attn_prefill: q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D] bf16 -> (out bf16, lse fp32 or None)."""
+def _prefill_args(q, k, v, out, lse, return_lse):
     _need(q, "q", torch.bfloat16, 4)
     _need(k, "k", torch.bfloat16, 4)
     _need(v, "v", torch.bfloat16, 4)
@@ -105,10 +109,37 @@ def prefill(q, k, v, causal: bool = True, scale: float | None = None, out=None, 
         _need(lse, "lse", torch.float32, 3)
         if tuple(lse.shape) != (B, Hq, Lq):
             raise ValueError("lse must be [B,Hq,Lq]")
+    return B, Hq, Hkv, Lq, Lk, D, out, lse
+
+
+def prefill(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=None,
+            return_lse: bool = True):
+    """attn_prefill: q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D] bf16 -> (out bf16, lse fp32 or None)."""
+    B, Hq, Hkv, Lq, Lk, D, out, lse = _prefill_args(q, k, v, out, lse, return_lse)
     scale = default_scale(D) if scale is None else float(scale)
     _check(lib.attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Lq, Lk, D,
                             1 if causal else 0, ctypes.c_float(scale), _stream(q.device)))
     return out, lse
+
+
+def prefill_ex(q, k, v, causal: bool = True, scale: float | None = None, splits: int = 0, out=None, lse=None,
+               return_lse: bool = True, workspace=None):
+    """attn_prefill_ex: prefill with a key-split count (0 = automatic) and an optional workspace."""
+    B, Hq, Hkv, Lq, Lk, D, out, lse = _prefill_args(q, k, v, out, lse, return_lse)
+    scale = default_scale(D) if scale is None else float(scale)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.attn_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Lq, Lk, D,
+                               1 if causal else 0, ctypes.c_float(scale), int(splits), _ptr(workspace), ws_bytes,
+                               _stream(q.device)))
+    return out, lse
+
+
+def prefill_splits(B, Hq, Hkv, Lq, Lk, D, causal=True, splits=0) -> int:
+    return int(lib.attn_prefill_splits(B, Hq, Hkv, Lq, Lk, D, 1 if causal else 0, splits))
+
+
+def prefill_workspace_bytes(B, Hq, Hkv, Lq, Lk, D, causal=True, splits=0) -> int:
+    return int(lib.attn_prefill_workspace_bytes(B, Hq, Hkv, Lq, Lk, D, 1 if causal else 0, splits))
 
 
 def decode(q, kcache, vcache, kv_lens, scale: float | None = None, out=None):
@@ -159,5 +190,5 @@ def _decode_shapes(q, kcache, vcache, kv_lens):
     return B, Hq, Hkv, Lmax, D
 
 
-__all__ = ["prefill", "decode", "decode_ex", "decode_workspace_bytes", "decode_waves", "AttnError", "lib",
+__all__ = ["prefill", "prefill_ex", "prefill_splits", "prefill_workspace_bytes", "decode", "decode_ex", "decode_workspace_bytes", "decode_waves", "AttnError", "lib",
            "LIB_PATH", "default_scale"]

@@ -159,39 +159,141 @@ int run_decode(const void *q, const void *kc, const void *vc, const int32_t *len
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
-}  // namespace
+int device_cus(int *cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
+  if (hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return ATTN_ERR_HIP;
+  if (*cus < 1) *cus = 1;
+  return ATTN_OK;
+}
 
-extern "C" {
-
-int attn_prefill(const void *q, const void *k, const void *v, void *out, float *lse, int B, int Hq, int Hkv,
-                 int Lq, int Lk, int D, int causal, float scale, void *stream) {
+// Argument checks and launch shape of a prefill (everything but pointers).
+// splits: 0 chooses the key-split count: 1 when the grid already has at least
+// two workgroups per compute unit, else enough ranges for that (each of at
+// least 8 tiles, at most 32 ranges); otherwise 1..kPrefillMaxSplits.
+int prefill_setup(PrefillArgs *pa, int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, float scale,
+                  int splits) {
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_GQA;
   if (!head_dim_ok(D)) return ATTN_ERR_HEADDIM;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
   if (B < 0 || Lq < 0 || Lk < 0) return ATTN_ERR_SHAPE;
-  if (B == 0 || Lq == 0) return ATTN_OK;  // empty: nothing read or written, pointers may be NULL
-  if (!q || !k || !v || !out) return ATTN_ERR_NULL;
+  if (splits < 0 || splits > attn::kPrefillMaxSplits) return ATTN_ERR_SPLIT;
+  if (B == 0 || Lq == 0) {
+    pa->nsplit = 0;
+    return ATTN_OK;
+  }
   if (Lk == 0) return ATTN_ERR_SHAPE;
   if (causal && Lq > Lk) return ATTN_ERR_SHAPE;
   if ((double)B * Hq * (double)Lq * D > 9.0e18 || (double)B * Hkv * (double)Lk * D > 9.0e18) return ATTN_ERR_SHAPE;
-
-  PrefillArgs a;
-  a.q = static_cast<const uint16_t *>(q);
-  a.k = static_cast<const uint16_t *>(k);
-  a.v = static_cast<const uint16_t *>(v);
-  a.out = static_cast<uint16_t *>(out);
-  a.lse = lse;
+  PrefillArgs &a = *pa;
+  a = PrefillArgs{};
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.Lq = Lq;
   a.Lk = Lk;
   a.G = Hq / Hkv;
-  if (!attn::prefill_plan(a, D)) return ATTN_ERR_SHAPE;
   a.causal = causal ? 1 : 0;
   a.c = scale * kLog2e;
-  hipError_t e = attn::launch_prefill(a, D, reinterpret_cast<hipStream_t>(stream));
+  a.nsplit = 1;
+  if (!attn::prefill_plan(a, D)) return ATTN_ERR_SHAPE;
+  int ns = splits;
+  if (ns == 0) {
+    int cus = 0;
+    if (device_cus(&cus) != ATTN_OK) return ATTN_ERR_HIP;
+    const long long units = a.total;
+    ns = 1;
+    if (units < 2LL * cus) {
+      const int tk = attn::prefill_tile_keys(D);
+      long long cap = ((long long)Lk + tk - 1) / tk / 8;
+      if (cap > 32) cap = 32;
+      long long want = (2LL * cus + units - 1) / units;
+      if (want > cap) want = cap;
+      if (want > 1) ns = (int)want;
+    }
+  }
+  a.nsplit = ns;
+  if (!attn::prefill_plan(a, D)) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+// Workspace of a split prefill: part_lse [rows][nsplit] | part_o [rows][nsplit][D].
+size_t prefill_lse_bytes(const PrefillArgs &a) {
+  return align256((size_t)a.B * a.Hq * (size_t)a.Lq * a.nsplit * sizeof(float));
+}
+size_t prefill_workspace(const PrefillArgs &a, int D) {
+  if (a.nsplit <= 1) return 0;
+  return prefill_lse_bytes(a) + align256((size_t)a.B * a.Hq * (size_t)a.Lq * a.nsplit * D * sizeof(float));
+}
+
+int run_prefill(const void *q, const void *k, const void *v, void *out, float *lse, int B, int Hq, int Hkv, int Lq,
+                int Lk, int D, int causal, float scale, int splits, void *ws, size_t ws_bytes, void *stream) {
+  // checks in the documented order; prefill_setup repeats the first ones
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_GQA;
+  if (!head_dim_ok(D)) return ATTN_ERR_HEADDIM;
+  if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  if (B < 0 || Lq < 0 || Lk < 0) return ATTN_ERR_SHAPE;
+  if (splits < 0 || splits > attn::kPrefillMaxSplits) return ATTN_ERR_SPLIT;
+  if (B == 0 || Lq == 0) return ATTN_OK;  // empty: nothing read or written, pointers may be NULL
+  if (!q || !k || !v || !out) return ATTN_ERR_NULL;
+  PrefillArgs a;
+  int st = prefill_setup(&a, B, Hq, Hkv, Lq, Lk, D, causal, scale, splits);
+  if (st != ATTN_OK) return st;
+  const size_t need = prefill_workspace(a, D);
+  if (ws != nullptr && ws_bytes < need) return ATTN_ERR_WORKSPACE;
+  a.q = static_cast<const uint16_t *>(q);
+  a.k = static_cast<const uint16_t *>(k);
+  a.v = static_cast<const uint16_t *>(v);
+  a.out = static_cast<uint16_t *>(out);
+  a.lse = lse;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void *mem = ws;
+  bool owned = false;
+  if (need > 0 && mem == nullptr) {
+    hipMemPool_t pool;
+    if (device_pool(&pool) != hipSuccess) return ATTN_ERR_HIP;
+    if (hipMallocFromPoolAsync(&mem, need, pool, s) != hipSuccess) return ATTN_ERR_HIP;
+    owned = true;
+  }
+  if (need > 0) {
+    char *base = static_cast<char *>(mem);
+    a.part_lse = reinterpret_cast<float *>(base);
+    a.part_o = reinterpret_cast<float *>(base + prefill_lse_bytes(a));
+  }
+  hipError_t e = attn::launch_prefill(a, D, s);
+  if (owned) {
+    hipError_t f = hipFreeAsync(mem, s);
+    if (e == hipSuccess) e = f;
+  }
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_prefill(const void *q, const void *k, const void *v, void *out, float *lse, int B, int Hq, int Hkv,
+                 int Lq, int Lk, int D, int causal, float scale, void *stream) {
+  return run_prefill(q, k, v, out, lse, B, Hq, Hkv, Lq, Lk, D, causal, scale, 0, nullptr, 0, stream);
+}
+
+int attn_prefill_ex(const void *q, const void *k, const void *v, void *out, float *lse, int B, int Hq, int Hkv,
+                    int Lq, int Lk, int D, int causal, float scale, int splits, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+  return run_prefill(q, k, v, out, lse, B, Hq, Hkv, Lq, Lk, D, causal, scale, splits, workspace, workspace_bytes,
+                     stream);
+}
+
+int attn_prefill_splits(int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, int splits) {
+  PrefillArgs a;
+  int st = prefill_setup(&a, B, Hq, Hkv, Lq, Lk, D, causal, 1.f, splits);
+  return st == ATTN_OK ? a.nsplit : 0;
+}
+
+size_t attn_prefill_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, int splits) {
+  PrefillArgs a;
+  if (prefill_setup(&a, B, Hq, Hkv, Lq, Lk, D, causal, 1.f, splits) != ATTN_OK) return 0;
+  return prefill_workspace(a, D);
 }
 
 int attn_decode(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens, void *out, int B,

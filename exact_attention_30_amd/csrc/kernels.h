@@ -20,9 +20,12 @@ struct PrefillArgs {
   int Bq;      // query rows per head per workgroup = rows per wave * wph
   int n_qblk;  // ceil(Lq / Bq)
   int n_hg;    // head groups per KV head = G / hpw
-  int total;   // workgroups in the grid
+  int total;   // workgroups in the grid (including the key splits)
   int causal;
   float c;     // scale * log2(e)
+  int nsplit;       // key ranges per query block (1: the kernel writes out and lse itself)
+  float *part_o;    // nsplit > 1: [rows][nsplit][D] normalised partial outputs, rows = B * Hq * Lq
+  float *part_lse;  // nsplit > 1: [rows][nsplit] partial log-sum-exps (-inf for an empty range)
 };
 
 struct DecodeArgs {
@@ -45,8 +48,13 @@ struct DecodeArgs {
 constexpr int kDecodeMaxWaves = 4096;
 
 // Fill in the query-row packing (hpw, wph, Bq, n_qblk, n_hg, total) for the
-// kernel that serves head dim D; false if the grid would be too large.
+// kernel that serves head dim D, for a.nsplit key ranges per query block;
+// false if the grid would be too large.
 bool prefill_plan(PrefillArgs &a, int D);
+// Keys per tile of the prefill kernel for head dim D.
+int prefill_tile_keys(int D);
+// Largest key-split count the combine step supports.
+constexpr int kPrefillMaxSplits = 64;
 hipError_t launch_prefill(const PrefillArgs &a, int D, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int D, int waves, hipStream_t s);
 hipError_t decode_waves_per_cu(int D, int G, int *out);

@@ -46,6 +46,14 @@
 #ifndef ATTN_PF_PRIO
 #define ATTN_PF_PRIO 1
 #endif
+//  ATTN_PF_PV_AHEAD     V^T operand reads issued this many MFMAs ahead
+//  ATTN_PF_QK_AHEAD     K operand reads issued this many MFMAs ahead
+#ifndef ATTN_PF_PV_AHEAD
+#define ATTN_PF_PV_AHEAD 3
+#endif
+#ifndef ATTN_PF_QK_AHEAD
+#define ATTN_PF_QK_AHEAD 4
+#endif
 //  ATTN_PF_BK128        key-tile size for D = 128
 #ifndef ATTN_PF_BK128
 #define ATTN_PF_BK128 64
@@ -96,6 +104,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
   int t = bid;
   const int tf = a.total & ~7;
   if (bid < tf) t = (bid & 7) * (tf >> 3) + (bid >> 3);
+  const int sp = t % a.nsplit;  // key range of this workgroup
+  t /= a.nsplit;
   int unit = t / a.n_qblk;
   const int r = t - unit * a.n_qblk;
   const int qblk = a.causal ? (a.n_qblk - 1 - r) : r;
@@ -119,7 +129,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
   int kend_w = 0;
   if (q0w < a.Lq) kend_w = a.causal ? min(a.Lk, min(q0w + 31, a.Lq - 1) + off + 1) : a.Lk;
   const int kmask_from = a.causal ? min(a.Lk, q0w + off + 1) : a.Lk;  // first key some row of the wave hides
-  const int nt = (kend_wg + BK - 1) / BK;
+  // this workgroup's share of the tiles: [j0, j0 + nt)
+  const int nt_all = (kend_wg + BK - 1) / BK;
+  const int j0 = (int)((long long)nt_all * sp / a.nsplit);
+  const int nt = (int)((long long)nt_all * (sp + 1) / a.nsplit) - j0;
 
   // ---- Q (B operand of S^T), kept in registers ----------------------------
   const int qr = min(qrow, a.Lq - 1);
@@ -192,15 +205,16 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[kb], o[db], 0, 0, 0);
       }
     }
-    // keep the transposing reads three MFMAs ahead of their use
+    // keep the transposing reads ATTN_PF_PV_AHEAD MFMAs ahead of their use
     constexpr int N = (D / 32) * (BK / 16);
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    constexpr int A = ATTN_PF_PV_AHEAD;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * A, 0);
 #pragma unroll
-    for (int i = 0; i < N - 3; ++i) {
+    for (int i = 0; i < N - A; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
   };
 
   // Online-softmax update for one tile of S^T (this lane: one query, BK/2
@@ -282,7 +296,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
   // phases 2j and 2j+1).
   const bool grpA = w < C::NW / 2;
   f32x16 s[BK / 32];
-  auto active = [&](int jj) __attribute__((always_inline)) { return jj >= 0 && jj < nt && jj * BK < kend_w; };
+  auto active = [&](int jj) __attribute__((always_inline)) {
+    return jj >= 0 && jj < nt && (j0 + jj) * BK < kend_w;
+  };
   auto gemm = [&](int jj, const uint16_t *ks_, const uint16_t *vs_) __attribute__((always_inline)) {
     if (active(jj - 1)) pv(vs_);
     if (active(jj)) {
@@ -294,20 +310,21 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
           s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(ks_ + 32 * rb * D + koffs[ks])), qf[ks],
                                                           s[rb], 0, 0, 0);
       }
-      // K operand reads four MFMAs ahead of their use
+      // K operand reads ATTN_PF_QK_AHEAD MFMAs ahead of their use
       constexpr int N = (BK / 32) * (D / 16);
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      constexpr int A = ATTN_PF_QK_AHEAD;
+      __builtin_amdgcn_sched_group_barrier(0x100, A, 0);
 #pragma unroll
-      for (int i = 0; i < N - 4; ++i) {
+      for (int i = 0; i < N - A; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
     }
   };
   auto soft = [&](int jj) __attribute__((always_inline)) {
     if (!active(jj)) return;
-    const int k0 = jj * BK;
+    const int k0 = (j0 + jj) * BK;
     if (k0 + BK > kmask_from) {
       const int lim = a.causal ? min(a.Lk - 1, qrow + off) : a.Lk - 1;
 #pragma unroll
@@ -342,10 +359,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
       if (ATTN_PF_PRIO) __builtin_amdgcn_s_setprio(1);
       gemm(j, kcur, vprev);
       if (ATTN_PF_PRIO) __builtin_amdgcn_s_setprio(0);
-      if (j + 1 < nt) dma(kg, knext, j + 1, std::false_type{});
+      if (j + 1 < nt) dma(kg, knext, j0 + j + 1, std::false_type{});
       soft(j);
     } else {
-      if (j < nt) dma(vg, vcur, j, std::true_type{});
+      if (j < nt) dma(vg, vcur, j0 + j, std::true_type{});
       soft(j - 1);
       ATTN_WAIT_VMEM();
       if (ATTN_PF_PRIO) __builtin_amdgcn_s_setprio(1);
@@ -356,7 +373,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
     __syncthreads();
   };
 
-  if (nt > 0 && grpA) dma(kg, kb0, 0, std::false_type{});
+  if (nt > 0 && grpA) dma(kg, kb0, j0, std::false_type{});
   ATTN_WAIT_VMEM();
   __syncthreads();
   for (int j = 0; j <= nt; j += 2) {
@@ -367,7 +384,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
 
   // ---- epilogue: out = O / l, lse = m ln2 + ln l -------------------------
   const float lt = pair_sum(l_run);
-  if (qrow < a.Lq && kend_w > 0) {
+  if (qrow < a.Lq && a.nsplit == 1) {
     const float inv = 1.f / lt;
     uint16_t *op = a.out + (((size_t)b * a.Hq + head) * a.Lq + qrow) * D;
 #pragma unroll
@@ -384,14 +401,75 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
     }
     if (a.lse != nullptr && hh == 0)
       a.lse[((size_t)b * a.Hq + head) * a.Lq + qrow] = m_run * ATTN_LN2 + __logf(lt);
+  } else if (qrow < a.Lq) {
+    // one key range of several: its normalised output and log-sum-exp (a row
+    // that sees no key of this range has l = 0: output 0, lse -inf)
+    const size_t row = ((size_t)b * a.Hq + head) * a.Lq + qrow;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    float *po = a.part_o + (row * a.nsplit + sp) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 v4 = {o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv, o[db][4 * g4 + 2] * inv,
+                          o[db][4 * g4 + 3] * inv};
+        *reinterpret_cast<f32x4 *>(po + 32 * db + 8 * g4 + 4 * hh) = v4;
+      }
+    }
+    if (hh == 0) a.part_lse[row * a.nsplit + sp] = lt > 0.f ? m_run * ATTN_LN2 + __logf(lt) : -__builtin_inff();
   }
+}
+
+// Merge of the key ranges of one query row (one wave per row, nsplit <= 64):
+// lse = log sum_s exp(lse_s), out = sum_s exp(lse_s - lse) out_s.  This is the
+// softmax sum split over disjoint key sets.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a, long long rows) {
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int S = a.nsplit;
+  const float lv = lane < S ? a.part_lse[row * S + lane] : -__builtin_inff();
+  float mx = lv;
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, sh));
+  const float wgt = (lane < S && lv > -__builtin_inff()) ? fast_exp2((lv - mx) * ATTN_LOG2E) : 0.f;
+  float den = wgt;
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) den += __shfl_xor(den, sh);
+  constexpr int PER = D / 64;
+  float acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  const float *po = a.part_o + (size_t)row * S * D + lane * PER;
+  for (int s = 0; s < S; ++s) {
+    const float ws = __shfl(wgt, s);
+    if (ws != 0.f) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] += ws * po[(size_t)s * D + i];
+    }
+  }
+  const float inv = 1.f / den;
+  uint16_t *op = a.out + (size_t)row * D + lane * PER;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const __bf16 h = (__bf16)(acc[i] * inv);
+    op[i] = __builtin_bit_cast(uint16_t, h);
+  }
+  if (a.lse != nullptr && lane == 0) a.lse[row] = mx + __logf(den);
 }
 
 template <int D, int BK>
 static hipError_t launch_t(const PrefillArgs &a, hipStream_t s) {
   hipLaunchKernelGGL((prefill_kernel<D, BK>), dim3(a.total), dim3(PrefillCfg<D, BK>::NT), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  const long long rows = (long long)a.B * a.Hq * a.Lq;
+  hipLaunchKernelGGL((prefill_combine_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a, rows);
   return hipGetLastError();
 }
+
+int prefill_tile_keys(int D) { return D == 256 ? 32 : (D == 128 ? ATTN_PF_BK128 : 64); }
 
 // Query-row packing of the kernel above: 8 waves x 32 rows per workgroup.
 bool prefill_plan(PrefillArgs &a, int D) {
@@ -409,7 +487,7 @@ bool prefill_plan(PrefillArgs &a, int D) {
   a.Bq = rows * a.wph;             // query rows per head per workgroup
   a.n_qblk = (a.Lq + a.Bq - 1) / a.Bq;
   a.n_hg = a.G / a.hpw;
-  const long long total = (long long)a.n_qblk * a.Hkv * a.n_hg * a.B;
+  const long long total = (long long)a.n_qblk * a.Hkv * a.n_hg * a.B * a.nsplit;
   if (total > 0x7fffffffLL) return false;
   a.total = (int)total;
   return true;

@@ -49,7 +49,8 @@
  *     caller's next synchronisation.
  *   - Errors are returned as negative attn_status codes; nothing is thrown
  *     across the ABI; the library keeps no state between calls apart from
- *     HIP's stream-ordered memory pool used by attn_decode.
+ *     HIP's stream-ordered memory pool (partials of attn_decode and of a
+ *     key-split attn_prefill) and cached device properties.
  */
 #ifndef ATTN_H_
 #define ATTN_H_
@@ -70,8 +71,9 @@ typedef enum {
   ATTN_ERR_GQA = -4,      /* Hq < 1, Hkv < 1 or Hq % Hkv != 0 */
   ATTN_ERR_SCALE = -5,    /* scale is NaN or infinite */
   ATTN_ERR_HIP = -6,      /* a HIP call or kernel launch failed */
-  ATTN_ERR_SPLIT = -7,    /* split_keys not 0 and not a positive multiple of 128 */
-  ATTN_ERR_WORKSPACE = -8 /* workspace given but smaller than attn_decode_workspace_bytes() */
+  ATTN_ERR_SPLIT = -7,    /* decode split_keys not 0 and not a positive multiple of 128, or
+                             prefill splits outside 0..64 */
+  ATTN_ERR_WORKSPACE = -8 /* workspace given but smaller than the matching *_workspace_bytes() */
 } attn_status;
 
 /*
@@ -91,11 +93,54 @@ typedef enum {
  * B == 0 or Lq == 0 is an empty call: ATTN_OK, nothing is read, written or
  * enqueued, and the pointers may be NULL (the other arguments are still
  * checked).
+ *
+ * When the grid of query blocks is small (fewer than two workgroups per
+ * compute unit, e.g. a chunk of a few hundred rows over a long cache), the
+ * keys of each query block are cut into several ranges processed by separate
+ * workgroups, and a second kernel merges their normalised partial outputs
+ * and log-sum-exps (the same merge as the decode's; see attn_prefill_ex).
+ * The partials then live in a workspace taken from HIP's stream-ordered
+ * allocator on `stream` and released on it.
  * Returns ATTN_OK or a negative attn_status.
  */
 int attn_prefill(const void *q, const void *k, const void *v, void *out, float *lse,
                  int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, float scale,
                  void *stream);
+
+/*
+ * attn_prefill_ex -- attn_prefill with two extra controls:
+ *   splits     0: choose the number of key ranges per query block as
+ *              attn_prefill does; 1..64: use exactly that many (else
+ *              ATTN_ERR_SPLIT).  Results agree for every count up to fp32
+ *              rounding of the merge.
+ *   workspace  caller-owned device buffer of workspace_bytes for the partials
+ *              (needed only with more than one range); NULL takes it from the
+ *              stream-ordered allocator.  If non-NULL it must hold at least
+ *              attn_prefill_workspace_bytes(...) bytes (else
+ *              ATTN_ERR_WORKSPACE) and must not be used by other work until
+ *              this call's kernels have finished on `stream`.
+ * Validation order: as attn_prefill, with the splits check after the size
+ * checks and before the empty-call return.
+ */
+int attn_prefill_ex(const void *q, const void *k, const void *v, void *out, float *lse,
+                    int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, float scale,
+                    int splits, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * attn_prefill_splits -- the number of key ranges attn_prefill_ex uses for
+ * these sizes and splits on the current device; 0 for an empty call, invalid
+ * arguments, or splits == 0 with no device available.
+ */
+int attn_prefill_splits(int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, int splits);
+
+/*
+ * attn_prefill_workspace_bytes -- bytes of workspace attn_prefill_ex needs
+ * for these sizes and splits (0 when a single range is used, for an empty
+ * call and for invalid arguments).  Layout: B*Hq*Lq*n fp32 log-sum-exps, then
+ * B*Hq*Lq*n*D fp32 outputs (n ranges), each part 256-byte aligned.
+ */
+size_t attn_prefill_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal,
+                                    int splits);
 
 /*
  * attn_decode -- one new query row per sequence over a ragged KV cache.

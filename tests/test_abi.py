@@ -119,3 +119,34 @@ def test_binding_rejects_cpu_tensors(attn):
         attn.prefill(q, q[:, :1], q[:, :1])
     with pytest.raises(TypeError):
         attn.prefill(q.float(), q[:, :1], q[:, :1])
+
+
+def prefill_ex(attn, splits=0, ws=N, ws_bytes=0, q=P, B=1, Hq=32, Hkv=8, Lq=512, Lk=16384, D=128, causal=1):
+    return attn.lib.attn_prefill_ex(q, P, P, P, N, B, Hq, Hkv, Lq, Lk, D, causal, ctypes.c_float(0.0884), splits,
+                                    ws, ws_bytes, None)
+
+
+def test_prefill_split_validation_and_sizes(attn):
+    def al(x):
+        return (x + 255) // 256 * 256
+    # explicit split counts need no device
+    assert attn.prefill_splits(1, 32, 8, 512, 16384, 128, True, 8) == 8
+    assert attn.prefill_splits(1, 32, 8, 512, 16384, 128, True, 1) == 1
+    assert attn.prefill_splits(1, 32, 8, 512, 16384, 128, True, 65) == 0      # out of range
+    assert attn.prefill_splits(1, 32, 8, 512, 16384, 128, True, -1) == 0
+    assert attn.prefill_splits(0, 32, 8, 512, 16384, 128, True, 3) == 0       # empty call
+    assert attn.prefill_splits(1, 32, 8, 600, 512, 128, True, 3) == 0         # causal with Lq > Lk
+    rows = 1 * 32 * 512
+    assert attn.prefill_workspace_bytes(1, 32, 8, 512, 16384, 128, True, 8) == al(rows * 8 * 4) + al(rows * 8 * 128 * 4)
+    assert attn.prefill_workspace_bytes(1, 32, 8, 512, 16384, 128, True, 1) == 0
+    assert attn.prefill_workspace_bytes(2, 6, 3, 77, 300, 64, False, 5) == al(2 * 6 * 77 * 5 * 4) + al(2 * 6 * 77 * 5 * 64 * 4)
+    assert attn.prefill_workspace_bytes(1, 6, 4, 77, 300, 64, False, 5) == 0   # invalid GQA
+    # validation order: sizes, then splits, then the empty-call return, then pointers, then the workspace
+    assert prefill_ex(attn, splits=65) == -7
+    assert prefill_ex(attn, splits=-2) == -7
+    assert prefill_ex(attn, splits=65, D=96) == -3
+    assert prefill_ex(attn, splits=65, B=0) == -7
+    assert prefill_ex(attn, splits=3, B=0) == 0
+    assert prefill_ex(attn, splits=3, q=N) == -1
+    need = attn.prefill_workspace_bytes(1, 32, 8, 512, 16384, 128, True, 4)
+    assert prefill_ex(attn, splits=4, ws=P, ws_bytes=need - 1) == -8

@@ -73,6 +73,51 @@ def test_prefill_small(attn, case):
     run_full(attn, case)
 
 
+SPLIT_CASES = [SMALL[1], SMALL[2], SMALL[3], SMALL[8], SMALL[9], SMALL[10]]
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5, 13])
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: c.name)
+def test_prefill_forced_splits(attn, case, splits):
+    """Every key-split count (including more ranges than tiles, which leaves
+    some ranges empty) matches the oracle."""
+    d = PrefillData(case)
+    out, lse = attn.prefill_ex(d.q, d.k, d.v, causal=case.causal, scale=case.scale, splits=splits)
+    torch.cuda.synchronize()
+    q, k, v = d.f64()
+    ro, rl = oracle.attention(q, k, v, case.causal, case.scale)
+    check_out(to_np(out), ro, f"{case.name} splits={splits}")
+    check_lse(to_np(lse), rl, f"{case.name} splits={splits}")
+
+
+def test_prefill_split_independence_and_workspace(attn):
+    """The merge of key ranges equals the single-range result up to fp32
+    rounding; a caller workspace gives the same bits as the pool."""
+    case = ai.PrefillCase("split_G4_Lq300_Lk2000_D128", 21, B=2, Hq=8, Hkv=2, Lq=300, Lk=2000, D=128)
+    d = PrefillData(case)
+    o1, l1 = attn.prefill_ex(d.q, d.k, d.v, causal=True, scale=case.scale, splits=1)
+    o7, l7 = attn.prefill_ex(d.q, d.k, d.v, causal=True, scale=case.scale, splits=7)
+    nb = attn.prefill_workspace_bytes(case.B, case.Hq, case.Hkv, case.Lq, case.Lk, case.D, True, 7)
+    assert nb > 0
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    o7w, l7w = attn.prefill_ex(d.q, d.k, d.v, causal=True, scale=case.scale, splits=7, workspace=ws)
+    torch.cuda.synchronize()
+    a1, a7 = to_np(o1), to_np(o7)
+    # Each range rounds its own weights to bf16 against its own maximum, so
+    # the two results differ by a few weight roundings (absolute, not
+    # relative to the output), well inside the oracle tolerance both meet.
+    q, k, v = d.f64()
+    ro, rl = oracle.attention(q, k, v, True, case.scale)
+    for o, l in ((o1, l1), (o7, l7)):
+        check_out(to_np(o), ro, case.name)
+        check_lse(to_np(l), rl, case.name)
+    assert float(np.abs(a1 - a7).max()) <= 4e-3
+    assert float(np.abs(a1 - a7).mean()) <= 2e-4
+    assert float(np.abs(to_np(l1) - to_np(l7)).max()) <= 1e-5
+    assert torch.equal(o7, o7w) and torch.equal(l7, l7w)
+    assert attn.prefill_splits(case.B, case.Hq, case.Hkv, case.Lq, case.Lk, case.D, True, 0) >= 1
+
+
 def test_prefill_qwen_4k_full(attn):
     run_full(attn, ai.QWEN_4K)
 
