@@ -40,6 +40,9 @@ ATTN_DEV uint32_t pack_hi16(uint32_t a, uint32_t b) { return __builtin_amdgcn_pe
 
 // 16-byte global load / store helpers.
 ATTN_DEV u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+// Streaming load (nontemporal hint): for data read once, such as a KV cache
+// during decode, so that it does not displace reusable lines from the caches.
+ATTN_DEV u32x4 ld16_stream(const void *p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p)); }
 ATTN_DEV void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
 
 ATTN_DEV bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }

@@ -41,6 +41,22 @@
 #include "common.h"
 #include "kernels.h"
 
+// Load choices (compile-time):
+//  ATTN_DEC_KNT / ATTN_DEC_VNT   nontemporal (streaming) loads for K / V
+//  ATTN_DEC_KNAT                 K operand layout: lane group g, step ks holds
+//                                dims 32 ks + 8 g (each load instruction reads
+//                                64 contiguous bytes per key row) instead of
+//                                dims (D / 4) g + 8 ks
+#ifndef ATTN_DEC_KNT
+#define ATTN_DEC_KNT 1
+#endif
+#ifndef ATTN_DEC_VNT
+#define ATTN_DEC_VNT 1
+#endif
+#ifndef ATTN_DEC_KNAT
+#define ATTN_DEC_KNAT 1
+#endif
+
 namespace attn {
 
 // Which wave's range contains flat block x, for the balanced split of `total`
@@ -137,9 +153,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       const int qi = 16 * cb + ql;
-      const uint16_t *qp = a.q + ((size_t)b * a.Hq + hkv * a.G + gq0 + min(qi, gcnt - 1)) * D + (D / 4) * g;
+      const uint16_t *qp = a.q + ((size_t)b * a.Hq + hkv * a.G + gq0 + min(qi, gcnt - 1)) * D;
 #pragma unroll
-      for (int ks = 0; ks < KST; ++ks) qf[cb][ks] = as_bf16x8(qi < gcnt ? ld16(qp + 8 * ks) : zero4);
+      for (int ks = 0; ks < KST; ++ks)
+        qf[cb][ks] = as_bf16x8(qi < gcnt ? ld16(qp + (ATTN_DEC_KNAT ? 32 * ks + 8 * g : (D / 4) * g + 8 * ks)) : zero4);
     }
     const size_t base = ((size_t)b * a.Hkv + hkv) * (size_t)a.Lmax * D;
     const uint16_t *kg = a.kc + base;
@@ -159,9 +176,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
   #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         const int key = kb + 16 * rb + ql;
-        const uint16_t *p = kg + (size_t)key * D + (D / 4) * g;
+        const uint16_t *p = kg + (size_t)key * D;
   #pragma unroll
-        for (int ks = 0; ks < KST; ++ks) kr[rb * KST + ks] = key < k1 ? ld16(p + 8 * ks) : zero4;
+        for (int ks = 0; ks < KST; ++ks) {
+          const uint16_t *pk = p + (ATTN_DEC_KNAT ? 32 * ks + 8 * g : (D / 4) * g + 8 * ks);
+          kr[rb * KST + ks] = key < k1 ? (ATTN_DEC_KNT ? ld16_stream(pk) : ld16(pk)) : zero4;
+        }
       }
   #pragma unroll
       for (int iu = 0; iu < VU; ++iu) {
@@ -171,7 +191,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
   #pragma unroll
           for (int kk = 0; kk < 8; ++kk) {
             const int key = kb + (kk < 4 ? 4 * gg + kk : 16 + 4 * gg + kk - 4);
-            vr[iu][kk] = key < k1 ? ld16(vg + (size_t)key * D + 8 * c) : zero4;
+            const uint16_t *pv = vg + (size_t)key * D + 8 * c;
+            vr[iu][kk] = key < k1 ? (ATTN_DEC_VNT ? ld16_stream(pv) : ld16(pv)) : zero4;
           }
         }
       }

@@ -177,18 +177,25 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
   // 32-key block, logical chunk 2 ks + hh (+ 32 rb rows).  V^T: row
   // 4 hh + (j16 >> 2) of the 16-key block (+ 16 kb rows, + 8 for the upper
   // half), 4 columns starting at 32 db + 16 (g16 & 1) + 4 (j16 & 3).
+  // The swizzles touch only the low 4 bits of a chunk index (K) or the low 2
+  // bits of a 64-byte group index (V), so offsets repeat every 16 chunks / 4
+  // groups up to a constant: only the first 8 K and 4 V offsets are kept.
   const int g16 = lane >> 4, j16 = lane & 15;
-  int koffs[D / 16];
+  constexpr int NKO = D / 16 < 8 ? D / 16 : 8;
+  constexpr int NVO = D / 32 < 4 ? D / 32 : 4;
+  int koffs[NKO];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) koffs[ks] = ql * D + 8 * ((2 * ks + hh) ^ kswz<D>(ql));
-  int voffs[D / 32];
+  for (int ks = 0; ks < NKO; ++ks) koffs[ks] = ql * D + 8 * ((2 * ks + hh) ^ kswz<D>(ql));
+  int voffs[NVO];
   {
     const int vr = 4 * hh + (j16 >> 2);
     const int tv = vswz<D>(vr) >> 2;
     const int cin = 2 * (g16 & 1) + ((j16 & 3) >> 1);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) voffs[db] = vr * D + 8 * (4 * (db ^ tv) + cin) + 4 * (j16 & 1);
+    for (int db = 0; db < NVO; ++db) voffs[db] = vr * D + 8 * (4 * (db ^ tv) + cin) + 4 * (j16 & 1);
   }
+  auto koff = [&](int ks) __attribute__((always_inline)) { return koffs[ks % NKO] + (ks / NKO) * 128; };
+  auto voff = [&](int db) __attribute__((always_inline)) { return voffs[db % NVO] + (db / NVO) * 128; };
 
   bf16x8 pb[BK / 16];
   // O^T += V^T P^T for one tile; the V^T operand comes from row-major V by
@@ -198,7 +205,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
       for (int kb = 0; kb < BK / 16; ++kb) {
-        const uint16_t *vp = vs_ + 16 * kb * D + voffs[db];
+        const uint16_t *vp = vs_ + 16 * kb * D + voff(db);
         const bf16x4 lo = lds_tr16(vp);
         const bf16x4 hi = lds_tr16(vp + 8 * D);
         const bf16x8 vop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -307,7 +314,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
         s[rb] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks)
-          s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(ks_ + 32 * rb * D + koffs[ks])), qf[ks],
+          s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(ks_ + 32 * rb * D + koff(ks))), qf[ks],
                                                           s[rb], 0, 0, 0);
       }
       // K operand reads ATTN_PF_QK_AHEAD MFMAs ahead of their use
