@@ -55,8 +55,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // slots = kDecodeMaxWaves + B * Hkv * n_hg (independent of the device).
 void decode_workspace(int B, int Hq, int Hkv, int D, DecodeShape *ds) {
   const int G = Hq / Hkv;
-  const long long hh = (long long)Hkv * ((G + 63) / 64);
-  const long long gw = G < 64 ? G : 64;
+  const long long hh = (long long)Hkv * ((G + attn::kDecodeGroup - 1) / attn::kDecodeGroup);
+  const long long gw = G < attn::kDecodeGroup ? G : attn::kDecodeGroup;
   const size_t slots = (size_t)attn::kDecodeMaxWaves + (size_t)B * hh;
   ds->pre_bytes = align256((size_t)(B + 1) * sizeof(long long));
   ds->part_lse_bytes = align256(slots * gw * sizeof(float));
@@ -74,7 +74,7 @@ int device_waves(int D, int G, int *waves) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return ATTN_ERR_HIP;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return ATTN_ERR_HIP;
-  const int gw = G < 64 ? G : 64;
+  const int gw = G < attn::kDecodeGroup ? G : attn::kDecodeGroup;
   const int ci = (gw + 15) / 16 >= 3 ? 2 : (gw + 15) / 16 - 1;
   const int di = D == 64 ? 0 : (D == 128 ? 1 : 2);
   std::lock_guard<std::mutex> lk(g_occ_mu);
@@ -88,7 +88,8 @@ int device_waves(int D, int G, int *waves) {
 int decode_waves(int B, int Hq, int Hkv, int Lmax, int D, int split_keys, int *waves) {
   if (split_keys == 0) return device_waves(D, Hq / Hkv, waves);
   const int G = Hq / Hkv;
-  const double keys = (double)B * Hkv * ((G + 63) / 64) * (double)((Lmax + 31) / 32) * 32.0;
+  const double keys = (double)B * Hkv * ((G + attn::kDecodeGroup - 1) / attn::kDecodeGroup) *
+                      (double)((Lmax + 31) / 32) * 32.0;
   double w = keys / split_keys;
   if (w < 1) w = 1;
   if (w > attn::kDecodeMaxWaves) w = attn::kDecodeMaxWaves;
@@ -149,7 +150,7 @@ int run_decode(const void *q, const void *kc, const void *vc, const int32_t *len
   a.Hkv = Hkv;
   a.Lmax = Lmax;
   a.G = Hq / Hkv;
-  a.n_hg = (a.G + 63) / 64;
+  a.n_hg = (a.G + attn::kDecodeGroup - 1) / attn::kDecodeGroup;
   a.c = scale * kLog2e;
   hipError_t e = attn::launch_decode(a, D, ds.waves, s);
   if (owned) {

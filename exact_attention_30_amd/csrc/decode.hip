@@ -136,13 +136,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
   const float cexp = a.c;
   const bool cpos = cexp >= 0.f;
   const float maskval = cpos ? -__builtin_inff() : __builtin_inff();
-  const int GW = min(a.G, 64);
+  const int GW = min(a.G, kDecodeGroup);
 
   while (r < r1) {
     const long long take = min(nb - blk, r1 - r);
     const int hkv = hh / a.n_hg, hg = hh - hkv * a.n_hg;
-    const int gq0 = hg * 64;
-    const int gcnt = min(64, a.G - gq0);
+    const int gq0 = hg * kDecodeGroup;
+    const int gcnt = min(kDecodeGroup, a.G - gq0);
     const int n = max(0, min(a.lens[b], a.Lmax));
     const int k0 = (int)(blk * 32);
     const int k1 = min(n, (int)((blk + take) * 32));
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a, int W)
   const int b = row / a.Hq, h = row - b * a.Hq;
   const int lane = threadIdx.x;
   const int hkv = h / a.G, gfull = h - hkv * a.G;
-  const int hg = gfull / 64, qi = gfull - hg * 64;
+  const int hg = gfull / kDecodeGroup, qi = gfull - hg * kDecodeGroup;
   const long long HH = (long long)a.Hkv * a.n_hg;
   const long long hh = (long long)hkv * a.n_hg + hg;
   const long long nb = a.pre[b + 1] - a.pre[b];
@@ -394,7 +394,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a, int W)
   const long long s0 = HH * a.pre[b] + hh * nb;       // first flat block of the segment
   const long long w0 = wave_of(s0, total, W), w1 = wave_of(s0 + nb - 1, total, W);
   if (w0 == w1) return;  // one wave covered it and wrote the result
-  const int GW = min(a.G, 64);
+  const int GW = min(a.G, kDecodeGroup);
   const long long seg = (long long)b * HH + hh;
   const int np = (int)(w1 - w0 + 1);
   auto prow = [&](int c) { return ((size_t)(seg + w0 + c) * GW + qi); };
@@ -445,7 +445,7 @@ static hipError_t launch_t(const DecodeArgs &a, int W, hipStream_t s) {
 
 template <int D>
 static hipError_t launch_d(const DecodeArgs &a, int W, hipStream_t s) {
-  const int gw = a.G < 64 ? a.G : 64;
+  const int gw = a.G < kDecodeGroup ? a.G : kDecodeGroup;
   const int ncb = (gw + 15) / 16;
   if (ncb == 1) return launch_t<D, 1>(a, W, s);
   if (ncb == 2) return launch_t<D, 2>(a, W, s);
@@ -463,7 +463,7 @@ hipError_t launch_decode(const DecodeArgs &a, int D, int W, hipStream_t s) {
 
 // Resident 64-thread workgroups of the main kernel per CU for this shape.
 hipError_t decode_waves_per_cu(int D, int G, int *out) {
-  const int gw = G < 64 ? G : 64;
+  const int gw = G < kDecodeGroup ? G : kDecodeGroup;
   const int ncb = (gw + 15) / 16;
   const void *f = nullptr;
 #define ATTN_PICK(DD, NN) f = reinterpret_cast<const void *>(&decode_main_kernel<DD, NN>)

@@ -40,12 +40,19 @@ struct DecodeArgs {
   float *part_lse;  // [slots][GW] piece log-sum-exps
   int B, Hq, Hkv, Lmax;
   int G;            // Hq / Hkv
-  int n_hg;         // groups of up to 64 query heads per KV head (GW = min(G, 64))
+  int n_hg;         // groups of up to kDecodeGroup query heads per KV head (GW = min(G, kDecodeGroup))
   float c;          // scale * log2(e)
 };
 
 // Upper bound on the waves of the decode main kernel (sizes the workspace).
 constexpr int kDecodeMaxWaves = 4096;
+// Query heads of one KV head handled together by a decode wave (16 per MFMA
+// column block); larger groups are split into groups of this size, each read
+// of K/V then serving one group.
+#ifndef ATTN_DEC_GROUP
+#define ATTN_DEC_GROUP 64
+#endif
+constexpr int kDecodeGroup = ATTN_DEC_GROUP;
 
 // Fill in the query-row packing (hpw, wph, Bq, n_qblk, n_hg, total) for the
 // kernel that serves head dim D, for a.nsplit key ranges per query block;
