@@ -54,6 +54,16 @@
 #ifndef ATTN_PF_QK_AHEAD
 #define ATTN_PF_QK_AHEAD 4
 #endif
+//  ATTN_PF_QKFIRST      matrix work of a step in the order QK(j), P.V(j-1), so
+//                       the P.V MFMAs still run while the wave starts its
+//                       softmax of tile j
+//  ATTN_PF_ADMA         group A fetches both K(j+1) and V(j) (group B none)
+#ifndef ATTN_PF_QKFIRST
+#define ATTN_PF_QKFIRST 0
+#endif
+#ifndef ATTN_PF_ADMA
+#define ATTN_PF_ADMA 0
+#endif
 //  ATTN_PF_BK128        key-tile size for D = 128
 #ifndef ATTN_PF_BK128
 #define ATTN_PF_BK128 64
@@ -307,7 +317,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
     return jj >= 0 && jj < nt && (j0 + jj) * BK < kend_w;
   };
   auto gemm = [&](int jj, const uint16_t *ks_, const uint16_t *vs_) __attribute__((always_inline)) {
-    if (active(jj - 1)) pv(vs_);
+    if (!ATTN_PF_QKFIRST && active(jj - 1)) pv(vs_);
     if (active(jj)) {
 #pragma unroll
       for (int rb = 0; rb < BK / 32; ++rb) {
@@ -328,6 +338,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
       }
       __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
     }
+    if (ATTN_PF_QKFIRST && active(jj - 1)) pv(vs_);
   };
   auto soft = [&](int jj) __attribute__((always_inline)) {
     if (!active(jj)) return;
@@ -367,11 +378,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
       gemm(j, kcur, vprev);
       if (ATTN_PF_PRIO) __builtin_amdgcn_s_setprio(0);
       if (j + 1 < nt) dma(kg, knext, j0 + j + 1, std::false_type{});
+      if (ATTN_PF_ADMA && j < nt) dma(vg, vcur, j0 + j, std::true_type{});
       soft(j);
     } else {
-      if (j < nt) dma(vg, vcur, j0 + j, std::true_type{});
+      if (!ATTN_PF_ADMA && j < nt) dma(vg, vcur, j0 + j, std::true_type{});
       soft(j - 1);
-      ATTN_WAIT_VMEM();
+      if (!ATTN_PF_ADMA) ATTN_WAIT_VMEM();
       if (ATTN_PF_PRIO) __builtin_amdgcn_s_setprio(1);
       gemm(j, kcur, vprev);
       if (ATTN_PF_PRIO) __builtin_amdgcn_s_setprio(0);
