@@ -41,6 +41,10 @@ def _load(path: str = LIB_PATH):
     lib.attn_decode.restype = i
     lib.attn_decode_ex.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     lib.attn_decode_ex.restype = i
+    lib.attn_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+    lib.attn_decode_multi.restype = i
+    lib.attn_decode_multi_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.attn_decode_multi_workspace_bytes.restype = sz
     lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.attn_decode_workspace_bytes.restype = sz
     lib.attn_decode_waves.argtypes = [i, i, i, i, i, i]
@@ -170,6 +174,34 @@ def decode_ex(q, kcache, vcache, kv_lens, scale: float | None = None, split_keys
     return out, lse
 
 
+def decode_multi(q, kcache, vcache, kv_lens, scale: float | None = None, out=None, return_lse: bool = True,
+                 workspace=None):
+    """attn_decode_multi: q [B,Hq,T,D] (the last T cached tokens of each sequence) -> (out, lse [B,Hq,T])."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(kcache, "kcache", torch.bfloat16, 4)
+    _need(vcache, "vcache", torch.bfloat16, 4)
+    _need(kv_lens, "kv_lens", torch.int32, 1)
+    B, Hq, T, D = q.shape
+    Hkv, Lmax = kcache.shape[1], kcache.shape[2]
+    if vcache.shape != kcache.shape or kcache.shape[0] != B or kcache.shape[3] != D or kv_lens.shape[0] != B:
+        raise ValueError("shape mismatch between q, caches and kv_lens")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.bfloat16, 4)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device) if return_lse else None
+    scale = default_scale(D) if scale is None else float(scale)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.attn_decode_multi(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(kv_lens), _ptr(out), _ptr(lse), B, Hq,
+                                 Hkv, T, Lmax, D, ctypes.c_float(scale), _ptr(workspace), ws_bytes,
+                                 _stream(q.device)))
+    return out, lse
+
+
+def decode_multi_workspace_bytes(B, Hq, Hkv, T, Lmax, D) -> int:
+    return int(lib.attn_decode_multi_workspace_bytes(B, Hq, Hkv, T, Lmax, D))
+
+
 def decode_workspace_bytes(B, Hq, Hkv, Lmax, D, split_keys=0) -> int:
     return int(lib.attn_decode_workspace_bytes(B, Hq, Hkv, Lmax, D, split_keys))
 
@@ -190,5 +222,5 @@ def _decode_shapes(q, kcache, vcache, kv_lens):
     return B, Hq, Hkv, Lmax, D
 
 
-__all__ = ["prefill", "prefill_ex", "prefill_splits", "prefill_workspace_bytes", "decode", "decode_ex", "decode_workspace_bytes", "decode_waves", "AttnError", "lib",
+__all__ = ["prefill", "prefill_ex", "prefill_splits", "prefill_workspace_bytes", "decode", "decode_ex", "decode_multi", "decode_multi_workspace_bytes", "decode_workspace_bytes", "decode_waves", "AttnError", "lib",
            "LIB_PATH", "default_scale"]

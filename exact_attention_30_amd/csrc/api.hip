@@ -52,11 +52,12 @@ struct DecodeShape {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout: pre [B + 1] int64 | part_lse [slots][GW] | part_o [slots][GW][D],
-// slots = kDecodeMaxWaves + B * Hkv * n_hg (independent of the device).
-void decode_workspace(int B, int Hq, int Hkv, int D, DecodeShape *ds) {
-  const int G = Hq / Hkv;
-  const long long hh = (long long)Hkv * ((G + attn::kDecodeGroup - 1) / attn::kDecodeGroup);
-  const long long gw = G < attn::kDecodeGroup ? G : attn::kDecodeGroup;
+// slots = kDecodeMaxWaves + B * Hkv * n_hg (independent of the device); a KV
+// head has G * T query rows, in groups of up to kDecodeGroup (GW = the group size).
+void decode_workspace(int B, int Hq, int Hkv, int T, int D, DecodeShape *ds) {
+  const long long GT = (long long)(Hq / Hkv) * T;
+  const long long hh = (long long)Hkv * ((GT + attn::kDecodeGroup - 1) / attn::kDecodeGroup);
+  const long long gw = GT < attn::kDecodeGroup ? GT : attn::kDecodeGroup;
   const size_t slots = (size_t)attn::kDecodeMaxWaves + (size_t)B * hh;
   ds->pre_bytes = align256((size_t)(B + 1) * sizeof(long long));
   ds->part_lse_bytes = align256(slots * gw * sizeof(float));
@@ -70,25 +71,25 @@ void decode_workspace(int B, int Hq, int Hkv, int D, DecodeShape *ds) {
 std::mutex g_occ_mu;
 int g_occ_cache[64][3][3];
 
-int device_waves(int D, int G, int *waves) {
+int device_waves(int D, int GT, int *waves) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return ATTN_ERR_HIP;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return ATTN_ERR_HIP;
-  const int gw = G < attn::kDecodeGroup ? G : attn::kDecodeGroup;
+  const int gw = GT < attn::kDecodeGroup ? GT : attn::kDecodeGroup;
   const int ci = (gw + 15) / 16 >= 3 ? 2 : (gw + 15) / 16 - 1;
   const int di = D == 64 ? 0 : (D == 128 ? 1 : 2);
   std::lock_guard<std::mutex> lk(g_occ_mu);
   int &occ = g_occ_cache[dev][di][ci];
-  if (occ == 0 && attn::decode_waves_per_cu(D, G, &occ) != hipSuccess) return ATTN_ERR_HIP;
+  if (occ == 0 && attn::decode_waves_per_cu(D, gw, &occ) != hipSuccess) return ATTN_ERR_HIP;
   const long long w = (long long)cus * (occ > 0 ? occ : 1);
   *waves = (int)(w < attn::kDecodeMaxWaves ? w : attn::kDecodeMaxWaves);
   return ATTN_OK;
 }
 
-int decode_waves(int B, int Hq, int Hkv, int Lmax, int D, int split_keys, int *waves) {
-  if (split_keys == 0) return device_waves(D, Hq / Hkv, waves);
-  const int G = Hq / Hkv;
-  const double keys = (double)B * Hkv * ((G + attn::kDecodeGroup - 1) / attn::kDecodeGroup) *
+int decode_waves(int B, int Hq, int Hkv, int T, int Lmax, int D, int split_keys, int *waves) {
+  const int GT = (Hq / Hkv) * T;
+  if (split_keys == 0) return device_waves(D, GT, waves);
+  const double keys = (double)B * Hkv * ((GT + attn::kDecodeGroup - 1) / attn::kDecodeGroup) *
                       (double)((Lmax + 31) / 32) * 32.0;
   double w = keys / split_keys;
   if (w < 1) w = 1;
@@ -100,29 +101,29 @@ int decode_waves(int B, int Hq, int Hkv, int Lmax, int D, int split_keys, int *w
 }
 
 int decode_check(const void *q, const void *kc, const void *vc, const int32_t *lens, const void *out, int B,
-                 int Hq, int Hkv, int Lmax, int D, float scale) {
+                 int Hq, int Hkv, int T, int Lmax, int D, float scale) {
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_GQA;
   if (!head_dim_ok(D)) return ATTN_ERR_HEADDIM;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
-  if (B < 0 || Lmax < 1 || B > 65535) return ATTN_ERR_SHAPE;
+  if (B < 0 || Lmax < 1 || B > 65535 || T < 1 || T > Lmax) return ATTN_ERR_SHAPE;
   if (B > 0 && (!q || !kc || !vc || !lens || !out)) return ATTN_ERR_NULL;
-  if ((long long)B * Hq > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  if ((long long)B * Hq * T > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   // element counts must fit comfortably in 64-bit offsets
   if ((double)B * Hkv * (double)Lmax * D > 9.0e18) return ATTN_ERR_SHAPE;
   return ATTN_OK;
 }
 
 int run_decode(const void *q, const void *kc, const void *vc, const int32_t *lens, void *out, float *lse, int B,
-               int Hq, int Hkv, int Lmax, int D, float scale, int split_keys, void *ws, size_t ws_bytes,
+               int Hq, int Hkv, int T, int Lmax, int D, float scale, int split_keys, void *ws, size_t ws_bytes,
                void *stream) {
-  int st = decode_check(q, kc, vc, lens, out, B, Hq, Hkv, Lmax, D, scale);
+  int st = decode_check(q, kc, vc, lens, out, B, Hq, Hkv, T, Lmax, D, scale);
   if (st != ATTN_OK) return st;
   if (split_keys != 0 && (split_keys < 0 || split_keys % 128 != 0)) return ATTN_ERR_SPLIT;
   DecodeShape ds;
-  decode_workspace(B, Hq, Hkv, D, &ds);
+  decode_workspace(B, Hq, Hkv, T, D, &ds);
   if (ws != nullptr && ws_bytes < ds.total) return ATTN_ERR_WORKSPACE;
   if (B == 0) return ATTN_OK;
-  st = decode_waves(B, Hq, Hkv, Lmax, D, split_keys, &ds.waves);
+  st = decode_waves(B, Hq, Hkv, T, Lmax, D, split_keys, &ds.waves);
   if (st != ATTN_OK) return st;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -150,7 +151,8 @@ int run_decode(const void *q, const void *kc, const void *vc, const int32_t *len
   a.Hkv = Hkv;
   a.Lmax = Lmax;
   a.G = Hq / Hkv;
-  a.n_hg = (a.G + attn::kDecodeGroup - 1) / attn::kDecodeGroup;
+  a.T = T;
+  a.n_hg = (a.G * T + attn::kDecodeGroup - 1) / attn::kDecodeGroup;
   a.c = scale * kLog2e;
   hipError_t e = attn::launch_decode(a, D, ds.waves, s);
   if (owned) {
@@ -299,21 +301,36 @@ size_t attn_prefill_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int 
 
 int attn_decode(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens, void *out, int B,
                 int Hq, int Hkv, int Lmax, int D, float scale, void *stream) {
-  return run_decode(q, kcache, vcache, kv_lens, out, nullptr, B, Hq, Hkv, Lmax, D, scale, 0, nullptr, 0, stream);
+  return run_decode(q, kcache, vcache, kv_lens, out, nullptr, B, Hq, Hkv, 1, Lmax, D, scale, 0, nullptr, 0,
+                    stream);
 }
 
 int attn_decode_ex(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens, void *out,
                    float *lse, int B, int Hq, int Hkv, int Lmax, int D, float scale, int split_keys,
                    void *workspace, size_t workspace_bytes, void *stream) {
-  return run_decode(q, kcache, vcache, kv_lens, out, lse, B, Hq, Hkv, Lmax, D, scale, split_keys, workspace,
+  return run_decode(q, kcache, vcache, kv_lens, out, lse, B, Hq, Hkv, 1, Lmax, D, scale, split_keys, workspace,
                     workspace_bytes, stream);
+}
+
+int attn_decode_multi(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens, void *out,
+                      float *lse, int B, int Hq, int Hkv, int T, int Lmax, int D, float scale, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  return run_decode(q, kcache, vcache, kv_lens, out, lse, B, Hq, Hkv, T, Lmax, D, scale, 0, workspace,
+                    workspace_bytes, stream);
+}
+
+size_t attn_decode_multi_workspace_bytes(int B, int Hq, int Hkv, int T, int Lmax, int D) {
+  if (B <= 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || !head_dim_ok(D) || Lmax < 1 || T < 1 || T > Lmax) return 0;
+  DecodeShape ds;
+  decode_workspace(B, Hq, Hkv, T, D, &ds);
+  return ds.total;
 }
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Lmax, int D, int split_keys) {
   if (B <= 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || !head_dim_ok(D) || Lmax < 1) return 0;
   if (split_keys != 0 && (split_keys < 0 || split_keys % 128 != 0)) return 0;
   DecodeShape ds;
-  decode_workspace(B, Hq, Hkv, D, &ds);
+  decode_workspace(B, Hq, Hkv, 1, D, &ds);
   return ds.total;
 }
 
@@ -321,7 +338,7 @@ int attn_decode_waves(int B, int Hq, int Hkv, int Lmax, int D, int split_keys) {
   if (B <= 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || !head_dim_ok(D) || Lmax < 1) return 0;
   if (split_keys != 0 && (split_keys < 0 || split_keys % 128 != 0)) return 0;
   int w = 0;
-  return decode_waves(B, Hq, Hkv, Lmax, D, split_keys, &w) == ATTN_OK ? w : 0;
+  return decode_waves(B, Hq, Hkv, 1, Lmax, D, split_keys, &w) == ATTN_OK ? w : 0;
 }
 
 const char *attn_status_string(int status) {

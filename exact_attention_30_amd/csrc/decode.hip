@@ -136,24 +136,32 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
   const float cexp = a.c;
   const bool cpos = cexp >= 0.f;
   const float maskval = cpos ? -__builtin_inff() : __builtin_inff();
-  const int GW = min(a.G, kDecodeGroup);
+  const int GT = a.G * a.T;               // query rows of one KV head
+  const int GW = min(GT, kDecodeGroup);
 
   while (r < r1) {
     const long long take = min(nb - blk, r1 - r);
     const int hkv = hh / a.n_hg, hg = hh - hkv * a.n_hg;
     const int gq0 = hg * kDecodeGroup;
-    const int gcnt = min(kDecodeGroup, a.G - gq0);
+    const int gcnt = min(kDecodeGroup, GT - gq0);
     const int n = max(0, min(a.lens[b], a.Lmax));
     const int k0 = (int)(blk * 32);
     const int k1 = min(n, (int)((blk + take) * 32));
     const bool whole = (blk == 0) && (take == nb);
+    // causal limit of this lane's query row in each column block: with T new
+    // rows at the end of the cache, row t sees keys [0, n - T + t]
+    int kcol[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) kcol[cb] = n - a.T + 1 + (gq0 + 16 * cb + ql) % a.T;
+    const int kfull = min(k1, n - a.T + 1);   // keys below this are visible to every row
     const long long slot = (long long)b * HH + hh + w;
 
     bf16x8 qf[NCB][KST];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       const int qi = 16 * cb + ql;
-      const uint16_t *qp = a.q + ((size_t)b * a.Hq + hkv * a.G + gq0 + min(qi, gcnt - 1)) * D;
+      // rows of a KV head are contiguous: (head g, position t) -> g * T + t
+      const uint16_t *qp = a.q + (((size_t)b * a.Hq + hkv * a.G) * a.T + gq0 + min(qi, gcnt - 1)) * D;
 #pragma unroll
       for (int ks = 0; ks < KST; ++ks)
         qf[cb][ks] = as_bf16x8(qi < gcnt ? ld16(qp + (ATTN_DEC_KNAT ? 32 * ks + 8 * g : (D / 4) * g + 8 * ks)) : zero4);
@@ -236,7 +244,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
             s[cb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[rb * KST + ks]), qf[cb][ks], s[cb][rb], 0, 0, 0);
         }
       __syncthreads();
-      const bool partial = kb + 32 > k1;
+      const bool partial = kb + 32 > kfull;
       bf16x8 pb[NCB];
   #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
@@ -247,7 +255,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
           for (int rb = 0; rb < 2; ++rb)
   #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-              const bool vv = kb + 16 * rb + 4 * g + rr < k1;
+              const int key = kb + 16 * rb + 4 * g + rr;
+              const bool vv = key < k1 && key < kcol[cb];
               vis |= (vv ? 1u : 0u) << (4 * rb + rr);
               s[cb][rb][rr] = vv ? s[cb][rb][rr] : maskval;
             }
@@ -329,11 +338,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
       float lt = l_run[cb];
       lt += xor16(lt);
       lt += xor32(lt);
-      const float inv = 1.f / lt;
+      // a row that sees no key of this piece (only with T > 1) has l = 0
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
       const int qi = 16 * cb + ql;
       if (qi < gcnt) {
-        const size_t row = (size_t)b * a.Hq + hkv * a.G + gq0 + qi;
-        const float lse_c = m_run[cb] * ATTN_LN2 + __logf(lt);
+        const size_t row = ((size_t)b * a.Hq + hkv * a.G) * a.T + gq0 + qi;
+        const float lse_c = lt > 0.f ? m_run[cb] * ATTN_LN2 + __logf(lt) : -__builtin_inff();
         if (whole) {
 #pragma unroll
           for (int db = 0; db < D / 16; ++db) {
@@ -376,10 +386,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
 // reduced across the wave; each lane accumulates D/64 output elements.
 template <int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a, int W) {
-  const int row = blockIdx.x;  // b * Hq + h
-  const int b = row / a.Hq, h = row - b * a.Hq;
+  const int row = blockIdx.x;  // (b * Hq + h) * T + t
+  const int HT = a.Hq * a.T, GT = a.G * a.T;
+  const int b = row / HT, ht = row - b * HT;
   const int lane = threadIdx.x;
-  const int hkv = h / a.G, gfull = h - hkv * a.G;
+  const int hkv = ht / GT, gfull = ht - hkv * GT;   // row within the KV head's G * T rows
   const int hg = gfull / kDecodeGroup, qi = gfull - hg * kDecodeGroup;
   const long long HH = (long long)a.Hkv * a.n_hg;
   const long long hh = (long long)hkv * a.n_hg + hg;
@@ -394,7 +405,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a, int W)
   const long long s0 = HH * a.pre[b] + hh * nb;       // first flat block of the segment
   const long long w0 = wave_of(s0, total, W), w1 = wave_of(s0 + nb - 1, total, W);
   if (w0 == w1) return;  // one wave covered it and wrote the result
-  const int GW = min(a.G, kDecodeGroup);
+  const int GW = min(GT, kDecodeGroup);
   const long long seg = (long long)b * HH + hh;
   const int np = (int)(w1 - w0 + 1);
   auto prow = [&](int c) { return ((size_t)(seg + w0 + c) * GW + qi); };
@@ -405,6 +416,11 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a, int W)
   }
 #pragma unroll
   for (int sh = 32; sh >= 1; sh >>= 1) M = __builtin_fmaxf(M, __shfl_xor(M, sh));
+  if (M == -__builtin_inff()) {  // the row saw no key in any piece (only with T > 1)
+    for (int d = lane; d < D; d += 64) op[d] = 0;
+    if (a.lse != nullptr && lane == 0) a.lse[row] = -__builtin_inff();
+    return;
+  }
   float Z = 0.f;
   float acc[D / 64];
 #pragma unroll
@@ -439,13 +455,14 @@ static hipError_t launch_t(const DecodeArgs &a, int W, hipStream_t s) {
   hipLaunchKernelGGL((decode_main_kernel<D, NCB>), dim3(W), dim3(64), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.Hq), dim3(64), 0, s, a, W);
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.Hq * a.T), dim3(64), 0, s, a, W);
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_d(const DecodeArgs &a, int W, hipStream_t s) {
-  const int gw = a.G < kDecodeGroup ? a.G : kDecodeGroup;
+  const int gt = a.G * a.T;
+  const int gw = gt < kDecodeGroup ? gt : kDecodeGroup;
   const int ncb = (gw + 15) / 16;
   if (ncb == 1) return launch_t<D, 1>(a, W, s);
   if (ncb == 2) return launch_t<D, 2>(a, W, s);
@@ -461,9 +478,10 @@ hipError_t launch_decode(const DecodeArgs &a, int D, int W, hipStream_t s) {
   }
 }
 
-// Resident 64-thread workgroups of the main kernel per CU for this shape.
-hipError_t decode_waves_per_cu(int D, int G, int *out) {
-  const int gw = G < kDecodeGroup ? G : kDecodeGroup;
+// Resident 64-thread workgroups of the main kernel per CU for GW query rows
+// per wave group.
+hipError_t decode_waves_per_cu(int D, int GW, int *out) {
+  const int gw = GW < kDecodeGroup ? GW : kDecodeGroup;
   const int ncb = (gw + 15) / 16;
   const void *f = nullptr;
 #define ATTN_PICK(DD, NN) f = reinterpret_cast<const void *>(&decode_main_kernel<DD, NN>)

@@ -40,7 +40,9 @@ struct DecodeArgs {
   float *part_lse;  // [slots][GW] piece log-sum-exps
   int B, Hq, Hkv, Lmax;
   int G;            // Hq / Hkv
-  int n_hg;         // groups of up to kDecodeGroup query heads per KV head (GW = min(G, kDecodeGroup))
+  int T;            // query rows per sequence and head (1: plain decode)
+  int n_hg;         // groups of up to kDecodeGroup query rows per KV head
+                    // (a KV head's G * T rows; GW = min(G * T, kDecodeGroup))
   float c;          // scale * log2(e)
 };
 
@@ -64,6 +66,6 @@ int prefill_tile_keys(int D);
 constexpr int kPrefillMaxSplits = 64;
 hipError_t launch_prefill(const PrefillArgs &a, int D, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int D, int waves, hipStream_t s);
-hipError_t decode_waves_per_cu(int D, int G, int *out);
+hipError_t decode_waves_per_cu(int D, int GW, int *out);
 
 }  // namespace attn

@@ -66,7 +66,8 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = -1,     /* a required pointer is NULL */
   ATTN_ERR_SHAPE = -2,    /* a negative size, Lk = 0 with Lq > 0, causal with Lq > Lk,
-                             Lmax < 1, or a size whose element count overflows */
+                             Lmax < 1, T outside 1..Lmax, or a size whose element count
+                             overflows */
   ATTN_ERR_HEADDIM = -3,  /* D not in {64, 128, 256} */
   ATTN_ERR_GQA = -4,      /* Hq < 1, Hkv < 1 or Hq % Hkv != 0 */
   ATTN_ERR_SCALE = -5,    /* scale is NaN or infinite */
@@ -184,6 +185,38 @@ int attn_decode(const void *q, const void *kcache, const void *vcache, const int
 int attn_decode_ex(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens,
                    void *out, float *lse, int B, int Hq, int Hkv, int Lmax, int D, float scale,
                    int split_keys, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * attn_decode_multi -- T new query rows per sequence over the ragged cache
+ * (verification of T speculated tokens, or a short chunk appended to a cache).
+ *
+ * Pages: the cost guide's is_causal section (with fewer queries than keys
+ * the causal mask is anchored at the bottom-right corner) and its use_cache
+ * section (the new tokens' K/V are already in the cache).  The T new tokens
+ * of sequence b are its last T cached positions: with n_b = min(kv_lens[b],
+ * Lmax), row t (0 <= t < T) sees keys [0, n_b - T + t].  This is
+ * attn_prefill with Lq = T, causal, over each sequence's n_b keys; T = 1 is
+ * attn_decode.  A row that sees no key (n_b < T - t, including empty
+ * sequences) gets out = 0 and lse = -inf.
+ *
+ *   q, out  [B][Hq][T][D] bf16        lse [B][Hq][T] fp32, may be NULL
+ *   kcache, vcache [B][Hkv][Lmax][D] bf16, kv_lens [B] int32 (device)
+ *
+ * The G * T rows of one KV head (G = Hq / Hkv) share every K/V read, in
+ * groups of up to 64 rows.  1 <= T <= Lmax (else ATTN_ERR_SHAPE).  Key ranges
+ * are chosen as attn_decode does; workspace as attn_decode_ex (NULL: taken
+ * from the stream-ordered allocator), sized by
+ * attn_decode_multi_workspace_bytes.
+ */
+int attn_decode_multi(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens,
+                      void *out, float *lse, int B, int Hq, int Hkv, int T, int Lmax, int D, float scale,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * attn_decode_multi_workspace_bytes -- bytes of workspace attn_decode_multi
+ * needs for these sizes; 0 for an empty call and for invalid arguments.
+ */
+size_t attn_decode_multi_workspace_bytes(int B, int Hq, int Hkv, int T, int Lmax, int D);
 
 /*
  * attn_decode_workspace_bytes -- bytes of workspace attn_decode_ex needs for

@@ -150,3 +150,29 @@ def test_prefill_split_validation_and_sizes(attn):
     assert prefill_ex(attn, splits=3, q=N) == -1
     need = attn.prefill_workspace_bytes(1, 32, 8, 512, 16384, 128, True, 4)
     assert prefill_ex(attn, splits=4, ws=P, ws_bytes=need - 1) == -8
+
+
+def test_decode_multi_validation_and_sizes(attn):
+    def al(x):
+        return (x + 255) // 256 * 256
+
+    def multi(T=4, B=2, Hq=8, Hkv=2, Lmax=64, D=128, q=P, ws=N, ws_bytes=0):
+        return attn.lib.attn_decode_multi(q, P, P, P, P, N, B, Hq, Hkv, T, Lmax, D, ctypes.c_float(0.1), ws,
+                                          ws_bytes, None)
+    assert multi(T=0) == -2
+    assert multi(T=65) == -2            # more new rows than cache slots
+    assert multi(Hq=7) == -4
+    assert multi(D=32) == -3
+    assert multi(q=N) == -1
+    assert multi(B=0, q=N) == 0
+    # rows of a KV head: G * T, in groups of up to 64
+    B, Hq, Hkv, T, D = 3, 32, 8, 4, 128      # G * T = 16 -> one group of 16
+    slots = 4096 + B * Hkv
+    assert attn.decode_multi_workspace_bytes(B, Hq, Hkv, T, 64, D) == al((B + 1) * 8) + al(slots * 16 * 4) + al(slots * 16 * D * 4)
+    B, Hq, Hkv, T, D = 2, 8, 1, 16, 64       # G * T = 128 -> two groups of 64
+    slots = 4096 + B * 1 * 2
+    assert attn.decode_multi_workspace_bytes(B, Hq, Hkv, T, 64, D) == al((B + 1) * 8) + al(slots * 64 * 4) + al(slots * 64 * D * 4)
+    assert attn.decode_multi_workspace_bytes(2, 8, 2, 1, 64, 128) == attn.decode_workspace_bytes(2, 8, 2, 64, 128)
+    assert attn.decode_multi_workspace_bytes(2, 8, 2, 0, 64, 128) == 0
+    need = attn.decode_multi_workspace_bytes(2, 8, 2, 4, 64, 128)
+    assert multi(ws=P, ws_bytes=need - 1) == -8

@@ -152,3 +152,83 @@ def test_decode_deterministic(attn):
     b = attn.decode(q, kc, vc, ld, scale=c.scale)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# ---- several new rows per sequence (speculative verification) ---------------
+
+def multi_q_bits(case, T):
+    return ai.normal_bf16_bits((case.B, case.Hq, T, case.D), [case.wid, 0, case.variant, 1000 + T])
+
+
+def multi_reference(case, T, qb, lens):
+    """Oracle per sequence: the last min(n, T) rows attend [0, n) with the
+    bottom-right causal mask; rows that see no key are 0 / -inf."""
+    q = ai.bf16_bits_to_f64(qb)
+    out = np.zeros((case.B, case.Hq, T, case.D))
+    lse = np.full((case.B, case.Hq, T), -np.inf)
+    for b, n, kb, vb in case.iter_seqs(lens):
+        if n == 0:
+            continue
+        m = min(n, T)
+        o, l_ = oracle.attention(q[b:b + 1, :, T - m:], ai.bf16_bits_to_f64(kb)[None], ai.bf16_bits_to_f64(vb)[None],
+                                 True, case.scale)
+        out[b, :, T - m:], lse[b, :, T - m:] = o[0], l_[0]
+    return out, lse
+
+
+MULTI = [
+    # (T, case, lens): n < T, n = T, block edges, several column blocks and head groups
+    (4, ai.DecodeCase("multi_T4_G4_D128", 31, B=8, Hq=8, Hkv=2, Lmax=320, D=128, lens_lo=0, lens_hi=0,
+                      fixed_lens=[0, 1, 3, 4, 5, 33, 100, 300]), None),
+    (16, ai.DecodeCase("multi_T16_G4_D128", 32, B=3, Hq=8, Hkv=2, Lmax=256, D=128, lens_lo=0, lens_hi=0,
+                       fixed_lens=[16, 17, 250]), None),
+    (16, ai.DecodeCase("multi_T16_G8_D64_two_groups", 33, B=3, Hq=8, Hkv=1, Lmax=256, D=64, lens_lo=0, lens_hi=0,
+                       fixed_lens=[5, 64, 200]), None),
+    (2, ai.DecodeCase("multi_T2_G1_D256", 34, B=3, Hq=2, Hkv=2, Lmax=128, D=256, lens_lo=0, lens_hi=0,
+                      fixed_lens=[1, 2, 77]), None),
+    (7, ai.DecodeCase("multi_T7_G6_D128", 35, B=4, Hq=12, Hkv=2, Lmax=2048, D=128, lens_lo=0, lens_hi=0,
+                      fixed_lens=[6, 7, 1000, 2048]), None),
+    (4, ai.DecodeCase("multi_T4_ragged_B16_G4", 36, B=16, Hq=32, Hkv=8, Lmax=4096, D=128, lens_lo=64, lens_hi=4096),
+     None),
+]
+
+
+@pytest.mark.parametrize("T,case,_", MULTI, ids=lambda x: x.name if hasattr(x, "name") else str(x))
+def test_decode_multi_parity(attn, T, case, _):
+    lens = case.kv_lens()
+    qb = multi_q_bits(case, T)
+    kc, vc = decode_cache_on_device(case, lens)
+    ro, rl = multi_reference(case, T, qb, lens)
+    out, lse = attn.decode_multi(to_dev(qb), kc, vc, torch.from_numpy(lens).to(DEV), scale=case.scale)
+    torch.cuda.synchronize()
+    check_out(to_np(out), ro, case.name)
+    check_lse(to_np(lse), rl, case.name)
+
+
+def test_decode_multi_one_row_is_decode(attn):
+    """T = 1 is attn_decode (same kernel path, identical bits)."""
+    case = ai.DecodeCase("multi_T1", 37, B=5, Hq=8, Hkv=2, Lmax=700, D=128, lens_lo=0, lens_hi=0,
+                         fixed_lens=[0, 1, 31, 300, 700])
+    lens = case.kv_lens()
+    kc, vc = decode_cache_on_device(case, lens)
+    q3 = to_dev(case.q_bits())
+    ld = torch.from_numpy(lens).to(DEV)
+    o1, l1 = attn.decode_ex(q3, kc, vc, ld, scale=case.scale)
+    om, lm = attn.decode_multi(q3[:, :, None, :].contiguous(), kc, vc, ld, scale=case.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, om[:, :, 0]) and torch.equal(l1, lm[:, :, 0])
+
+
+def test_decode_multi_caller_workspace(attn):
+    T, case = MULTI[4][0], MULTI[4][1]
+    lens = case.kv_lens()
+    kc, vc = decode_cache_on_device(case, lens)
+    q = to_dev(multi_q_bits(case, T))
+    ld = torch.from_numpy(lens).to(DEV)
+    nb = attn.decode_multi_workspace_bytes(case.B, case.Hq, case.Hkv, T, case.Lmax, case.D)
+    assert nb > 0
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    o1, l1 = attn.decode_multi(q, kc, vc, ld, scale=case.scale)
+    o2, l2 = attn.decode_multi(q, kc, vc, ld, scale=case.scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
