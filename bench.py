@@ -227,6 +227,27 @@ def all_configs(iters: int):
                           "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}), flush=True)
         del q, k, v, out, lse
 
+    # several new rows per sequence (speculative verification) over the ragged cache
+    dc = ai.RAGGED_DECODE
+    lens = dc.kv_lens()
+    kc, vc = build_decode_cache(dc, lens, dev)
+    dl = torch.from_numpy(lens).to(dev)
+    nb = acc.decode_kv_bytes(lens, dc.Hkv, dc.D, dc.Lmax)
+    for T in (2, 4, 8, 16):
+        qm = to_dev(ai.normal_bf16_bits((dc.B, dc.Hq, T, dc.D), [dc.wid, 0, dc.variant, 1000 + T]), dev)
+        om = torch.empty_like(qm)
+        fn = lambda: attn.decode_multi(qm, kc, vc, dl, scale=dc.scale, out=om, return_lse=False)  # noqa: E731
+        for _ in range(2):
+            fn()
+        ms = _time_ms(fn, iters, stream, between=lambda i: flush.fill_(i & 0xFF))
+        gbps = nb / (ms * 1e-3) / 1e9
+        print(json.dumps({"config": f"multi_query_decode_T{T}_ragged_B64", "kind": "decode_multi", "T": T, "B": dc.B,
+                          "Hq": dc.Hq, "Hkv": dc.Hkv, "Lmax": dc.Lmax, "D": dc.D, "ms": round(ms, 4), "kv_bytes": nb,
+                          "GB/s": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                          "flops": 4 * dc.D * dc.Hq * T * int(lens.sum())}), flush=True)
+    del kc, vc
+    torch.cuda.empty_cache()
+
     decodes = [ai.RAGGED_DECODE] + [ai.gsweep_decode(G) for G in ai.G_SWEEP]
     gen = torch.Generator(device=dev)
     for dc in decodes:
