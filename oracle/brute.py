@@ -15,9 +15,11 @@ from __future__ import annotations
 import math
 
 
-def brute_attention(q, k, v, causal: bool, scale: float):
+def brute_attention(q, k, v, causal: bool, scale: float, window: int = 0):
     """q [B][Hq][Lq][D], k/v [B][Hkv][Lk][D] (nested sequences or arrays).
 
+    window > 0 (causal): a row keeps only its `window` most recent visible
+    keys (the diagonal key and the window - 1 before it).
     Returns (out, lse) as nested lists of Python floats.
     """
     B, Hq, Lq, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
@@ -29,7 +31,10 @@ def brute_attention(q, k, v, causal: bool, scale: float):
         for h in range(Hq):
             kh = h // group
             for i in range(Lq):
-                keys = [j for j in range(Lk) if (not causal) or (j - i <= Lk - Lq)]
+                diag = i + (Lk - Lq)          # the row's own position among the keys
+                keys = [j for j in range(Lk) if (not causal) or j <= diag]
+                if causal and window:
+                    keys = keys[max(0, len(keys) - window):]
                 sc = []
                 for j in keys:
                     dot = math.fsum(float(q[b][h][i][d]) * float(k[b][kh][j][d]) for d in range(D))

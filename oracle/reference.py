@@ -39,15 +39,32 @@ def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
     return h // (Hq // Hkv)
 
 
-def visible_mask(Lq: int, Lk: int, causal: bool, align: str = "bottom_right") -> np.ndarray:
-    """Boolean [Lq, Lk] table of the keys each query row may attend to."""
+def visible_mask(Lq: int, Lk: int, causal: bool, align: str = "bottom_right", window: int = 0) -> np.ndarray:
+    """Boolean [Lq, Lk] table of the keys each query row may attend to.
+
+    window > 0 (causal only) keeps, of the keys a row sees, only the `window`
+    most recent ones: j > i + (Lk - Lq) - window.  This is the sliding-window
+    (local) attention the pages name as a way to shorten the effective KV
+    history [nvidia-long, "Параметр третий: длина последовательности"; the
+    cost-guide's "상황별 추천 구현" lists sliding windows among the masks
+    written for flex_attention].
+    """
+    if window < 0:
+        raise ValueError("window must be >= 0")
     if not causal:
+        if window:
+            raise ValueError("a window needs the causal mask")
         return np.ones((Lq, Lk), dtype=bool)
     i = np.arange(Lq)[:, None]
     j = np.arange(Lk)[None, :]
     if align == "bottom_right":
-        return j <= i + (Lk - Lq)
+        keep = j <= i + (Lk - Lq)
+        if window:
+            keep &= j > i + (Lk - Lq) - window
+        return keep
     if align == "upper_left":
+        if window:
+            raise ValueError("windows are anchored like the bottom-right mask")
         return j <= i
     raise ValueError(align)
 
@@ -76,16 +93,17 @@ def _check(q, k, v):
     return B, Hq, k.shape[1], Lq, k.shape[2], D
 
 
-def attention(q, k, v, causal: bool, scale: float, align: str = "bottom_right"):
+def attention(q, k, v, causal: bool, scale: float, align: str = "bottom_right", window: int = 0):
     """Full eager attention.  q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D] -> (out, lse).
 
     out is [B,Hq,Lq,D] float64, lse [B,Hq,Lq] float64 (natural log).
+    window: see visible_mask.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, Hq, Hkv, Lq, Lk, D = _check(q, k, v)
-    keep = visible_mask(Lq, Lk, causal, align)
+    keep = visible_mask(Lq, Lk, causal, align, window)
     out = np.empty((B, Hq, Lq, D))
     lse = np.empty((B, Hq, Lq))
     sc = np.float64(scale)
@@ -114,13 +132,15 @@ def attention_probs(q, k, causal: bool, scale: float, align: str = "bottom_right
     return P
 
 
-def attention_rows(q, k, v, rows, causal: bool, scale: float):
+def attention_rows(q, k, v, rows, causal: bool, scale: float, window: int = 0):
     """Selected query rows only (sampled mode for long sequences).
 
     rows: int array [B, Hq, R] of query-row indices.  Each selected row is
     computed exactly as in ``attention`` (same definition, same mask); only
     the rows not asked for are skipped.  Returns out [B,Hq,R,D], lse [B,Hq,R].
     """
+    if window and not causal:
+        raise ValueError("a window needs the causal mask")
     B, Hq, Lq, D = q.shape
     Hkv, Lk = k.shape[1], k.shape[2]
     rows = np.asarray(rows)
@@ -139,6 +159,8 @@ def attention_rows(q, k, v, rows, causal: bool, scale: float):
             s = sc * (qr @ kb.T)
             if causal:
                 s = np.where(j <= r[:, None] + (Lk - Lq), s, -np.inf)
+                if window:
+                    s = np.where(j > r[:, None] + (Lk - Lq) - window, s, -np.inf)
             p, lse[b, h] = _softmax_rows(s)
             out[b, h] = p @ vb
     return out, lse

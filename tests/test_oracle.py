@@ -295,6 +295,105 @@ def test_brute_force_enumeration():
 
 
 # ---------------------------------------------------------------------------
+# 5b. Sliding window (causal rows keep their `window` most recent keys).
+# ---------------------------------------------------------------------------
+def test_window_brute_force_enumeration():
+    rng = np.random.default_rng(21)
+    n = 0
+    for B, G, D in itertools.product((1, 2), (1, 4), (1, 8)):
+        Hkv = 2 if G < 4 else 1
+        Hq = G * Hkv
+        for Lk in range(1, 9):
+            for Lq in (1, 2, Lk):
+                if Lq > Lk:
+                    continue
+                for window in (1, 2, 3, 5):
+                    q = rng.standard_normal((B, Hq, Lq, D))
+                    k = rng.standard_normal((B, Hkv, Lk, D))
+                    v = rng.standard_normal((B, Hkv, Lk, D))
+                    o1, l1 = oracle.attention(q, k, v, True, 0.37, window=window)
+                    o2, l2 = oracle.brute_attention(q.tolist(), k.tolist(), v.tolist(), True, 0.37, window=window)
+                    np.testing.assert_allclose(o1, np.array(o2), rtol=0, atol=1e-12)
+                    np.testing.assert_allclose(l1, np.array(l2), rtol=0, atol=1e-12)
+                    n += 1
+    assert n > 300
+
+
+def _windowed_by_slices(q, k, v, scale, window):
+    """Each row as full (unmasked) attention over its own slice of keys: the
+    window's definition spelled without any mask."""
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    off = Lk - Lq
+    out = np.empty((B, Hq, Lq, D))
+    lse = np.empty((B, Hq, Lq))
+    for i in range(Lq):
+        hi = i + off + 1
+        lo = max(0, hi - window)
+        o, l_ = oracle.attention(q[:, :, i:i + 1], k[:, :, lo:hi], v[:, :, lo:hi], False, scale)
+        out[:, :, i], lse[:, :, i] = o[:, :, 0], l_[:, :, 0]
+    return out, lse
+
+
+@pytest.mark.parametrize("Lq,Lk,window", [(40, 40, 7), (16, 100, 33), (1, 50, 50), (30, 30, 1), (64, 200, 64)])
+def test_window_equals_attention_over_each_rows_slice(Lq, Lk, window):
+    rng = np.random.default_rng([22, Lq, Lk, window])
+    q = rng.standard_normal((1, 4, Lq, 8))
+    k = rng.standard_normal((1, 2, Lk, 8))
+    v = rng.standard_normal((1, 2, Lk, 8))
+    o1, l1 = oracle.attention(q, k, v, True, 0.3, window=window)
+    o2, l2 = _windowed_by_slices(q, k, v, 0.3, window)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-12)
+    rows = np.stack([np.stack([np.arange(0, Lq, 3) for _ in range(4)])])
+    o3, l3 = oracle.attention_rows(q, k, v, rows, True, 0.3, window=window)
+    np.testing.assert_allclose(o3, o1[:, :, ::3], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l3, l1[:, :, ::3], rtol=0, atol=1e-12)
+
+
+def test_window_special_cases():
+    rng = np.random.default_rng(23)
+    q = rng.standard_normal((1, 2, 20, 8))
+    k = rng.standard_normal((1, 1, 50, 8))
+    v = rng.standard_normal((1, 1, 50, 8))
+    off = 30
+    # a window at least as long as the keys is the plain causal mask
+    full = oracle.attention(q, k, v, True, 0.5)
+    for w in (50, 51, 1000):
+        o, l_ = oracle.attention(q, k, v, True, 0.5, window=w)
+        assert np.array_equal(o, full[0]) and np.array_equal(l_, full[1])
+    # a window of one key: the row's own position, weight 1
+    o, l_ = oracle.attention(q, k, v, True, 0.5, window=1)
+    for i in range(20):
+        np.testing.assert_allclose(o[0, :, i], np.repeat(v[0, :, i + off], 2, axis=0), rtol=0, atol=1e-15)
+        np.testing.assert_allclose(l_[0, :, i], 0.5 * (q[0, :, i] @ k[0, 0, i + off]), rtol=0, atol=1e-12)
+    # the window is anchored bottom-right: row i's keys end at i + Lk - Lq
+    keep = oracle.visible_mask(20, 50, True, window=4)
+    assert [int(np.flatnonzero(r)[0]) for r in keep] == [i + off - 3 for i in range(20)]
+    assert [int(np.flatnonzero(r)[-1]) for r in keep] == [i + off for i in range(20)]
+    with pytest.raises(ValueError):
+        oracle.visible_mask(4, 4, False, window=2)
+
+
+def test_window_planted_off_by_one_is_caught():
+    """A mask that keeps one key too many (j >= i + off - W) differs from the
+    slice definition: the slice test above would catch it."""
+    rng = np.random.default_rng(24)
+    q = rng.standard_normal((1, 1, 12, 4))
+    k = rng.standard_normal((1, 1, 30, 4))
+    v = rng.standard_normal((1, 1, 30, 4))
+    W, off = 5, 18
+    i = np.arange(12)[:, None]
+    j = np.arange(30)[None, :]
+    wrong = (j <= i + off) & (j >= i + off - W)
+    s = np.where(wrong, 0.3 * (q[0, 0] @ k[0, 0].T), -np.inf)
+    p, _ = ref._softmax_rows(s)
+    o_wrong = p @ v[0, 0]
+    o_right, _ = _windowed_by_slices(q, k, v, 0.3, W)
+    assert np.max(np.abs(o_wrong - o_right[0, 0])) > 1e-3
+
+
+# ---------------------------------------------------------------------------
 # 6. Input recipe.
 # ---------------------------------------------------------------------------
 def test_bf16_rounding_is_nearest_even():
@@ -328,13 +427,13 @@ def test_ragged_lengths_and_nan_tail():
 def test_planted_wrong_alignment_is_caught(golden_dir, monkeypatch):
     orig = ref.visible_mask
     monkeypatch.setattr(ref, "visible_mask",
-                        lambda Lq, Lk, causal, align="bottom_right": orig(Lq, Lk, causal, "upper_left"))
+                        lambda Lq, Lk, causal, align="bottom_right", window=0: orig(Lq, Lk, causal, "upper_left"))
     with pytest.raises(AssertionError):
         test_page_is_causal_example(golden_dir)
 
 
 def test_planted_off_by_one_mask_is_caught(monkeypatch):
-    def shifted(Lq, Lk, causal, align="bottom_right"):
+    def shifted(Lq, Lk, causal, align="bottom_right", window=0):
         if not causal:
             return np.ones((Lq, Lk), bool)
         i = np.arange(Lq)[:, None]
