@@ -31,11 +31,11 @@ def _load(path: str = LIB_PATH):
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.attn_prefill.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
     lib.attn_prefill.restype = i
-    lib.attn_prefill_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.attn_prefill_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp, sz, vp]
     lib.attn_prefill_ex.restype = i
-    lib.attn_prefill_splits.argtypes = [i, i, i, i, i, i, i, i]
+    lib.attn_prefill_splits.argtypes = [i, i, i, i, i, i, i, i, i]
     lib.attn_prefill_splits.restype = i
-    lib.attn_prefill_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
+    lib.attn_prefill_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i]
     lib.attn_prefill_workspace_bytes.restype = sz
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
     lib.attn_decode.restype = i
@@ -127,23 +127,24 @@ def prefill(q, k, v, causal: bool = True, scale: float | None = None, out=None, 
 
 
 def prefill_ex(q, k, v, causal: bool = True, scale: float | None = None, splits: int = 0, out=None, lse=None,
-               return_lse: bool = True, workspace=None):
-    """attn_prefill_ex: prefill with a key-split count (0 = automatic) and an optional workspace."""
+               return_lse: bool = True, workspace=None, window: int = 0):
+    """attn_prefill_ex: prefill with a sliding window (0 = none), a key-split count (0 = automatic) and an
+    optional workspace."""
     B, Hq, Hkv, Lq, Lk, D, out, lse = _prefill_args(q, k, v, out, lse, return_lse)
     scale = default_scale(D) if scale is None else float(scale)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.attn_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Lq, Lk, D,
-                               1 if causal else 0, ctypes.c_float(scale), int(splits), _ptr(workspace), ws_bytes,
-                               _stream(q.device)))
+                               1 if causal else 0, int(window), ctypes.c_float(scale), int(splits), _ptr(workspace),
+                               ws_bytes, _stream(q.device)))
     return out, lse
 
 
-def prefill_splits(B, Hq, Hkv, Lq, Lk, D, causal=True, splits=0) -> int:
-    return int(lib.attn_prefill_splits(B, Hq, Hkv, Lq, Lk, D, 1 if causal else 0, splits))
+def prefill_splits(B, Hq, Hkv, Lq, Lk, D, causal=True, splits=0, window=0) -> int:
+    return int(lib.attn_prefill_splits(B, Hq, Hkv, Lq, Lk, D, 1 if causal else 0, window, splits))
 
 
-def prefill_workspace_bytes(B, Hq, Hkv, Lq, Lk, D, causal=True, splits=0) -> int:
-    return int(lib.attn_prefill_workspace_bytes(B, Hq, Hkv, Lq, Lk, D, 1 if causal else 0, splits))
+def prefill_workspace_bytes(B, Hq, Hkv, Lq, Lk, D, causal=True, splits=0, window=0) -> int:
+    return int(lib.attn_prefill_workspace_bytes(B, Hq, Hkv, Lq, Lk, D, 1 if causal else 0, window, splits))
 
 
 def decode(q, kcache, vcache, kv_lens, scale: float | None = None, out=None):

@@ -174,12 +174,12 @@ int device_cus(int *cus) {
 // splits: 0 chooses the key-split count: 1 when the grid already has at least
 // two workgroups per compute unit, else enough ranges for that (each of at
 // least 8 tiles, at most 32 ranges); otherwise 1..kPrefillMaxSplits.
-int prefill_setup(PrefillArgs *pa, int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, float scale,
-                  int splits) {
+int prefill_setup(PrefillArgs *pa, int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, int window,
+                  float scale, int splits) {
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_GQA;
   if (!head_dim_ok(D)) return ATTN_ERR_HEADDIM;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
-  if (B < 0 || Lq < 0 || Lk < 0) return ATTN_ERR_SHAPE;
+  if (B < 0 || Lq < 0 || Lk < 0 || window < 0 || (window > 0 && !causal)) return ATTN_ERR_SHAPE;
   if (splits < 0 || splits > attn::kPrefillMaxSplits) return ATTN_ERR_SPLIT;
   if (B == 0 || Lq == 0) {
     pa->nsplit = 0;
@@ -197,6 +197,7 @@ int prefill_setup(PrefillArgs *pa, int B, int Hq, int Hkv, int Lq, int Lk, int D
   a.Lk = Lk;
   a.G = Hq / Hkv;
   a.causal = causal ? 1 : 0;
+  a.window = (causal && window < Lk) ? window : 0;   // a window of Lk or more keys hides nothing
   a.c = scale * kLog2e;
   a.nsplit = 1;
   if (!attn::prefill_plan(a, D)) return ATTN_ERR_SHAPE;
@@ -208,7 +209,8 @@ int prefill_setup(PrefillArgs *pa, int B, int Hq, int Hkv, int Lq, int Lk, int D
     ns = 1;
     if (units < 2LL * cus) {
       const int tk = attn::prefill_tile_keys(D);
-      long long cap = ((long long)Lk + tk - 1) / tk / 8;
+      const long long keys = a.window ? (long long)a.window + a.Bq : (long long)Lk;   // per query block, at most
+      long long cap = (keys + tk - 1) / tk / 8;
       if (cap > 32) cap = 32;
       long long want = (2LL * cus + units - 1) / units;
       if (want > cap) want = cap;
@@ -230,17 +232,18 @@ size_t prefill_workspace(const PrefillArgs &a, int D) {
 }
 
 int run_prefill(const void *q, const void *k, const void *v, void *out, float *lse, int B, int Hq, int Hkv, int Lq,
-                int Lk, int D, int causal, float scale, int splits, void *ws, size_t ws_bytes, void *stream) {
+                int Lk, int D, int causal, int window, float scale, int splits, void *ws, size_t ws_bytes,
+                void *stream) {
   // checks in the documented order; prefill_setup repeats the first ones
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_GQA;
   if (!head_dim_ok(D)) return ATTN_ERR_HEADDIM;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
-  if (B < 0 || Lq < 0 || Lk < 0) return ATTN_ERR_SHAPE;
+  if (B < 0 || Lq < 0 || Lk < 0 || window < 0 || (window > 0 && !causal)) return ATTN_ERR_SHAPE;
   if (splits < 0 || splits > attn::kPrefillMaxSplits) return ATTN_ERR_SPLIT;
   if (B == 0 || Lq == 0) return ATTN_OK;  // empty: nothing read or written, pointers may be NULL
   if (!q || !k || !v || !out) return ATTN_ERR_NULL;
   PrefillArgs a;
-  int st = prefill_setup(&a, B, Hq, Hkv, Lq, Lk, D, causal, scale, splits);
+  int st = prefill_setup(&a, B, Hq, Hkv, Lq, Lk, D, causal, window, scale, splits);
   if (st != ATTN_OK) return st;
   const size_t need = prefill_workspace(a, D);
   if (ws != nullptr && ws_bytes < need) return ATTN_ERR_WORKSPACE;
@@ -277,25 +280,26 @@ extern "C" {
 
 int attn_prefill(const void *q, const void *k, const void *v, void *out, float *lse, int B, int Hq, int Hkv,
                  int Lq, int Lk, int D, int causal, float scale, void *stream) {
-  return run_prefill(q, k, v, out, lse, B, Hq, Hkv, Lq, Lk, D, causal, scale, 0, nullptr, 0, stream);
+  return run_prefill(q, k, v, out, lse, B, Hq, Hkv, Lq, Lk, D, causal, 0, scale, 0, nullptr, 0, stream);
 }
 
 int attn_prefill_ex(const void *q, const void *k, const void *v, void *out, float *lse, int B, int Hq, int Hkv,
-                    int Lq, int Lk, int D, int causal, float scale, int splits, void *workspace,
+                    int Lq, int Lk, int D, int causal, int window, float scale, int splits, void *workspace,
                     size_t workspace_bytes, void *stream) {
-  return run_prefill(q, k, v, out, lse, B, Hq, Hkv, Lq, Lk, D, causal, scale, splits, workspace, workspace_bytes,
-                     stream);
+  return run_prefill(q, k, v, out, lse, B, Hq, Hkv, Lq, Lk, D, causal, window, scale, splits, workspace,
+                     workspace_bytes, stream);
 }
 
-int attn_prefill_splits(int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, int splits) {
+int attn_prefill_splits(int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, int window, int splits) {
   PrefillArgs a;
-  int st = prefill_setup(&a, B, Hq, Hkv, Lq, Lk, D, causal, 1.f, splits);
+  int st = prefill_setup(&a, B, Hq, Hkv, Lq, Lk, D, causal, window, 1.f, splits);
   return st == ATTN_OK ? a.nsplit : 0;
 }
 
-size_t attn_prefill_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, int splits) {
+size_t attn_prefill_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, int window,
+                                    int splits) {
   PrefillArgs a;
-  if (prefill_setup(&a, B, Hq, Hkv, Lq, Lk, D, causal, 1.f, splits) != ATTN_OK) return 0;
+  if (prefill_setup(&a, B, Hq, Hkv, Lq, Lk, D, causal, window, 1.f, splits) != ATTN_OK) return 0;
   return prefill_workspace(a, D);
 }
 

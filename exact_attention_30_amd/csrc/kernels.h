@@ -23,6 +23,7 @@ struct PrefillArgs {
   int total;   // workgroups in the grid (including the key splits)
   int causal;
   float c;     // scale * log2(e)
+  int window;       // causal sliding window: a row sees its `window` most recent keys (0: all)
   int nsplit;       // key ranges per query block (1: the kernel writes out and lse itself)
   float *part_o;    // nsplit > 1: [rows][nsplit][D] normalised partial outputs, rows = B * Hq * Lq
   float *part_lse;  // nsplit > 1: [rows][nsplit] partial log-sum-exps (-inf for an empty range)

@@ -139,10 +139,17 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
   int kend_w = 0;
   if (q0w < a.Lq) kend_w = a.causal ? min(a.Lk, min(q0w + 31, a.Lq - 1) + off + 1) : a.Lk;
   const int kmask_from = a.causal ? min(a.Lk, q0w + off + 1) : a.Lk;  // first key some row of the wave hides
+  // sliding window: row i sees keys [i + off - window + 1, i + off]
+  const int win = a.window;
+  const int kbeg_wg = win ? max(0, qblk * a.Bq + off - win + 1) : 0;   // first key of the first row
+  const int kbeg_w = win ? max(0, q0w + off - win + 1) : 0;             // ... of this wave's first row
+  const int klo_until = win ? q0w + 31 + off - win + 1 : 0;             // keys below: hidden from some row
+  const int qlo = win ? qrow + off - win + 1 : -0x7fffffff;             // this lane's first visible key
   // this workgroup's share of the tiles: [j0, j0 + nt)
-  const int nt_all = (kend_wg + BK - 1) / BK;
-  const int j0 = (int)((long long)nt_all * sp / a.nsplit);
-  const int nt = (int)((long long)nt_all * (sp + 1) / a.nsplit) - j0;
+  const int jbeg = kbeg_wg / BK;
+  const int nt_all = (kend_wg + BK - 1) / BK - jbeg;
+  const int j0 = jbeg + (int)((long long)nt_all * sp / a.nsplit);
+  const int nt = jbeg + (int)((long long)nt_all * (sp + 1) / a.nsplit) - j0;
 
   // ---- Q (B operand of S^T), kept in registers ----------------------------
   const int qr = min(qrow, a.Lq - 1);
@@ -314,7 +321,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
   const bool grpA = w < C::NW / 2;
   f32x16 s[BK / 32];
   auto active = [&](int jj) __attribute__((always_inline)) {
-    return jj >= 0 && jj < nt && (j0 + jj) * BK < kend_w;
+    return jj >= 0 && jj < nt && (j0 + jj) * BK < kend_w && (j0 + jj + 1) * BK > kbeg_w;
   };
   auto gemm = [&](int jj, const uint16_t *ks_, const uint16_t *vs_) __attribute__((always_inline)) {
     if (!ATTN_PF_QKFIRST && active(jj - 1)) pv(vs_);
@@ -343,14 +350,14 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
   auto soft = [&](int jj) __attribute__((always_inline)) {
     if (!active(jj)) return;
     const int k0 = (j0 + jj) * BK;
-    if (k0 + BK > kmask_from) {
+    if (k0 + BK > kmask_from || k0 < klo_until) {
       const int lim = a.causal ? min(a.Lk - 1, qrow + off) : a.Lk - 1;
 #pragma unroll
       for (int rb = 0; rb < BK / 32; ++rb)
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
           const int key = k0 + 32 * rb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-          s[rb][rr] = key <= lim ? s[rb][rr] : maskval;
+          s[rb][rr] = (key <= lim && key >= qlo) ? s[rb][rr] : maskval;
         }
       softmax(s, std::true_type{});
     } else {

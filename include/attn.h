@@ -109,7 +109,14 @@ int attn_prefill(const void *q, const void *k, const void *v, void *out, float *
                  void *stream);
 
 /*
- * attn_prefill_ex -- attn_prefill with two extra controls:
+ * attn_prefill_ex -- attn_prefill with three extra controls:
+ *   window     0: no window.  > 0 (needs causal, else ATTN_ERR_SHAPE): sliding
+ *              window, row i sees only its `window` most recent visible keys,
+ *              j in [i + (Lk - Lq) - window + 1, i + (Lk - Lq)] (the local
+ *              attention the NVIDIA page names for cutting the effective KV
+ *              length, section "Параметр третий: длина последовательности").
+ *              Tiles outside every row's window are skipped.  window >= Lk is
+ *              the plain causal mask.  Negative: ATTN_ERR_SHAPE.
  *   splits     0: choose the number of key ranges per query block as
  *              attn_prefill does; 1..64: use exactly that many (else
  *              ATTN_ERR_SPLIT).  Results agree for every count up to fp32
@@ -120,11 +127,12 @@ int attn_prefill(const void *q, const void *k, const void *v, void *out, float *
  *              attn_prefill_workspace_bytes(...) bytes (else
  *              ATTN_ERR_WORKSPACE) and must not be used by other work until
  *              this call's kernels have finished on `stream`.
- * Validation order: as attn_prefill, with the splits check after the size
- * checks and before the empty-call return.
+ * Validation order: as attn_prefill (the window is checked with the sizes),
+ * with the splits check after the size checks and before the empty-call
+ * return.
  */
 int attn_prefill_ex(const void *q, const void *k, const void *v, void *out, float *lse,
-                    int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, float scale,
+                    int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, int window, float scale,
                     int splits, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
@@ -132,7 +140,7 @@ int attn_prefill_ex(const void *q, const void *k, const void *v, void *out, floa
  * these sizes and splits on the current device; 0 for an empty call, invalid
  * arguments, or splits == 0 with no device available.
  */
-int attn_prefill_splits(int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, int splits);
+int attn_prefill_splits(int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, int window, int splits);
 
 /*
  * attn_prefill_workspace_bytes -- bytes of workspace attn_prefill_ex needs
@@ -141,7 +149,7 @@ int attn_prefill_splits(int B, int Hq, int Hkv, int Lq, int Lk, int D, int causa
  * B*Hq*Lq*n*D fp32 outputs (n ranges), each part 256-byte aligned.
  */
 size_t attn_prefill_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal,
-                                    int splits);
+                                    int window, int splits);
 
 /*
  * attn_decode -- one new query row per sequence over a ragged KV cache.

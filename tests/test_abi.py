@@ -121,9 +121,9 @@ def test_binding_rejects_cpu_tensors(attn):
         attn.prefill(q.float(), q[:, :1], q[:, :1])
 
 
-def prefill_ex(attn, splits=0, ws=N, ws_bytes=0, q=P, B=1, Hq=32, Hkv=8, Lq=512, Lk=16384, D=128, causal=1):
-    return attn.lib.attn_prefill_ex(q, P, P, P, N, B, Hq, Hkv, Lq, Lk, D, causal, ctypes.c_float(0.0884), splits,
-                                    ws, ws_bytes, None)
+def prefill_ex(attn, splits=0, ws=N, ws_bytes=0, q=P, B=1, Hq=32, Hkv=8, Lq=512, Lk=16384, D=128, causal=1, window=0):
+    return attn.lib.attn_prefill_ex(q, P, P, P, N, B, Hq, Hkv, Lq, Lk, D, causal, window, ctypes.c_float(0.0884),
+                                    splits, ws, ws_bytes, None)
 
 
 def test_prefill_split_validation_and_sizes(attn):
@@ -150,6 +150,12 @@ def test_prefill_split_validation_and_sizes(attn):
     assert prefill_ex(attn, splits=3, q=N) == -1
     need = attn.prefill_workspace_bytes(1, 32, 8, 512, 16384, 128, True, 4)
     assert prefill_ex(attn, splits=4, ws=P, ws_bytes=need - 1) == -8
+    # sliding window: causal only, not negative
+    assert prefill_ex(attn, splits=2, window=-1) == -2
+    assert prefill_ex(attn, splits=2, window=16, causal=0, Lq=16, Lk=16) == -2
+    assert prefill_ex(attn, splits=2, window=16, B=0) == 0
+    assert attn.prefill_splits(1, 32, 8, 512, 16384, 128, True, 3, window=100) == 3
+    assert attn.prefill_splits(1, 32, 8, 512, 16384, 128, False, 3, window=100) == 0
 
 
 def test_decode_multi_validation_and_sizes(attn):

@@ -215,3 +215,54 @@ def test_prefill_lse_optional(attn):
     q, k, v = d.f64()
     ro, _ = oracle.attention(q, k, v, True, ai.TINY.scale)
     check_out(to_np(out), ro, "no-lse")
+
+
+# ---- sliding window ------------------------------------------------------------
+
+WINDOW_CASES = [
+    (ai.PrefillCase("win37_G2_L300_D64", 41, B=1, Hq=4, Hkv=2, Lq=300, Lk=300, D=64), 37),
+    (ai.PrefillCase("win64_chunk_G3_Lq77_Lk200_D128", 42, B=1, Hq=6, Hkv=2, Lq=77, Lk=200, D=128), 64),
+    (ai.PrefillCase("win1_G1_L130_D128", 43, B=1, Hq=2, Hkv=2, Lq=130, Lk=130, D=128), 1),
+    (ai.PrefillCase("win_ge_Lk_G1_Lq33_Lk129_D128", 44, B=1, Hq=2, Hkv=2, Lq=33, Lk=129, D=128), 200),
+    (ai.PrefillCase("win50_G2_L100_D256", 45, B=2, Hq=4, Hkv=2, Lq=100, Lk=100, D=256), 50),
+    (ai.PrefillCase("win100_G8_L257_D128", 46, B=1, Hq=8, Hkv=1, Lq=257, Lk=257, D=128), 100),
+    (ai.PrefillCase("win65_G4_L1000_D128", 47, B=1, Hq=8, Hkv=2, Lq=1000, Lk=1000, D=128), 65),
+]
+
+
+@pytest.mark.parametrize("splits", [0, 3])
+@pytest.mark.parametrize("case,window", WINDOW_CASES, ids=lambda x: x.name if hasattr(x, "name") else str(x))
+def test_prefill_window(attn, case, window, splits):
+    d = PrefillData(case)
+    out, lse = attn.prefill_ex(d.q, d.k, d.v, causal=True, scale=case.scale, window=window, splits=splits)
+    torch.cuda.synchronize()
+    q, k, v = d.f64()
+    ro, rl = oracle.attention(q, k, v, True, case.scale, window=window)
+    check_out(to_np(out), ro, f"{case.name} splits={splits}")
+    check_lse(to_np(lse), rl, f"{case.name} splits={splits}")
+
+
+def test_prefill_window_long_sampled(attn):
+    """Qwen3-8B heads at 16K with a 4096-key window, 64 sampled rows per head."""
+    case, window = ai.QWEN_16K, 4096
+    d = PrefillData(case)
+    out, lse = attn.prefill_ex(d.q, d.k, d.v, causal=True, scale=case.scale, window=window)
+    torch.cuda.synchronize()
+    rows = np.stack([np.stack([ai.rows_for_head(case.wid * 1000 + case.variant, b, h, case.Lq, 64)
+                               for h in range(case.Hq)]) for b in range(case.B)])
+    q, k, v = d.f64()
+    ro, rl = oracle.attention_rows(q, k, v, rows, True, case.scale, window=window)
+    bi = np.arange(case.B)[:, None, None]
+    hi = np.arange(case.Hq)[None, :, None]
+    check_out(to_np(out)[bi, hi, rows], ro, "window 4096 at 16K")
+    check_lse(to_np(lse)[bi, hi, rows], rl, "window 4096 at 16K")
+
+
+def test_prefill_window_at_least_lk_is_causal(attn):
+    case = WINDOW_CASES[0][0]
+    d = PrefillData(case)
+    o1, l1 = attn.prefill(d.q, d.k, d.v, causal=True, scale=case.scale)
+    o2, l2 = attn.prefill_ex(d.q, d.k, d.v, causal=True, scale=case.scale, window=case.Lk)
+    o3, l3 = attn.prefill_ex(d.q, d.k, d.v, causal=True, scale=case.scale, window=10 * case.Lk)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(o1, o3) and torch.equal(l1, l3)
