@@ -41,7 +41,7 @@ def _load(path: str = LIB_PATH):
     lib.attn_decode.restype = i
     lib.attn_decode_ex.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     lib.attn_decode_ex.restype = i
-    lib.attn_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+    lib.attn_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
     lib.attn_decode_multi.restype = i
     lib.attn_decode_multi_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.attn_decode_multi_workspace_bytes.restype = sz
@@ -176,8 +176,9 @@ def decode_ex(q, kcache, vcache, kv_lens, scale: float | None = None, split_keys
 
 
 def decode_multi(q, kcache, vcache, kv_lens, scale: float | None = None, out=None, return_lse: bool = True,
-                 workspace=None):
-    """attn_decode_multi: q [B,Hq,T,D] (the last T cached tokens of each sequence) -> (out, lse [B,Hq,T])."""
+                 workspace=None, window: int = 0):
+    """attn_decode_multi: q [B,Hq,T,D] (the last T cached tokens of each sequence) -> (out, lse [B,Hq,T]);
+    window > 0 limits each row to its window most recent keys."""
     _need(q, "q", torch.bfloat16, 4)
     _need(kcache, "kcache", torch.bfloat16, 4)
     _need(vcache, "vcache", torch.bfloat16, 4)
@@ -194,7 +195,7 @@ def decode_multi(q, kcache, vcache, kv_lens, scale: float | None = None, out=Non
     scale = default_scale(D) if scale is None else float(scale)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.attn_decode_multi(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(kv_lens), _ptr(out), _ptr(lse), B, Hq,
-                                 Hkv, T, Lmax, D, ctypes.c_float(scale), _ptr(workspace), ws_bytes,
+                                 Hkv, T, int(window), Lmax, D, ctypes.c_float(scale), _ptr(workspace), ws_bytes,
                                  _stream(q.device)))
     return out, lse
 

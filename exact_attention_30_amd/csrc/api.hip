@@ -114,10 +114,11 @@ int decode_check(const void *q, const void *kc, const void *vc, const int32_t *l
 }
 
 int run_decode(const void *q, const void *kc, const void *vc, const int32_t *lens, void *out, float *lse, int B,
-               int Hq, int Hkv, int T, int Lmax, int D, float scale, int split_keys, void *ws, size_t ws_bytes,
-               void *stream) {
+               int Hq, int Hkv, int T, int window, int Lmax, int D, float scale, int split_keys, void *ws,
+               size_t ws_bytes, void *stream) {
   int st = decode_check(q, kc, vc, lens, out, B, Hq, Hkv, T, Lmax, D, scale);
   if (st != ATTN_OK) return st;
+  if (window < 0) return ATTN_ERR_SHAPE;
   if (split_keys != 0 && (split_keys < 0 || split_keys % 128 != 0)) return ATTN_ERR_SPLIT;
   DecodeShape ds;
   decode_workspace(B, Hq, Hkv, T, D, &ds);
@@ -152,6 +153,7 @@ int run_decode(const void *q, const void *kc, const void *vc, const int32_t *len
   a.Lmax = Lmax;
   a.G = Hq / Hkv;
   a.T = T;
+  a.window = window < Lmax ? window : 0;   // a window of Lmax or more keys hides nothing
   a.n_hg = (a.G * T + attn::kDecodeGroup - 1) / attn::kDecodeGroup;
   a.c = scale * kLog2e;
   hipError_t e = attn::launch_decode(a, D, ds.waves, s);
@@ -305,21 +307,21 @@ size_t attn_prefill_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int 
 
 int attn_decode(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens, void *out, int B,
                 int Hq, int Hkv, int Lmax, int D, float scale, void *stream) {
-  return run_decode(q, kcache, vcache, kv_lens, out, nullptr, B, Hq, Hkv, 1, Lmax, D, scale, 0, nullptr, 0,
+  return run_decode(q, kcache, vcache, kv_lens, out, nullptr, B, Hq, Hkv, 1, 0, Lmax, D, scale, 0, nullptr, 0,
                     stream);
 }
 
 int attn_decode_ex(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens, void *out,
                    float *lse, int B, int Hq, int Hkv, int Lmax, int D, float scale, int split_keys,
                    void *workspace, size_t workspace_bytes, void *stream) {
-  return run_decode(q, kcache, vcache, kv_lens, out, lse, B, Hq, Hkv, 1, Lmax, D, scale, split_keys, workspace,
+  return run_decode(q, kcache, vcache, kv_lens, out, lse, B, Hq, Hkv, 1, 0, Lmax, D, scale, split_keys, workspace,
                     workspace_bytes, stream);
 }
 
 int attn_decode_multi(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens, void *out,
-                      float *lse, int B, int Hq, int Hkv, int T, int Lmax, int D, float scale, void *workspace,
-                      size_t workspace_bytes, void *stream) {
-  return run_decode(q, kcache, vcache, kv_lens, out, lse, B, Hq, Hkv, T, Lmax, D, scale, 0, workspace,
+                      float *lse, int B, int Hq, int Hkv, int T, int window, int Lmax, int D, float scale,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+  return run_decode(q, kcache, vcache, kv_lens, out, lse, B, Hq, Hkv, T, window, Lmax, D, scale, 0, workspace,
                     workspace_bytes, stream);
 }
 

@@ -68,16 +68,26 @@ ATTN_DEV long long wave_of(long long x, long long total, long long W) {
   return rem + (x - big) / q;
 }
 
-// Planner: pre[b] = sum over b' < b of ceil(min(max(lens[b'], 0), Lmax) / 32),
-// pre[B] = the total.  One workgroup of 1024 threads; each thread owns a
-// contiguous slice of sequences.
+// First key of sequence b's segment: with a window, the earliest key any of
+// its T rows sees, rounded down to a 32-key block; else 0.
+ATTN_DEV int seg_begin(const DecodeArgs &a, int n) {
+  return a.window ? (max(0, n - a.T - a.window + 1) & ~31) : 0;
+}
+ATTN_DEV long long seg_blocks(const DecodeArgs &a, int b) {
+  const int n = max(0, min(a.lens[b], a.Lmax));
+  return (n - seg_begin(a, n) + 31) / 32;
+}
+
+// Planner: pre[b] = sum over b' < b of the key blocks of sequence b'
+// (ceil((n - first key) / 32)), pre[B] = the total.  One workgroup of 1024
+// threads; each thread owns a contiguous slice of sequences.
 __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a) {
   __shared__ long long part[1024];
   const int t = threadIdx.x;
   const int per = (a.B + 1023) / 1024;
   const int b0 = min(a.B, t * per), b1 = min(a.B, b0 + per);
   long long sum = 0;
-  for (int b = b0; b < b1; ++b) sum += (max(0, min(a.lens[b], a.Lmax)) + 31) / 32;
+  for (int b = b0; b < b1; ++b) sum += seg_blocks(a, b);
   part[t] = sum;
   __syncthreads();
   // inclusive scan of the 1024 slice sums (Hillis-Steele)
@@ -90,7 +100,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a) {
   long long run = part[t] - sum;  // exclusive prefix of this slice
   for (int b = b0; b < b1; ++b) {
     a.pre[b] = run;
-    run += (max(0, min(a.lens[b], a.Lmax)) + 31) / 32;
+    run += seg_blocks(a, b);
   }
   if (t == 1023) a.pre[a.B] = part[1023];
 }
@@ -145,15 +155,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
     const int gq0 = hg * kDecodeGroup;
     const int gcnt = min(kDecodeGroup, GT - gq0);
     const int n = max(0, min(a.lens[b], a.Lmax));
-    const int k0 = (int)(blk * 32);
-    const int k1 = min(n, (int)((blk + take) * 32));
+    const int kseg = seg_begin(a, n);
+    const int kmin = a.window ? max(0, n - a.T - a.window + 1) : 0;   // keys below are never read
+    const int k0 = kseg + (int)(blk * 32);
+    const int k1 = min(n, kseg + (int)((blk + take) * 32));
     const bool whole = (blk == 0) && (take == nb);
     // causal limit of this lane's query row in each column block: with T new
     // rows at the end of the cache, row t sees keys [0, n - T + t]
-    int kcol[NCB];
+    // (and with a window, keys [n - T + t - window + 1, ...])
+    int kcol[NCB], klo[NCB];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) kcol[cb] = n - a.T + 1 + (gq0 + 16 * cb + ql) % a.T;
-    const int kfull = min(k1, n - a.T + 1);   // keys below this are visible to every row
+    for (int cb = 0; cb < NCB; ++cb) {
+      kcol[cb] = n - a.T + 1 + (gq0 + 16 * cb + ql) % a.T;
+      klo[cb] = a.window ? kcol[cb] - a.window : -0x7fffffff;
+    }
+    const int kfull = min(k1, n - a.T + 1);                      // keys below: below every row's limit
+    const int klo_all = a.window ? n - a.window : -0x7fffffff;   // keys from here: above every row's start
     const long long slot = (long long)b * HH + hh + w;
 
     bf16x8 qf[NCB][KST];
@@ -188,7 +205,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
   #pragma unroll
         for (int ks = 0; ks < KST; ++ks) {
           const uint16_t *pk = p + (ATTN_DEC_KNAT ? 32 * ks + 8 * g : (D / 4) * g + 8 * ks);
-          kr[rb * KST + ks] = key < k1 ? (ATTN_DEC_KNT ? ld16_stream(pk) : ld16(pk)) : zero4;
+          kr[rb * KST + ks] = (key < k1 && key >= kmin) ? (ATTN_DEC_KNT ? ld16_stream(pk) : ld16(pk)) : zero4;
         }
       }
   #pragma unroll
@@ -200,7 +217,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
           for (int kk = 0; kk < 8; ++kk) {
             const int key = kb + (kk < 4 ? 4 * gg + kk : 16 + 4 * gg + kk - 4);
             const uint16_t *pv = vg + (size_t)key * D + 8 * c;
-            vr[iu][kk] = key < k1 ? (ATTN_DEC_VNT ? ld16_stream(pv) : ld16(pv)) : zero4;
+            vr[iu][kk] = (key < k1 && key >= kmin) ? (ATTN_DEC_VNT ? ld16_stream(pv) : ld16(pv)) : zero4;
           }
         }
       }
@@ -244,7 +261,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
             s[cb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[rb * KST + ks]), qf[cb][ks], s[cb][rb], 0, 0, 0);
         }
       __syncthreads();
-      const bool partial = kb + 32 > kfull;
+      const bool partial = kb + 32 > kfull || kb < klo_all;
       bf16x8 pb[NCB];
   #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
@@ -256,7 +273,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
   #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
               const int key = kb + 16 * rb + 4 * g + rr;
-              const bool vv = key < k1 && key < kcol[cb];
+              const bool vv = key < k1 && key < kcol[cb] && key >= klo[cb];
               vis |= (vv ? 1u : 0u) << (4 * rb + rr);
               s[cb][rb][rr] = vv ? s[cb][rb][rr] : maskval;
             }

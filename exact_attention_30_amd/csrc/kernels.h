@@ -42,6 +42,7 @@ struct DecodeArgs {
   int B, Hq, Hkv, Lmax;
   int G;            // Hq / Hkv
   int T;            // query rows per sequence and head (1: plain decode)
+  int window;       // sliding window: row t sees its `window` most recent keys (0: all)
   int n_hg;         // groups of up to kDecodeGroup query rows per KV head
                     // (a KV head's G * T rows; GW = min(G * T, kDecodeGroup))
   float c;          // scale * log2(e)

@@ -210,6 +210,11 @@ int attn_decode_ex(const void *q, const void *kcache, const void *vcache, const 
  *   q, out  [B][Hq][T][D] bf16        lse [B][Hq][T] fp32, may be NULL
  *   kcache, vcache [B][Hkv][Lmax][D] bf16, kv_lens [B] int32 (device)
  *
+ * window > 0: sliding window, row t sees only keys [n_b - T + t - window + 1,
+ * n_b - T + t] (keys before the earliest window start are not read at all);
+ * 0: no window; negative: ATTN_ERR_SHAPE.  With T = 1 this is a windowed
+ * single-token decode.
+ *
  * The G * T rows of one KV head (G = Hq / Hkv) share every K/V read, in
  * groups of up to 64 rows.  1 <= T <= Lmax (else ATTN_ERR_SHAPE).  Key ranges
  * are chosen as attn_decode does; workspace as attn_decode_ex (NULL: taken
@@ -217,8 +222,8 @@ int attn_decode_ex(const void *q, const void *kcache, const void *vcache, const 
  * attn_decode_multi_workspace_bytes.
  */
 int attn_decode_multi(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens,
-                      void *out, float *lse, int B, int Hq, int Hkv, int T, int Lmax, int D, float scale,
-                      void *workspace, size_t workspace_bytes, void *stream);
+                      void *out, float *lse, int B, int Hq, int Hkv, int T, int window, int Lmax, int D,
+                      float scale, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * attn_decode_multi_workspace_bytes -- bytes of workspace attn_decode_multi

@@ -162,8 +162,8 @@ def test_decode_multi_validation_and_sizes(attn):
     def al(x):
         return (x + 255) // 256 * 256
 
-    def multi(T=4, B=2, Hq=8, Hkv=2, Lmax=64, D=128, q=P, ws=N, ws_bytes=0):
-        return attn.lib.attn_decode_multi(q, P, P, P, P, N, B, Hq, Hkv, T, Lmax, D, ctypes.c_float(0.1), ws,
+    def multi(T=4, B=2, Hq=8, Hkv=2, Lmax=64, D=128, q=P, ws=N, ws_bytes=0, window=0):
+        return attn.lib.attn_decode_multi(q, P, P, P, P, N, B, Hq, Hkv, T, window, Lmax, D, ctypes.c_float(0.1), ws,
                                           ws_bytes, None)
     assert multi(T=0) == -2
     assert multi(T=65) == -2            # more new rows than cache slots
@@ -171,6 +171,7 @@ def test_decode_multi_validation_and_sizes(attn):
     assert multi(D=32) == -3
     assert multi(q=N) == -1
     assert multi(B=0, q=N) == 0
+    assert multi(window=-1) == -2
     # rows of a KV head: G * T, in groups of up to 64
     B, Hq, Hkv, T, D = 3, 32, 8, 4, 128      # G * T = 16 -> one group of 16
     slots = 4096 + B * Hkv

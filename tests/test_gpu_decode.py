@@ -160,9 +160,10 @@ def multi_q_bits(case, T):
     return ai.normal_bf16_bits((case.B, case.Hq, T, case.D), [case.wid, 0, case.variant, 1000 + T])
 
 
-def multi_reference(case, T, qb, lens):
+def multi_reference(case, T, qb, lens, window=0):
     """Oracle per sequence: the last min(n, T) rows attend [0, n) with the
-    bottom-right causal mask; rows that see no key are 0 / -inf."""
+    bottom-right causal mask (and the window, if any); rows that see no key
+    are 0 / -inf."""
     q = ai.bf16_bits_to_f64(qb)
     out = np.zeros((case.B, case.Hq, T, case.D))
     lse = np.full((case.B, case.Hq, T), -np.inf)
@@ -171,7 +172,7 @@ def multi_reference(case, T, qb, lens):
             continue
         m = min(n, T)
         o, l_ = oracle.attention(q[b:b + 1, :, T - m:], ai.bf16_bits_to_f64(kb)[None], ai.bf16_bits_to_f64(vb)[None],
-                                 True, case.scale)
+                                 True, case.scale, window=window)
         out[b, :, T - m:], lse[b, :, T - m:] = o[0], l_[0]
     return out, lse
 
@@ -232,3 +233,24 @@ def test_decode_multi_caller_workspace(attn):
     o2, l2 = attn.decode_multi(q, kc, vc, ld, scale=case.scale, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("T,window,idx", [(1, 64, 0), (4, 37, 0), (16, 100, 2), (7, 1, 4), (4, 4000, 5)])
+def test_decode_window(attn, T, window, idx):
+    """Sliding window over the ragged cache: keys before the earliest window
+    start are not read (the cache there could hold anything)."""
+    case = MULTI[idx][1]
+    lens = case.kv_lens()
+    qb = multi_q_bits(case, T)
+    kc, vc = decode_cache_on_device(case, lens)
+    # poison every key before the earliest window start: reading it would show as NaN
+    for b, n in enumerate(lens):
+        start = max(0, int(min(n, case.Lmax)) - T - window + 1)
+        if start > 0:
+            kc[b, :, :start] = float("nan")
+            vc[b, :, :start] = float("nan")
+    ro, rl = multi_reference(case, T, qb, lens, window=window)
+    out, lse = attn.decode_multi(to_dev(qb), kc, vc, torch.from_numpy(lens).to(DEV), scale=case.scale, window=window)
+    torch.cuda.synchronize()
+    check_out(to_np(out), ro, f"{case.name} window={window}")
+    check_lse(to_np(lse), rl, f"{case.name} window={window}")
