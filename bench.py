@@ -248,6 +248,39 @@ def all_configs(iters: int):
     del kc, vc
     torch.cuda.empty_cache()
 
+    # sliding window (4096 keys): prefill at 16K and the ragged decode; work counted on visible keys
+    W = 4096
+    pc = ai.QWEN_16K
+    q, k, v = to_dev(pc.q_bits(), dev), to_dev(pc.k_bits(), dev), to_dev(pc.v_bits(), dev)
+    out = torch.empty_like(q)
+    fn = lambda: attn.prefill_ex(q, k, v, causal=True, scale=pc.scale, window=W, out=out, return_lse=False)  # noqa: E731
+    for _ in range(2):
+        fn()
+    ms = _time_ms(fn, iters, stream)
+    i = np.arange(pc.Lq, dtype=np.int64)
+    vis = int(np.minimum(W, i + (pc.Lk - pc.Lq) + 1).sum())
+    fl = 4 * pc.B * pc.Hq * pc.D * vis
+    print(json.dumps({"config": f"qwen3_8b_prefill_L16384_window{W}", "kind": "prefill", "window": W, "ms": round(ms, 4),
+                      "flops": fl, "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
+                      "frac_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}), flush=True)
+    del q, k, v, out
+    dc = ai.RAGGED_DECODE
+    lens = dc.kv_lens()
+    kc, vc = build_decode_cache(dc, lens, dev)
+    dl = torch.from_numpy(lens).to(dev)
+    dq = to_dev(dc.q_bits(), dev)[:, :, None, :].contiguous()
+    dout = torch.empty_like(dq)
+    fn = lambda: attn.decode_multi(dq, kc, vc, dl, scale=dc.scale, window=W, out=dout, return_lse=False)  # noqa: E731
+    for _ in range(2):
+        fn()
+    ms = _time_ms(fn, iters, stream, between=lambda i: flush.fill_(i & 0xFF))
+    nb = int(np.minimum(lens, W).sum()) * dc.Hkv * dc.D * 2 * 2
+    print(json.dumps({"config": f"ragged_gqa_decode_B64_window{W}", "kind": "decode", "window": W, "ms": round(ms, 4),
+                      "kv_bytes": nb, "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
+                      "frac_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}), flush=True)
+    del kc, vc
+    torch.cuda.empty_cache()
+
     decodes = [ai.RAGGED_DECODE] + [ai.gsweep_decode(G) for G in ai.G_SWEEP]
     gen = torch.Generator(device=dev)
     for dc in decodes:
