@@ -15,7 +15,12 @@ Recipe (the same for every consumer):
     first ``kv_lens[b]`` rows only; rows past the length hold a NaN fill so
     that a kernel which reads past a sequence's end produces NaN;
   * ragged lengths are integers uniform on [lo, hi], both ends inclusive;
-  * sampled query rows are {0, Lq-1} plus distinct uniform rows.
+  * sampled query rows are {0, Lq-1} plus distinct uniform rows;
+  * int8 caches (tensor ids k=11, v=12): per sequence, codes uniform on
+    [-128, 127] and one binary16 scale per 32-element block, uniform on
+    [0.5, 1.5) * sqrt(3) / 127 (so the elements have about unit variance),
+    from one generator, codes first; positions past the length hold code 0
+    and a NaN scale.
 """
 from __future__ import annotations
 
@@ -26,8 +31,10 @@ import os
 import numpy as np
 
 BF16_NAN_BITS = np.uint16(0x7FC0)
+F16_NAN_BITS = np.uint16(0x7E00)
 
 Q_ID, K_ID, V_ID, LENS_ID, ROWS_ID = 0, 1, 2, 3, 7
+KQ_ID, VQ_ID = 11, 12
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -56,6 +63,15 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 def normal_bf16_bits(shape, seed) -> np.ndarray:
     rng = np.random.default_rng(seed)
     return f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+
+
+def q8_codes_scales(shape, seed):
+    """(codes int8 [..., D], scale bits uint16 [..., D/32]) for rows of D elements."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(-128, 127, size=shape, endpoint=True, dtype=np.int16).astype(np.int8)
+    sshape = tuple(shape[:-1]) + (shape[-1] // 32,)
+    scales = (rng.uniform(0.5, 1.5, size=sshape) * (np.sqrt(3.0) / 127.0)).astype(np.float16)
+    return codes, scales.view(np.uint16)
 
 
 @dataclass
@@ -137,6 +153,20 @@ class DecodeCase:
         with ThreadPoolExecutor(workers) as ex:
             for s0 in range(0, self.B, workers):
                 yield from ex.map(one, range(s0, min(self.B, s0 + workers)))
+
+    def q8_seq(self, tensor_id: int, b: int, n: int):
+        """int8 rows of sequence b: (codes [Hkv, n, D], scale bits [Hkv, n, D/32])."""
+        return q8_codes_scales((self.Hkv, n, self.D), [self.wid, tensor_id, self.variant, b])
+
+    def iter_q8_seqs(self, lens: np.ndarray | None = None):
+        """Yield (b, n, (k codes, k scales), (v codes, v scales)) in order of b."""
+        lens = self.kv_lens() if lens is None else lens
+        for b in range(self.B):
+            n = int(min(max(int(lens[b]), 0), self.Lmax))
+            if n == 0:
+                yield b, 0, None, None
+            else:
+                yield b, n, self.q8_seq(KQ_ID, b, n), self.q8_seq(VQ_ID, b, n)
 
     def cache_bits(self, tensor_id: int, lens: np.ndarray | None = None) -> np.ndarray:
         """Full [B, Hkv, Lmax, D] cache; rows past each length are NaN."""

@@ -16,6 +16,9 @@ Pages cited (by title):
   [nvidia-long]  "Как NVIDIA учит нейросети думать быстрее: оптимизация
                  внимания для длинных контекстов" (iphoneandroid24.ru)
   [gqa-glossary] "grouped-query attention 그룹 쿼리 어텐션" (0to1log.com)
+  [slack]        "Attention Slack (어텐션 슬랙): KV 캐시 크기가 추론 능력을
+                 결정한다" (kiban.pages.dev; llama.cpp runs with q8_0 K/V
+                 caches)
 
 Pinned by tests/test_oracle.py (page example, closed forms, invariants,
 brute force).  Every function here is pinned; none is "parity unpinned".
@@ -23,7 +26,8 @@ brute force).  Every function here is pinned; none is "parity unpinned".
 from .reference import (visible_mask, kv_head_of, attention, attention_rows, decode, combine_partials,
                         attention_probs)
 from .brute import brute_attention
+from .quant import dequantize_q8, round_to_bf16, half_bits_to_f64
 from . import accounting
 
 __all__ = ["visible_mask", "kv_head_of", "attention", "attention_rows", "decode", "combine_partials",
-           "attention_probs", "brute_attention", "accounting"]
+           "attention_probs", "brute_attention", "dequantize_q8", "round_to_bf16", "half_bits_to_f64", "accounting"]

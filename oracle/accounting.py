@@ -66,6 +66,13 @@ def decode_kv_bytes(kv_lens, Hkv: int, D: int, Lmax: int, elem_bytes: int = 2) -
     return int(n.sum()) * Hkv * D * 2 * elem_bytes
 
 
+def decode_q8_kv_bytes(kv_lens, Hkv: int, D: int, Lmax: int) -> int:
+    """int8 caches: per visible key and KV head, D one-byte codes and D / 32
+    two-byte scales, for K and for V."""
+    n = np.minimum(np.maximum(np.asarray(kv_lens, dtype=np.int64), 0), Lmax)
+    return int(n.sum()) * Hkv * 2 * (D + 2 * (D // 32))
+
+
 def decode_flops(kv_lens, Hq: int, D: int, Lmax: int) -> int:
     n = np.minimum(np.maximum(np.asarray(kv_lens, dtype=np.int64), 0), Lmax)
     return 4 * Hq * D * int(n.sum())
