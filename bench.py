@@ -305,8 +305,44 @@ def all_configs(iters: int):
                           "Lmax": dc.Lmax, "D": dc.D, "sum_lens": int(lens.sum()), "ms": round(ms, 4),
                           "kv_bytes": nb, "GB/s": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
                           "waves": attn.decode_waves(dc.B, dc.Hq, dc.Hkv, dc.Lmax, dc.D)}), flush=True)
+        if dc is ai.RAGGED_DECODE:
+            bf16_ms = ms
         del kc, vc
         torch.cuda.empty_cache()
+
+    # int8 (q8_0-style) caches on the ragged workload: codes uniform on
+    # [-128, 127], block scales uniform on [0.5, 1.5) * sqrt(3) / 127
+    dc = ai.RAGGED_DECODE
+    lens = dc.kv_lens()
+    shape = (dc.B, dc.Hkv, dc.Lmax, dc.D)
+    sshape = (dc.B, dc.Hkv, dc.Lmax, dc.D // 32)
+    gen.manual_seed(dc.wid * 1000 + 8)
+    kq = torch.randint(-128, 128, shape, generator=gen, device=dev, dtype=torch.int8)
+    vq = torch.randint(-128, 128, shape, generator=gen, device=dev, dtype=torch.int8)
+    ks = ((torch.rand(sshape, generator=gen, device=dev) + 0.5) * (3 ** 0.5 / 127)).to(torch.float16)
+    vs = ((torch.rand(sshape, generator=gen, device=dev) + 0.5) * (3 ** 0.5 / 127)).to(torch.float16)
+    dl = torch.from_numpy(lens).to(dev)
+    for T in (1, 4):
+        dq = torch.randn((dc.B, dc.Hq, T, dc.D), generator=gen, device=dev).to(torch.bfloat16)
+        dout = torch.empty_like(dq)
+        ws = torch.empty(attn.decode_multi_workspace_bytes(dc.B, dc.Hq, dc.Hkv, T, dc.Lmax, dc.D),
+                         dtype=torch.uint8, device=dev)
+        fn = lambda: attn.decode_q8(dq, kq, ks, vq, vs, dl, scale=dc.scale, out=dout, return_lse=False,  # noqa: E731
+                                    workspace=ws)
+        for _ in range(2):
+            fn()
+        ms = _time_ms(fn, iters, stream, between=lambda i: flush.fill_(i & 0xFF))
+        nb = acc.decode_q8_kv_bytes(lens, dc.Hkv, dc.D, dc.Lmax)
+        gbps = nb / (ms * 1e-3) / 1e9
+        rec = {"config": f"q8_{dc.name}_T{T}", "kind": "decode_q8", "B": dc.B, "Hq": dc.Hq, "Hkv": dc.Hkv,
+               "T": T, "Lmax": dc.Lmax, "D": dc.D, "sum_lens": int(lens.sum()), "ms": round(ms, 4),
+               "kv_bytes": nb, "GB/s": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+        if T == 1:
+            rec["bf16_cache_ms"] = round(bf16_ms, 4)
+            rec["speedup_vs_bf16_cache"] = round(bf16_ms / ms, 3)
+        print(json.dumps(rec), flush=True)
+    del kq, vq, ks, vs
+    torch.cuda.empty_cache()
 
 
 def main():
@@ -406,7 +442,7 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": ptraffic},
         "decode": {"value": round(gbps, 1), "unit": "GB/s",
-                   "roofline": {"bound": "hbm", "kernel": "decode_plan_kernel + decode_main_kernel<128,1> + decode_combine_kernel<128>",
+                   "roofline": {"bound": "hbm", "kernel": "decode_plan_kernel + decode_main_kernel<128,1,false> + decode_combine_kernel<128>",
                                 "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                 "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": dtraffic}},
         "kernel_source_hash": src,

@@ -43,6 +43,8 @@ def _load(path: str = LIB_PATH):
     lib.attn_decode_ex.restype = i
     lib.attn_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
     lib.attn_decode_multi.restype = i
+    lib.attn_decode_q8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
+    lib.attn_decode_q8.restype = i
     lib.attn_decode_multi_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.attn_decode_multi_workspace_bytes.restype = sz
     lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
@@ -200,6 +202,34 @@ def decode_multi(q, kcache, vcache, kv_lens, scale: float | None = None, out=Non
     return out, lse
 
 
+def decode_q8(q, kq, kscale, vq, vscale, kv_lens, scale: float | None = None, out=None, return_lse: bool = True,
+              workspace=None, window: int = 0):
+    """attn_decode_q8: decode_multi over int8 caches kq/vq [B,Hkv,Lmax,D] with fp16 block scales
+    kscale/vscale [B,Hkv,Lmax,D/32] (element = scale of its 32-element block * code)."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(kq, "kq", torch.int8, 4)
+    _need(vq, "vq", torch.int8, 4)
+    _need(kscale, "kscale", torch.float16, 4)
+    _need(vscale, "vscale", torch.float16, 4)
+    _need(kv_lens, "kv_lens", torch.int32, 1)
+    B, Hq, T, D = q.shape
+    Hkv, Lmax = kq.shape[1], kq.shape[2]
+    if (vq.shape != kq.shape or kq.shape[0] != B or kq.shape[3] != D or kv_lens.shape[0] != B
+            or D % 32 != 0 or kscale.shape != (B, Hkv, Lmax, D // 32) or vscale.shape != kscale.shape):
+        raise ValueError("shape mismatch between q, int8 caches, scales and kv_lens")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.bfloat16, 4)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device) if return_lse else None
+    scale = default_scale(D) if scale is None else float(scale)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.attn_decode_q8(_ptr(q), _ptr(kq), _ptr(kscale), _ptr(vq), _ptr(vscale), _ptr(kv_lens), _ptr(out),
+                              _ptr(lse), B, Hq, Hkv, T, int(window), Lmax, D, ctypes.c_float(scale),
+                              _ptr(workspace), ws_bytes, _stream(q.device)))
+    return out, lse
+
+
 def decode_multi_workspace_bytes(B, Hq, Hkv, T, Lmax, D) -> int:
     return int(lib.attn_decode_multi_workspace_bytes(B, Hq, Hkv, T, Lmax, D))
 
@@ -224,5 +254,5 @@ def _decode_shapes(q, kcache, vcache, kv_lens):
     return B, Hq, Hkv, Lmax, D
 
 
-__all__ = ["prefill", "prefill_ex", "prefill_splits", "prefill_workspace_bytes", "decode", "decode_ex", "decode_multi", "decode_multi_workspace_bytes", "decode_workspace_bytes", "decode_waves", "AttnError", "lib",
+__all__ = ["prefill", "prefill_ex", "prefill_splits", "prefill_workspace_bytes", "decode", "decode_ex", "decode_multi", "decode_q8", "decode_multi_workspace_bytes", "decode_workspace_bytes", "decode_waves", "AttnError", "lib",
            "LIB_PATH", "default_scale"]

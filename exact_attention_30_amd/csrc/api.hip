@@ -69,9 +69,9 @@ void decode_workspace(int B, int Hq, int Hkv, int T, int D, DecodeShape *ds) {
 // with split_keys, enough waves that no wave gets more than split_keys keys
 // when every sequence has Lmax keys (capped at kDecodeMaxWaves).
 std::mutex g_occ_mu;
-int g_occ_cache[64][3][3];
+int g_occ_cache[64][3][3][2];
 
-int device_waves(int D, int GT, int *waves) {
+int device_waves(int D, int GT, bool q8, int *waves) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return ATTN_ERR_HIP;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return ATTN_ERR_HIP;
@@ -79,16 +79,16 @@ int device_waves(int D, int GT, int *waves) {
   const int ci = (gw + 15) / 16 >= 3 ? 2 : (gw + 15) / 16 - 1;
   const int di = D == 64 ? 0 : (D == 128 ? 1 : 2);
   std::lock_guard<std::mutex> lk(g_occ_mu);
-  int &occ = g_occ_cache[dev][di][ci];
-  if (occ == 0 && attn::decode_waves_per_cu(D, gw, &occ) != hipSuccess) return ATTN_ERR_HIP;
+  int &occ = g_occ_cache[dev][di][ci][q8 ? 1 : 0];
+  if (occ == 0 && attn::decode_waves_per_cu(D, gw, q8, &occ) != hipSuccess) return ATTN_ERR_HIP;
   const long long w = (long long)cus * (occ > 0 ? occ : 1);
   *waves = (int)(w < attn::kDecodeMaxWaves ? w : attn::kDecodeMaxWaves);
   return ATTN_OK;
 }
 
-int decode_waves(int B, int Hq, int Hkv, int T, int Lmax, int D, int split_keys, int *waves) {
+int decode_waves(int B, int Hq, int Hkv, int T, int Lmax, int D, int split_keys, bool q8, int *waves) {
   const int GT = (Hq / Hkv) * T;
-  if (split_keys == 0) return device_waves(D, GT, waves);
+  if (split_keys == 0) return device_waves(D, GT, q8, waves);
   const double keys = (double)B * Hkv * ((GT + attn::kDecodeGroup - 1) / attn::kDecodeGroup) *
                       (double)((Lmax + 31) / 32) * 32.0;
   double w = keys / split_keys;
@@ -113,18 +113,22 @@ int decode_check(const void *q, const void *kc, const void *vc, const int32_t *l
   return ATTN_OK;
 }
 
+// kscale / vscale: per-block fp16 scales of int8 caches (both null for bf16
+// caches; q8 says which the caller meant, so a missing scale is an error).
 int run_decode(const void *q, const void *kc, const void *vc, const int32_t *lens, void *out, float *lse, int B,
                int Hq, int Hkv, int T, int window, int Lmax, int D, float scale, int split_keys, void *ws,
-               size_t ws_bytes, void *stream) {
+               size_t ws_bytes, void *stream, bool q8 = false, const void *kscale = nullptr,
+               const void *vscale = nullptr) {
   int st = decode_check(q, kc, vc, lens, out, B, Hq, Hkv, T, Lmax, D, scale);
   if (st != ATTN_OK) return st;
+  if (q8 && B > 0 && (kscale == nullptr || vscale == nullptr)) return ATTN_ERR_NULL;
   if (window < 0) return ATTN_ERR_SHAPE;
   if (split_keys != 0 && (split_keys < 0 || split_keys % 128 != 0)) return ATTN_ERR_SPLIT;
   DecodeShape ds;
   decode_workspace(B, Hq, Hkv, T, D, &ds);
   if (ws != nullptr && ws_bytes < ds.total) return ATTN_ERR_WORKSPACE;
   if (B == 0) return ATTN_OK;
-  st = decode_waves(B, Hq, Hkv, T, Lmax, D, split_keys, &ds.waves);
+  st = decode_waves(B, Hq, Hkv, T, Lmax, D, split_keys, q8, &ds.waves);
   if (st != ATTN_OK) return st;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -144,6 +148,8 @@ int run_decode(const void *q, const void *kc, const void *vc, const int32_t *len
   a.lens = lens;
   a.out = static_cast<uint16_t *>(out);
   a.lse = lse;
+  a.kscale = q8 ? static_cast<const uint16_t *>(kscale) : nullptr;
+  a.vscale = q8 ? static_cast<const uint16_t *>(vscale) : nullptr;
   a.pre = reinterpret_cast<long long *>(base);
   a.part_lse = reinterpret_cast<float *>(base + ds.pre_bytes);
   a.part_o = reinterpret_cast<float *>(base + ds.pre_bytes + ds.part_lse_bytes);
@@ -325,6 +331,13 @@ int attn_decode_multi(const void *q, const void *kcache, const void *vcache, con
                     workspace_bytes, stream);
 }
 
+int attn_decode_q8(const void *q, const void *kq, const void *kscale, const void *vq, const void *vscale,
+                   const int32_t *kv_lens, void *out, float *lse, int B, int Hq, int Hkv, int T, int window, int Lmax,
+                   int D, float scale, void *workspace, size_t workspace_bytes, void *stream) {
+  return run_decode(q, kq, vq, kv_lens, out, lse, B, Hq, Hkv, T, window, Lmax, D, scale, 0, workspace,
+                    workspace_bytes, stream, true, kscale, vscale);
+}
+
 size_t attn_decode_multi_workspace_bytes(int B, int Hq, int Hkv, int T, int Lmax, int D) {
   if (B <= 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || !head_dim_ok(D) || Lmax < 1 || T < 1 || T > Lmax) return 0;
   DecodeShape ds;
@@ -344,7 +357,7 @@ int attn_decode_waves(int B, int Hq, int Hkv, int Lmax, int D, int split_keys) {
   if (B <= 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || !head_dim_ok(D) || Lmax < 1) return 0;
   if (split_keys != 0 && (split_keys < 0 || split_keys % 128 != 0)) return 0;
   int w = 0;
-  return decode_waves(B, Hq, Hkv, 1, Lmax, D, split_keys, &w) == ATTN_OK ? w : 0;
+  return decode_waves(B, Hq, Hkv, 1, Lmax, D, split_keys, false, &w) == ATTN_OK ? w : 0;
 }
 
 const char *attn_status_string(int status) {

@@ -107,7 +107,43 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a) {
 
 // One query-column block: two waves per SIMD (256 registers each); more
 // column blocks need the whole register file.
-template <int D, int NCB>
+// int8 -> bf16 for 8 codes (two dwords) of one 32-element block with scale s:
+// the codes are biased to unsigned bytes (xor 0x80), converted exactly, and
+// x = s * (u - 128) is rounded to bf16 (nearest even).
+ATTN_DEV u32x4 dequant8(uint32_t lo, uint32_t hi, float s) {
+  const uint32_t a = lo ^ 0x80808080u, b = hi ^ 0x80808080u;
+  const float o = -128.f * s;
+  const bf16x8 r = pack8(__builtin_fmaf((float)(a & 0xffu), s, o), __builtin_fmaf((float)((a >> 8) & 0xffu), s, o),
+                         __builtin_fmaf((float)((a >> 16) & 0xffu), s, o), __builtin_fmaf((float)(a >> 24), s, o),
+                         __builtin_fmaf((float)(b & 0xffu), s, o), __builtin_fmaf((float)((b >> 8) & 0xffu), s, o),
+                         __builtin_fmaf((float)((b >> 16) & 0xffu), s, o), __builtin_fmaf((float)(b >> 24), s, o));
+  return __builtin_bit_cast(u32x4, r);
+}
+ATTN_DEV float half_bits_to_float(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+// Registers of one 32-key block in flight: bf16 K operands and V rows, or
+// (Q8) the int8 codes and scales they are dequantized from.
+template <int D, bool Q8>
+struct DecodeRaw;
+template <int D>
+struct DecodeRaw<D, false> {
+  static constexpr int KST = D / 32, VU = (D / 2 + 63) / 64;
+  u32x4 kr[2 * KST];
+  u32x4 vr[VU][8];
+};
+template <int D>
+struct DecodeRaw<D, true> {
+  // K: piece i of a lane in group g holds the 16 codes of dims 64 i + 16 g ...,
+  // all inside one 32-element block (2 i + g / 2), so one scale per piece
+  static constexpr int KQ = D / 64;
+  static constexpr int VU = (D / 2 + 63) / 64;
+  u32x4 kq[2][KQ];
+  uint16_t ksc[2][KQ];
+  u32x2 vq[VU][8];
+  uint16_t vsc[VU][8];
+};
+
+template <int D, int NCB, bool Q8>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2 : 1))) void decode_main_kernel(DecodeArgs a) {
   constexpr int KST = D / 32;            // 32-dim MFMA steps over the head dim
   constexpr int NKR = 2 * KST;           // K registers (16 B each) per 32-key block
@@ -181,7 +217,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
       const uint16_t *qp = a.q + (((size_t)b * a.Hq + hkv * a.G) * a.T + gq0 + min(qi, gcnt - 1)) * D;
 #pragma unroll
       for (int ks = 0; ks < KST; ++ks)
-        qf[cb][ks] = as_bf16x8(qi < gcnt ? ld16(qp + (ATTN_DEC_KNAT ? 32 * ks + 8 * g : (D / 4) * g + 8 * ks)) : zero4);
+        qf[cb][ks] = as_bf16x8(qi < gcnt ? ld16(qp + (Q8              ? 64 * (ks >> 1) + 16 * g + 8 * (ks & 1)
+                                                      : ATTN_DEC_KNAT ? 32 * ks + 8 * g
+                                                                      : (D / 4) * g + 8 * ks))
+                                         : zero4);
     }
     const size_t base = ((size_t)b * a.Hkv + hkv) * (size_t)a.Lmax * D;
     const uint16_t *kg = a.kc + base;
@@ -197,7 +236,48 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
       for (int db = 0; db < D / 16; ++db) o[cb][db] = f32x4{};
     }
 
-    auto load = [&](u32x4(&kr)[NKR], u32x4(&vr)[VU][8], int kb) {
+    using Raw = DecodeRaw<D, Q8>;
+    const int8_t *kq8 = reinterpret_cast<const int8_t *>(a.kc) + base;
+    const int8_t *vq8 = reinterpret_cast<const int8_t *>(a.vc) + base;
+    const uint16_t *ksg = Q8 ? a.kscale + base / 32 : nullptr;
+    const uint16_t *vsg = Q8 ? a.vscale + base / 32 : nullptr;
+    const uint32_t zero2 = 0u;
+    auto load = [&](Raw &raw, int kb) {
+      if constexpr (Q8) {
+        // K: 16 codes of dims 64 i + 16 g ... per piece (each instruction reads
+        // 64 contiguous bytes of a row), and the scale of their block
+  #pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const int key = kb + 16 * rb + ql;
+          const bool in = key < k1 && key >= kmin;
+          const int8_t *p = kq8 + (size_t)key * D + 16 * g;
+          const uint16_t *ps = ksg + (size_t)key * (D / 32) + (g >> 1);
+  #pragma unroll
+          for (int i = 0; i < Raw::KQ; ++i) {
+            raw.kq[rb][i] = in ? ld16_stream(p + 64 * i) : zero4;
+            raw.ksc[rb][i] = in ? ps[2 * i] : (uint16_t)0;
+          }
+        }
+        // V: 8 codes (one 8-dim chunk) of 8 keys per unit, and the scale of each
+  #pragma unroll
+        for (int iu = 0; iu < VU; ++iu) {
+          const int u = lane + 64 * iu;
+          if (VUN % 64 == 0 || u < VUN) {
+            const int c = u % (D / 8), gg = u / (D / 8);
+  #pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+              const int key = kb + (kk < 4 ? 4 * gg + kk : 16 + 4 * gg + kk - 4);
+              const bool in = key < k1 && key >= kmin;
+              const u32x2 *pv = reinterpret_cast<const u32x2 *>(vq8 + (size_t)key * D + 8 * c);
+              raw.vq[iu][kk] = in ? __builtin_nontemporal_load(pv) : u32x2{zero2, zero2};
+              raw.vsc[iu][kk] = in ? vsg[(size_t)key * (D / 32) + c / 4] : (uint16_t)0;
+            }
+          }
+        }
+        return;
+      } else {
+      u32x4(&kr)[NKR] = raw.kr;
+      u32x4(&vr)[VU][8] = raw.vr;
   #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         const int key = kb + 16 * rb + ql;
@@ -221,9 +301,35 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
           }
         }
       }
+      }
     };
 
-    auto compute = [&](const u32x4(&kr)[NKR], const u32x4(&vr)[VU][8], int kb) {
+    auto compute = [&](const Raw &raw, int kb) {
+      u32x4 kr[NKR];
+      u32x4 vr[VU][8];
+      if constexpr (Q8) {
+  #pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+  #pragma unroll
+          for (int ks = 0; ks < KST; ++ks) {
+            // chunk ks = dims 64 (ks / 2) + 16 g + 8 (ks % 2): half of piece ks / 2
+            const int i = ks >> 1, h = ks & 1;
+            kr[rb * KST + ks] =
+                dequant8(raw.kq[rb][i][2 * h], raw.kq[rb][i][2 * h + 1], half_bits_to_float(raw.ksc[rb][i]));
+          }
+  #pragma unroll
+        for (int iu = 0; iu < VU; ++iu)
+  #pragma unroll
+          for (int kk = 0; kk < 8; ++kk)
+            vr[iu][kk] = dequant8(raw.vq[iu][kk][0], raw.vq[iu][kk][1], half_bits_to_float(raw.vsc[iu][kk]));
+      } else {
+  #pragma unroll
+        for (int i = 0; i < NKR; ++i) kr[i] = raw.kr[i];
+  #pragma unroll
+        for (int iu = 0; iu < VU; ++iu)
+  #pragma unroll
+          for (int kk = 0; kk < 8; ++kk) vr[iu][kk] = raw.vr[iu][kk];
+      }
       // V block -> V^T in LDS, keys in the order the P^T operand holds them
   #pragma unroll
       for (int iu = 0; iu < VU; ++iu) {
@@ -329,23 +435,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
     const int nblk = (k1 - k0 + 31) / 32;
     if constexpr (D <= 128) {
       // two register sets: block i+1 is in flight while block i is computed
-      u32x4 kA[NKR], kB[NKR];
-      u32x4 vA[VU][8], vB[VU][8];
-      load(kA, vA, k0);
+      Raw rA, rB;
+      load(rA, k0);
       for (int bi = 0; bi < nblk; bi += 2) {
-        if (bi + 1 < nblk) load(kB, vB, k0 + 32 * (bi + 1));
-        compute(kA, vA, k0 + 32 * bi);
+        if (bi + 1 < nblk) load(rB, k0 + 32 * (bi + 1));
+        compute(rA, k0 + 32 * bi);
         if (bi + 1 >= nblk) break;
-        if (bi + 2 < nblk) load(kA, vA, k0 + 32 * (bi + 2));
-        compute(kB, vB, k0 + 32 * (bi + 1));
+        if (bi + 2 < nblk) load(rA, k0 + 32 * (bi + 2));
+        compute(rB, k0 + 32 * (bi + 1));
       }
     } else {
       // D = 256: one register set (a second would not fit next to the accumulators)
-      u32x4 kA[NKR];
-      u32x4 vA[VU][8];
+      Raw rA;
       for (int bi = 0; bi < nblk; ++bi) {
-        load(kA, vA, k0 + 32 * bi);
-        compute(kA, vA, k0 + 32 * bi);
+        load(rA, k0 + 32 * bi);
+        compute(rA, k0 + 32 * bi);
       }
     }
 
@@ -469,7 +573,8 @@ static hipError_t launch_t(const DecodeArgs &a, int W, hipStream_t s) {
   hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_main_kernel<D, NCB>), dim3(W), dim3(64), 0, s, a);
+  if (a.kscale != nullptr) hipLaunchKernelGGL((decode_main_kernel<D, NCB, true>), dim3(W), dim3(64), 0, s, a);
+  else hipLaunchKernelGGL((decode_main_kernel<D, NCB, false>), dim3(W), dim3(64), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.Hq * a.T), dim3(64), 0, s, a, W);
@@ -496,12 +601,14 @@ hipError_t launch_decode(const DecodeArgs &a, int D, int W, hipStream_t s) {
 }
 
 // Resident 64-thread workgroups of the main kernel per CU for GW query rows
-// per wave group.
-hipError_t decode_waves_per_cu(int D, int GW, int *out) {
+// per wave group (q8: the int8-cache kernel).
+hipError_t decode_waves_per_cu(int D, int GW, bool q8, int *out) {
   const int gw = GW < kDecodeGroup ? GW : kDecodeGroup;
   const int ncb = (gw + 15) / 16;
   const void *f = nullptr;
-#define ATTN_PICK(DD, NN) f = reinterpret_cast<const void *>(&decode_main_kernel<DD, NN>)
+#define ATTN_PICK(DD, NN)                                                                \
+  f = q8 ? reinterpret_cast<const void *>(&decode_main_kernel<DD, NN, true>)           \
+         : reinterpret_cast<const void *>(&decode_main_kernel<DD, NN, false>)
   if (D == 64) { if (ncb == 1) ATTN_PICK(64, 1); else if (ncb == 2) ATTN_PICK(64, 2); else ATTN_PICK(64, 4); }
   else if (D == 128) { if (ncb == 1) ATTN_PICK(128, 1); else if (ncb == 2) ATTN_PICK(128, 2); else ATTN_PICK(128, 4); }
   else { if (ncb == 1) ATTN_PICK(256, 1); else if (ncb == 2) ATTN_PICK(256, 2); else ATTN_PICK(256, 4); }

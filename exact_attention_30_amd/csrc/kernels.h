@@ -36,6 +36,10 @@ struct DecodeArgs {
   const int32_t *lens;
   uint16_t *out;
   float *lse;
+  // int8 caches (kc / vc then hold int8 codes): fp16 scale per 32-element
+  // block of each row, [B][Hkv][Lmax][D / 32]; null for bf16 caches
+  const uint16_t *kscale;
+  const uint16_t *vscale;
   long long *pre;   // [B + 1] prefix sums of 32-key blocks per sequence (planner output)
   float *part_o;    // [slots][GW][D] normalised piece outputs, slots = waves + B * Hkv * n_hg
   float *part_lse;  // [slots][GW] piece log-sum-exps
@@ -68,6 +72,6 @@ int prefill_tile_keys(int D);
 constexpr int kPrefillMaxSplits = 64;
 hipError_t launch_prefill(const PrefillArgs &a, int D, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int D, int waves, hipStream_t s);
-hipError_t decode_waves_per_cu(int D, int GW, int *out);
+hipError_t decode_waves_per_cu(int D, int GW, bool q8, int *out);
 
 }  // namespace attn

@@ -226,6 +226,33 @@ int attn_decode_multi(const void *q, const void *kcache, const void *vcache, con
                       float scale, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * attn_decode_q8 -- attn_decode_multi over int8 (q8_0-style) K and V caches.
+ *
+ * Pages: the Attention Slack page (Gemma-4 26B) runs llama.cpp's flash
+ * attention with both caches stored as q8_0 (its llama-server service
+ * configuration); the pages do not define the format.  The format read here:
+ * every row of D elements is cut into D / 32 blocks of 32 consecutive
+ * elements; block j of a row holds one fp16 scale s_j and 32 int8 codes c_i,
+ * and element i of the block is x = s_j * c_i (computed in fp32 and rounded
+ * to bf16, nearest even, before it enters the products; scores, softmax
+ * statistics and accumulators are fp32 as in attn_decode).
+ *
+ *   q, out          [B][Hq][T][D] bf16       lse [B][Hq][T] fp32, may be NULL
+ *   kq, vq          [B][Hkv][Lmax][D] int8   (codes -128..127; -128 is legal)
+ *   kscale, vscale  [B][Hkv][Lmax][D / 32] fp16 (IEEE binary16 bits)
+ *   kv_lens         [B] int32 (device)
+ *
+ * Everything else -- T, window, the causal limits, empty sequences, lengths
+ * above Lmax, workspace and its size (attn_decode_multi_workspace_bytes with
+ * the same sizes) and the status codes -- is as attn_decode_multi.  Codes and
+ * scales of positions at or past a sequence's length (or before its window)
+ * are never read.  A NULL kscale or vscale with B > 0 is ATTN_ERR_NULL.
+ */
+int attn_decode_q8(const void *q, const void *kq, const void *kscale, const void *vq, const void *vscale,
+                   const int32_t *kv_lens, void *out, float *lse, int B, int Hq, int Hkv, int T, int window,
+                   int Lmax, int D, float scale, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * attn_decode_multi_workspace_bytes -- bytes of workspace attn_decode_multi
  * needs for these sizes; 0 for an empty call and for invalid arguments.
  */

@@ -183,3 +183,18 @@ def test_decode_multi_validation_and_sizes(attn):
     assert attn.decode_multi_workspace_bytes(2, 8, 2, 0, 64, 128) == 0
     need = attn.decode_multi_workspace_bytes(2, 8, 2, 4, 64, 128)
     assert multi(ws=P, ws_bytes=need - 1) == -8
+
+
+def test_decode_q8_validation(attn):
+    def q8(T=1, B=2, Hq=8, Hkv=2, Lmax=64, D=128, q=P, ks=P, vs=P, window=0, ws=N, ws_bytes=0):
+        return attn.lib.attn_decode_q8(q, P, ks, P, vs, P, P, N, B, Hq, Hkv, T, window, Lmax, D, ctypes.c_float(0.1),
+                                       ws, ws_bytes, None)
+    assert q8(ks=N) == -1               # a missing scale array
+    assert q8(vs=N) == -1
+    assert q8(B=0, q=N, ks=N, vs=N) == 0
+    assert q8(T=0) == -2
+    assert q8(window=-1) == -2
+    assert q8(Hq=7) == -4
+    assert q8(D=96) == -3
+    need = attn.decode_multi_workspace_bytes(2, 8, 2, 1, 64, 128)
+    assert q8(ws=P, ws_bytes=need - 1) == -8
