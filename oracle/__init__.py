@@ -27,7 +27,9 @@ from .reference import (visible_mask, kv_head_of, attention, attention_rows, dec
                         attention_probs)
 from .brute import brute_attention
 from .quant import dequantize_q8, round_to_bf16, half_bits_to_f64
+from .backward import attention_backward, attention_backward_sampled, delta_rows
 from . import accounting
 
 __all__ = ["visible_mask", "kv_head_of", "attention", "attention_rows", "decode", "combine_partials",
-           "attention_probs", "brute_attention", "dequantize_q8", "round_to_bf16", "half_bits_to_f64", "accounting"]
+           "attention_probs", "brute_attention", "dequantize_q8", "round_to_bf16", "half_bits_to_f64",
+           "attention_backward", "attention_backward_sampled", "delta_rows", "accounting"]
