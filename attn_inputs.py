@@ -8,7 +8,8 @@ sequence lengths and sampled query rows.
 Recipe (the same for every consumer):
   * every tensor is drawn as float32 ``standard_normal`` from
     ``numpy.random.default_rng([workload_id, tensor_id, variant, ...])`` with
-    tensor_id q=0, k=1, v=2, lens=3, rows=7, and rounded to bfloat16 with
+    tensor_id q=0, k=1, v=2, lens=3, rows=7, dout=8 (the upstream gradient
+    of the backward pass), and rounded to bfloat16 with
     round-to-nearest-even; the bf16 bit patterns (uint16) are what both the
     oracle (widened to float64) and the GPU (as torch.bfloat16) consume;
   * decode caches are drawn per sequence (seed ``[id, t, variant, b]``) for the
@@ -33,7 +34,7 @@ import numpy as np
 BF16_NAN_BITS = np.uint16(0x7FC0)
 F16_NAN_BITS = np.uint16(0x7E00)
 
-Q_ID, K_ID, V_ID, LENS_ID, ROWS_ID = 0, 1, 2, 3, 7
+Q_ID, K_ID, V_ID, LENS_ID, ROWS_ID, DOUT_ID = 0, 1, 2, 3, 7, 8
 KQ_ID, VQ_ID = 11, 12
 
 
@@ -100,6 +101,9 @@ class PrefillCase:
 
     def v_bits(self) -> np.ndarray:
         return normal_bf16_bits((self.B, self.Hkv, self.Lk, self.D), [self.wid, V_ID, self.variant])
+
+    def dout_bits(self) -> np.ndarray:
+        return normal_bf16_bits((self.B, self.Hq, self.Lq, self.D), [self.wid, DOUT_ID, self.variant])
 
 
 @dataclass

@@ -43,6 +43,10 @@ def _load(path: str = LIB_PATH):
     lib.attn_decode_ex.restype = i
     lib.attn_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
     lib.attn_decode_multi.restype = i
+    lib.attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp, sz, vp]
+    lib.attn_backward.restype = i
+    lib.attn_backward_workspace_bytes.argtypes = [i, i, i]
+    lib.attn_backward_workspace_bytes.restype = sz
     lib.attn_decode_q8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
     lib.attn_decode_q8.restype = i
     lib.attn_decode_multi_workspace_bytes.argtypes = [i, i, i, i, i, i]
@@ -230,6 +234,39 @@ def decode_q8(q, kq, kscale, vq, vscale, kv_lens, scale: float | None = None, ou
     return out, lse
 
 
+def backward(q, k, v, out, dout, lse, causal: bool = True, scale: float | None = None, window: int = 0,
+             dq=None, dk=None, dv=None, workspace=None):
+    """attn_backward: (dq, dk, dv) of attention from the forward's out and lse and the gradient dout."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    _need(out, "out", torch.bfloat16, 4)
+    _need(dout, "dout", torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    if (v.shape != k.shape or k.shape[0] != B or k.shape[3] != D or out.shape != q.shape or dout.shape != q.shape
+            or lse.shape != (B, Hq, Lq)):
+        raise ValueError("shape mismatch between q, k, v, out, dout and lse")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, n, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        _need(t, n, torch.bfloat16, 4)
+        if t.shape != ref.shape:
+            raise ValueError(f"{n} must have the shape of its input")
+    scale = default_scale(D) if scale is None else float(scale)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.attn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                             _ptr(dv), B, Hq, Hkv, Lq, Lk, D, int(bool(causal)), int(window), ctypes.c_float(scale),
+                             _ptr(workspace), ws_bytes, _stream(q.device)))
+    return dq, dk, dv
+
+
+def backward_workspace_bytes(B, Hq, Lq) -> int:
+    return int(lib.attn_backward_workspace_bytes(B, Hq, Lq))
+
+
 def decode_multi_workspace_bytes(B, Hq, Hkv, T, Lmax, D) -> int:
     return int(lib.attn_decode_multi_workspace_bytes(B, Hq, Hkv, T, Lmax, D))
 
@@ -254,5 +291,5 @@ def _decode_shapes(q, kcache, vcache, kv_lens):
     return B, Hq, Hkv, Lmax, D
 
 
-__all__ = ["prefill", "prefill_ex", "prefill_splits", "prefill_workspace_bytes", "decode", "decode_ex", "decode_multi", "decode_q8", "decode_multi_workspace_bytes", "decode_workspace_bytes", "decode_waves", "AttnError", "lib",
+__all__ = ["prefill", "prefill_ex", "prefill_splits", "prefill_workspace_bytes", "decode", "decode_ex", "decode_multi", "decode_q8", "backward", "backward_workspace_bytes", "decode_multi_workspace_bytes", "decode_workspace_bytes", "decode_waves", "AttnError", "lib",
            "LIB_PATH", "default_scale"]

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn.so")
-SOURCES = ["prefill.hip", "decode.hip", "api.hip"]
+SOURCES = ["prefill.hip", "decode.hip", "backward.hip", "api.hip"]
 # Per-source flags.  The prefill kernel never sees NaN scores from finite
 # inputs (masked scores are infinities, which stay honoured), so its max/min
 # reductions need not quiet signalling NaNs first.

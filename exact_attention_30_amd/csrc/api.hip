@@ -8,6 +8,7 @@
 
 using attn::DecodeArgs;
 using attn::PrefillArgs;
+using attn::BackwardArgs;
 
 namespace {
 
@@ -309,6 +310,67 @@ size_t attn_prefill_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int 
   PrefillArgs a;
   if (prefill_setup(&a, B, Hq, Hkv, Lq, Lk, D, causal, window, 1.f, splits) != ATTN_OK) return 0;
   return prefill_workspace(a, D);
+}
+
+size_t attn_backward_workspace_bytes(int B, int Hq, int Lq) {
+  if (B <= 0 || Hq < 1 || Lq <= 0) return 0;
+  return 2 * align256((size_t)B * Hq * Lq * sizeof(float));
+}
+
+int attn_backward(const void *q, const void *k, const void *v, const void *out, const void *dout, const float *lse,
+                  void *dq, void *dk, void *dv, int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, int window,
+                  float scale, void *workspace, size_t workspace_bytes, void *stream) {
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_GQA;
+  if (D != 64 && D != 128) return ATTN_ERR_HEADDIM;
+  if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  if (B < 0 || Lq < 0 || Lk < 0 || window < 0 || (window > 0 && !causal)) return ATTN_ERR_SHAPE;
+  if (B == 0 || (Lq == 0 && Lk == 0)) return ATTN_OK;
+  if (Lk == 0 || Lq == 0) return ATTN_ERR_SHAPE;   // rows without keys, or keys without rows: no gradient defined
+  if (causal && Lq > Lk) return ATTN_ERR_SHAPE;
+  if ((double)B * Hq * (double)Lq * D > 9.0e18 || (double)B * Hkv * (double)Lk * D > 9.0e18) return ATTN_ERR_SHAPE;
+  if ((long long)B * Hkv * ((Lk + 127) / 128) > 0x7fffffffLL || (long long)B * Hq * ((Lq + 31) / 32) > 0x7fffffffLL)
+    return ATTN_ERR_SHAPE;
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL;
+  const size_t need = attn_backward_workspace_bytes(B, Hq, Lq);
+  if (workspace != nullptr && workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  BackwardArgs a;
+  a.q = static_cast<const uint16_t *>(q);
+  a.k = static_cast<const uint16_t *>(k);
+  a.v = static_cast<const uint16_t *>(v);
+  a.out = static_cast<const uint16_t *>(out);
+  a.dout = static_cast<const uint16_t *>(dout);
+  a.lse = lse;
+  a.dq = static_cast<uint16_t *>(dq);
+  a.dk = static_cast<uint16_t *>(dk);
+  a.dv = static_cast<uint16_t *>(dv);
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Lq = Lq;
+  a.Lk = Lk;
+  a.G = Hq / Hkv;
+  a.causal = causal ? 1 : 0;
+  a.window = (causal && window < Lk) ? window : 0;
+  a.dq_hpw = attn::backward_dq_heads(a.G);
+  a.scale = scale;
+  a.c = scale * kLog2e;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void *mem = workspace;
+  bool owned = false;
+  if (mem == nullptr) {
+    hipMemPool_t pool;
+    if (device_pool(&pool) != hipSuccess) return ATTN_ERR_HIP;
+    if (hipMallocFromPoolAsync(&mem, need, pool, s) != hipSuccess) return ATTN_ERR_HIP;
+    owned = true;
+  }
+  a.delta = static_cast<float *>(mem);
+  a.lse2 = reinterpret_cast<float *>(static_cast<char *>(mem) + need / 2);
+  hipError_t e = attn::launch_backward(a, D, s);
+  if (owned) {
+    hipError_t f = hipFreeAsync(mem, s);
+    if (e == hipSuccess) e = f;
+  }
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 int attn_decode(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens, void *out, int B,

@@ -1,0 +1,516 @@
+// Backward: dq, dk, dv of exact GQA attention from the forward's out and lse.
+//
+// Method (pages, by title): "어텐션 구현 고르기, SDPA·FlashAttention 메모리와
+// GPU 비용", section "eager 어텐션 메모리, 길이에 따라 얼마나 커지나" (training
+// keeps a score table per layer for the backward pass; FlashAttention keeps
+// only per-row statistics instead); the gradients are the chain rule through
+// the forward definition: with p_ij = exp(scale s_ij - lse_i),
+//   dv_j = sum_i p_ij dout_i,  dp_ij = <dout_i, v_j>,
+//   ds_ij = p_ij (dp_ij - delta_i),  delta_i = <dout_i, out_i>,
+//   dq_i = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,
+// summed over the G query heads of a KV head for dk and dv.
+//
+// gfx950 design
+//  * No score table: every tile of p is recomputed from q, k and the saved
+//    lse (one exp2 per element), as the forward never stored it.
+//  * dk/dv kernel: a wave owns 32 keys of one KV head and keeps their k and v
+//    rows as MFMA operands in registers; the workgroup (4 waves, 128 keys)
+//    walks the query tiles (32 rows) of all G query heads that read the KV
+//    head, staging q, dout, lse and delta in LDS.  Per tile and wave, four
+//    v_mfma_f32_32x32x16_bf16 chains: S = Q K^T and dP = dO V^T (queries on
+//    M, keys on N), then dV^T += dO^T P and dK^T += Q^T dS, where P and dS
+//    come straight from the S / dP accumulators (a lane holds one key column)
+//    and dO^T, Q^T are read with ds_read_b64_tr_b16.  dk and dv of a KV head
+//    are complete in one workgroup: no atomics.
+//  * dq kernel: a wave owns 32 query rows (q and dout rows as operands in
+//    registers) and walks the key tiles (64 keys) in reach of its rows:
+//    S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T with K^T read
+//    transposed from the same LDS tile.
+//  * A tile that is read both row-wise (b128) and transposed (tr16) is stored
+//    with a 16-byte-chunk XOR swizzle that keeps both access patterns free of
+//    bank conflicts (tswz).
+//  * Causal (bottom-right) and window masks: query or key tiles that no row
+//    or key of a wave can see are skipped; the mask is applied per element
+//    only on tiles that cross a boundary.
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace attn {
+namespace {
+
+// XOR on the 16-byte chunk index of row r of a tile read both by rows
+// (b128: 16 consecutive rows, one chunk each) and transposed (tr16: 4
+// consecutive rows, 64 bytes each): D = 64 rows are 128 bytes long, larger
+// rows a multiple of 256 bytes.
+template <int D>
+ATTN_DEV int tswz(int r) {
+  return D == 64 ? 4 * ((r >> 1) & 1) + ((r >> 2) & 3) : 4 * (r & 3) + ((r >> 2) & 3);
+}
+
+// element offset of logical chunk c (8 bf16) of row r in a swizzled tile
+template <int D>
+ATTN_DEV int toff(int r, int c) {
+  return r * D + 8 * (c ^ tswz<D>(r));
+}
+
+ATTN_DEV bf16x8 tr_operand(const uint16_t *lo, const uint16_t *hi) {
+  const bf16x4 a = lds_tr16(lo);
+  const bf16x4 b = lds_tr16(hi);
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// delta_i = <dout_i, out_i> (fp32), and lse_i * log2(e); one wave per row.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BackwardArgs a) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long rows = (long long)a.B * a.Hq * a.Lq;
+  if (row >= rows) return;
+  const uint16_t *o = a.out + row * D;
+  const uint16_t *g = a.dout + row * D;
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) {
+    const float x = (float)__builtin_bit_cast(__bf16, o[lane + 64 * i]);
+    const float y = (float)__builtin_bit_cast(__bf16, g[lane + 64 * i]);
+    s = __builtin_fmaf(x, y, s);
+  }
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) s += __shfl_xor(s, sh);
+  if (lane == 0) {
+    a.delta[row] = s;
+    a.lse2[row] = a.lse[row] * ATTN_LOG2E;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dk / dv
+// ---------------------------------------------------------------------------
+constexpr int kBwdWaves = 4;
+constexpr int kBwdKeys = 32 * kBwdWaves;   // keys per dk/dv workgroup
+constexpr int kBwdRows = 32;               // query rows per tile of the dk/dv loop
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void bwd_dkdv_kernel(BackwardArgs a) {
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int TILE = kBwdRows * D;         // elements of a q (or dout) tile
+  constexpr int LPT = TILE / 8 / 256;        // 16-byte chunks per thread per tile
+  static_assert(LPT >= 1, "tile too small");
+  __shared__ __attribute__((aligned(16))) uint16_t qs[2][TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t ds_[2][TILE];
+  __shared__ float lse_s[2][kBwdRows];
+  __shared__ float del_s[2][kBwdRows];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int ql = lane & 31, hh = lane >> 5, g16 = lane >> 4, j16 = lane & 15;
+
+  // workgroup -> (b, hkv, key block); key blocks in ascending order, so the
+  // blocks with the most visible query rows (causal) start first
+  const int nkb = (a.Lk + kBwdKeys - 1) / kBwdKeys;
+  const int t = blockIdx.x;
+  const int kbk = t % nkb;
+  const int bh = t / nkb;                     // b * Hkv + hkv
+  const int b = bh / a.Hkv, hkv = bh - b * a.Hkv;
+  const int j0 = kbk * kBwdKeys;
+  const int kw0 = j0 + 32 * w;                // this wave's first key
+  const int key = kw0 + ql;                   // this lane's key (column)
+  const int off = a.Lk - a.Lq;
+  const int win = a.window;
+
+  // k and v rows of the wave's keys as B operands: lane (ql, hh) holds key
+  // kw0 + ql, dims 16 ks + 8 hh ...
+  const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)a.Lk * D;
+  bf16x8 kf[D / 16], vf[D / 16];
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const bool in = key < a.Lk;
+    const uint16_t *kp = a.k + kvbase + (size_t)(in ? key : 0) * D + 8 * hh;
+    const uint16_t *vp = a.v + kvbase + (size_t)(in ? key : 0) * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      kf[ks] = as_bf16x8(in ? ld16(kp + 16 * ks) : z);
+      vf[ks] = as_bf16x8(in ? ld16(vp + 16 * ks) : z);
+    }
+  }
+
+  // query rows that see some key of this workgroup (per head: the same)
+  int qlo = 0, qhi = a.Lq;
+  if (a.causal) {
+    qlo = max(0, j0 - off);
+    if (win) qhi = min(a.Lq, j0 + kBwdKeys - 1 - off + win);
+  }
+  qlo = qlo / kBwdRows * kBwdRows;
+  const int ntile_h = qhi > qlo ? (qhi - qlo + kBwdRows - 1) / kBwdRows : 0;
+  const int ntile = ntile_h * a.G;
+
+  // per-lane LDS offsets: b128 operand (row ql, chunk 2 ks + hh) and the
+  // transposed operand (rows 4 hh + (j16 >> 2) [+8], 4 columns at
+  // 32 db + 16 (g16 & 1) + 4 (j16 & 3)); the 16-row chunk qc adds 16 D.
+  int roff[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) roff[ks] = toff<D>(ql, 2 * ks + hh);
+  int tlo[D / 32], thi[D / 32];
+  {
+    const int r = 4 * hh + (j16 >> 2);
+    const int c = 2 * (g16 & 1) + ((j16 & 3) >> 1);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      tlo[db] = toff<D>(r, 4 * db + c) + 4 * (j16 & 1);
+      thi[db] = toff<D>(r + 8, 4 * db + c) + 4 * (j16 & 1);
+    }
+  }
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    dk[i] = f32x16{};
+    dv[i] = f32x16{};
+  }
+
+  // staging of one tile (head hq, rows i0 ..): q and dout rows -> registers
+  u32x4 rq[LPT], rd[LPT];
+  float rl = 0.f, rdel = 0.f;
+  auto fetch = [&](int tt) __attribute__((always_inline)) {
+    const int hq = hkv * a.G + tt / ntile_h;
+    const int i0 = qlo + (tt % ntile_h) * kBwdRows;
+    const size_t rowbase = ((size_t)b * a.Hq + hq) * a.Lq;
+#pragma unroll
+    for (int n = 0; n < LPT; ++n) {
+      const int u = tid + 256 * n;
+      const int r = u / CPR, c = u % CPR;
+      const int i = i0 + r;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      rq[n] = i < a.Lq ? ld16(a.q + (rowbase + i) * D + 8 * c) : z;
+      rd[n] = i < a.Lq ? ld16(a.dout + (rowbase + i) * D + 8 * c) : z;
+    }
+    if (tid < kBwdRows) {
+      const int i = i0 + tid;
+      // rows past the end: lse = +inf gives p = 0
+      rl = i < a.Lq ? a.lse2[rowbase + i] : __builtin_inff();
+      rdel = i < a.Lq ? a.delta[rowbase + i] : 0.f;
+    }
+  };
+  auto stash = [&](int p) __attribute__((always_inline)) {
+#pragma unroll
+    for (int n = 0; n < LPT; ++n) {
+      const int u = tid + 256 * n;
+      const int r = u / CPR, c = u % CPR;
+      st16(&qs[p][toff<D>(r, c)], rq[n]);
+      st16(&ds_[p][toff<D>(r, c)], rd[n]);
+    }
+    if (tid < kBwdRows) {
+      lse_s[p][tid] = rl;
+      del_s[p][tid] = rdel;
+    }
+  };
+
+  const float c = a.c;
+  auto compute = [&](int tt, int p) __attribute__((always_inline)) {
+    const int i0 = qlo + (tt % ntile_h) * kBwdRows;
+    // tiles no row of which sees a key of this wave
+    if (a.causal) {
+      if (i0 + kBwdRows - 1 + off < kw0) return;                   // all keys after every row's diagonal
+      if (win && i0 + off - win + 1 > kw0 + 31) return;             // all keys before every row's window
+    }
+    const uint16_t *qt = qs[p];
+    const uint16_t *dt = ds_[p];
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(qt + roff[ks])), kf[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(dt + roff[ks])), vf[ks], dp, 0, 0, 0);
+    }
+    // this lane: key column `key`, query rows 8 (rr >> 2) + 4 hh + (rr & 3)
+    const bool crosses = a.causal && (i0 + off < kw0 + 31 || (win && i0 + kBwdRows - 1 + off - win + 1 > kw0));
+    float pv[16], dsv[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int r = 8 * (rr >> 2) + 4 * hh + (rr & 3);
+      float pe = fast_exp2(__builtin_fmaf(s[rr], c, -lse_s[p][r]));
+      if (crosses) {
+        const int lim = i0 + r + off;
+        const bool vis = key <= lim && (!win || key > lim - win);
+        pe = vis ? pe : 0.f;
+      }
+      pv[rr] = pe;
+      dsv[rr] = pe * (dp[rr] - del_s[p][r]);
+    }
+    bf16x8 pb[2], sb[2];
+#pragma unroll
+    for (int qc = 0; qc < 2; ++qc) {
+      pb[qc] = pack8(pv[8 * qc], pv[8 * qc + 1], pv[8 * qc + 2], pv[8 * qc + 3], pv[8 * qc + 4], pv[8 * qc + 5],
+                     pv[8 * qc + 6], pv[8 * qc + 7]);
+      sb[qc] = pack8(dsv[8 * qc], dsv[8 * qc + 1], dsv[8 * qc + 2], dsv[8 * qc + 3], dsv[8 * qc + 4],
+                     dsv[8 * qc + 5], dsv[8 * qc + 6], dsv[8 * qc + 7]);
+    }
+    // dV^T += dO^T P,  dK^T += Q^T dS  (k = the tile's query rows)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int qc = 0; qc < 2; ++qc) {
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            tr_operand(dt + 16 * qc * D + tlo[db], dt + 16 * qc * D + thi[db]), pb[qc], dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            tr_operand(qt + 16 * qc * D + tlo[db], qt + 16 * qc * D + thi[db]), sb[qc], dk[db], 0, 0, 0);
+      }
+    }
+  };
+
+  if (ntile > 0) {
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int tt = 0; tt < ntile; ++tt) {
+      const int p = tt & 1;
+      if (tt + 1 < ntile) fetch(tt + 1);
+      compute(tt, p);
+      if (tt + 1 < ntile) stash(p ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // dk = scale dK, dv = dV; lane: key column, dims 32 db + 8 j + 4 hh + (0..3)
+  if (key < a.Lk) {
+    uint16_t *kp = a.dk + kvbase + (size_t)key * D;
+    uint16_t *vp = a.dv + kvbase + (size_t)key * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * db + 8 * j + 4 * hh;
+        bf16x4 kk4, vv4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          kk4[i] = (__bf16)(dk[db][4 * j + i] * sc);
+          vv4[i] = (__bf16)(dv[db][4 * j + i]);
+        }
+        *reinterpret_cast<bf16x4 *>(kp + d) = kk4;
+        *reinterpret_cast<bf16x4 *>(vp + d) = vv4;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dq
+// ---------------------------------------------------------------------------
+constexpr int kBwdQKeys = 64;   // keys per tile of the dq loop
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void bwd_dq_kernel(BackwardArgs a) {
+  constexpr int CPR = D / 8;
+  constexpr int BK = kBwdQKeys;
+  constexpr int TILE = BK * D;
+  constexpr int LPT = TILE / 8 / 256;
+  static_assert(LPT >= 1, "tile too small");
+  __shared__ __attribute__((aligned(16))) uint16_t ks_[2][TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t vs_[2][TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int ql = lane & 31, hh = lane >> 5, g16 = lane >> 4, j16 = lane & 15;
+
+  // workgroup -> (b, hkv, head group, row block); waves: hpw heads x wph row
+  // sub-blocks of 32 rows.  Row blocks in descending order (causal: the rows
+  // that see the most keys start first).
+  const int hpw = a.dq_hpw, wph = kBwdWaves / hpw;
+  const int rows_wg = 32 * wph;
+  const int nrb = (a.Lq + rows_wg - 1) / rows_wg;
+  const int ngrp = a.G / hpw;
+  int t = blockIdx.x;
+  const int rbk = nrb - 1 - t % nrb;
+  t /= nrb;
+  const int grp = t % ngrp;
+  t /= ngrp;
+  const int hkv = t % a.Hkv;
+  const int b = t / a.Hkv;
+  const int hq = hkv * a.G + grp * hpw + w / wph;
+  const int r0w = rbk * rows_wg + 32 * (w % wph);   // this wave's first row
+  const int qrow = r0w + ql;                        // this lane's query row
+  const int off = a.Lk - a.Lq;
+  const int win = a.window;
+
+  // q and dout rows as B operands: lane (ql, hh) holds row qrow, dims 16 ks + 8 hh
+  const size_t rowi = ((size_t)b * a.Hq + hq) * a.Lq + (qrow < a.Lq ? qrow : 0);
+  bf16x8 qf[D / 16], of[D / 16];
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const bool in = qrow < a.Lq;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      qf[ks] = as_bf16x8(in ? ld16(a.q + rowi * D + 16 * ks + 8 * hh) : z);
+      of[ks] = as_bf16x8(in ? ld16(a.dout + rowi * D + 16 * ks + 8 * hh) : z);
+    }
+  }
+  const float lse2 = qrow < a.Lq ? a.lse2[rowi] : __builtin_inff();
+  const float del = qrow < a.Lq ? a.delta[rowi] : 0.f;
+
+  // key range of the workgroup's rows
+  const int rlo = rbk * rows_wg, rhi = min(a.Lq, rlo + rows_wg) - 1;
+  int kbeg = 0, kend = a.Lk;
+  if (a.causal) {
+    kend = min(a.Lk, rhi + off + 1);
+    if (win) kbeg = max(0, rlo + off - win + 1);
+  }
+  const int jbeg = kbeg / BK;
+  const int nt = kend > kbeg ? (kend + BK - 1) / BK - jbeg : 0;
+  // this wave's key range (for skipping and masking)
+  const int wlo = r0w, whi = min(a.Lq, r0w + 32) - 1;
+  const int kend_w = a.causal ? min(a.Lk, whi + off + 1) : a.Lk;
+  const int kbeg_w = (a.causal && win) ? max(0, wlo + off - win + 1) : 0;
+  // keys from kfull on may be hidden from some row of the wave (or lie past Lk)
+  const int kfull = a.causal ? min(a.Lk, wlo + off + 1) : a.Lk;
+  const int klo_until = (a.causal && win) ? whi + off - win + 1 : 0;
+
+  int roff[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) roff[ks] = toff<D>(ql, 2 * ks + hh);
+  int tlo[D / 32], thi[D / 32];
+  {
+    const int r = 4 * hh + (j16 >> 2);
+    const int c = 2 * (g16 & 1) + ((j16 & 3) >> 1);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      tlo[db] = toff<D>(r, 4 * db + c) + 4 * (j16 & 1);
+      thi[db] = toff<D>(r + 8, 4 * db + c) + 4 * (j16 & 1);
+    }
+  }
+
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) dq[i] = f32x16{};
+
+  const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)a.Lk * D;
+  u32x4 rk[LPT], rv[LPT];
+  auto fetch = [&](int jj) __attribute__((always_inline)) {
+    const int k0 = (jbeg + jj) * BK;
+#pragma unroll
+    for (int n = 0; n < LPT; ++n) {
+      const int u = tid + 256 * n;
+      const int r = u / CPR, c = u % CPR;
+      const int kk = k0 + r;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      rk[n] = kk < a.Lk ? ld16(a.k + kvbase + (size_t)kk * D + 8 * c) : z;
+      rv[n] = kk < a.Lk ? ld16(a.v + kvbase + (size_t)kk * D + 8 * c) : z;
+    }
+  };
+  auto stash = [&](int p) __attribute__((always_inline)) {
+#pragma unroll
+    for (int n = 0; n < LPT; ++n) {
+      const int u = tid + 256 * n;
+      const int r = u / CPR, c = u % CPR;
+      st16(&ks_[p][toff<D>(r, c)], rk[n]);
+      st16(&vs_[p][toff<D>(r, c)], rv[n]);
+    }
+  };
+
+  const float c = a.c;
+  auto compute = [&](int jj, int p) __attribute__((always_inline)) {
+    const int k0 = (jbeg + jj) * BK;
+    if (k0 >= kend_w || k0 + BK <= kbeg_w) return;
+    const uint16_t *kt = ks_[p];
+    const uint16_t *vt = vs_[p];
+    f32x16 s[BK / 32], dp[BK / 32];
+#pragma unroll
+    for (int rb = 0; rb < BK / 32; ++rb) {
+      s[rb] = f32x16{};
+      dp[rb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(kt + 32 * rb * D + roff[ks])), qf[ks], s[rb],
+                                                        0, 0, 0);
+        dp[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(vt + 32 * rb * D + roff[ks])), of[ks],
+                                                         dp[rb], 0, 0, 0);
+      }
+    }
+    // this lane: query row qrow, keys k0 + 32 rb + 8 (rr >> 2) + 4 hh + (rr & 3)
+    const bool crosses = k0 + BK > kfull || k0 < klo_until;
+    const int lim = a.causal ? qrow + off : a.Lk - 1;
+    bf16x8 sb[BK / 16];
+#pragma unroll
+    for (int rb = 0; rb < BK / 32; ++rb) {
+      float dsv[16];
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int kk = k0 + 32 * rb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+        float pe = fast_exp2(__builtin_fmaf(s[rb][rr], c, -lse2));
+        if (crosses) {
+          const bool vis = kk < a.Lk && kk <= lim && (!(a.causal && win) || kk > lim - win);
+          pe = vis ? pe : 0.f;
+        }
+        dsv[rr] = pe * (dp[rb][rr] - del);
+      }
+      sb[2 * rb] = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+      sb[2 * rb + 1] = pack8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
+    }
+    // dQ^T += K^T dS^T  (k = the tile's keys)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int kc = 0; kc < BK / 16; ++kc)
+        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            tr_operand(kt + 16 * kc * D + tlo[db], kt + 16 * kc * D + thi[db]), sb[kc], dq[db], 0, 0, 0);
+  };
+
+  if (nt > 0) {
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int jj = 0; jj < nt; ++jj) {
+      const int p = jj & 1;
+      if (jj + 1 < nt) fetch(jj + 1);
+      compute(jj, p);
+      if (jj + 1 < nt) stash(p ^ 1);
+      __syncthreads();
+    }
+  }
+
+  if (qrow < a.Lq) {
+    uint16_t *qp = a.dq + rowi * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x4 v4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v4[i] = (__bf16)(dq[db][4 * j + i] * sc);
+        *reinterpret_cast<bf16x4 *>(qp + 32 * db + 8 * j + 4 * hh) = v4;
+      }
+  }
+}
+
+template <int D>
+static hipError_t launch_bwd_t(const BackwardArgs &a, hipStream_t s) {
+  const long long rows = (long long)a.B * a.Hq * a.Lq;
+  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long nkb = (a.Lk + kBwdKeys - 1) / kBwdKeys;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)(nkb * a.B * a.Hkv)), dim3(256), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int rows_wg = 32 * (kBwdWaves / a.dq_hpw);
+  const long long nrb = (a.Lq + rows_wg - 1) / rows_wg;
+  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(nrb * (a.G / a.dq_hpw) * a.Hkv * a.B)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+int backward_dq_heads(int G) {
+  return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1);
+}
+
+hipError_t launch_backward(const BackwardArgs &a, int D, hipStream_t s) {
+  switch (D) {
+    case 64: return launch_bwd_t<64>(a, s);
+    case 128: return launch_bwd_t<128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace attn

@@ -52,6 +52,27 @@ struct DecodeArgs {
   float c;          // scale * log2(e)
 };
 
+struct BackwardArgs {
+  const uint16_t *q;      // [B][Hq][Lq][D]
+  const uint16_t *k;      // [B][Hkv][Lk][D]
+  const uint16_t *v;
+  const uint16_t *out;    // forward output [B][Hq][Lq][D]
+  const uint16_t *dout;   // gradient of the loss w.r.t. out
+  const float *lse;       // forward log-sum-exp [B][Hq][Lq] (natural log)
+  uint16_t *dq;           // [B][Hq][Lq][D]
+  uint16_t *dk;           // [B][Hkv][Lk][D]
+  uint16_t *dv;
+  float *delta;           // workspace [B][Hq][Lq]: <dout_i, out_i>
+  float *lse2;            // workspace [B][Hq][Lq]: lse * log2(e)
+  int B, Hq, Hkv, Lq, Lk;
+  int G;
+  int causal;
+  int window;
+  int dq_hpw;             // query heads per dq workgroup (divides G and 4)
+  float scale;
+  float c;                // scale * log2(e)
+};
+
 // Upper bound on the waves of the decode main kernel (sizes the workspace).
 constexpr int kDecodeMaxWaves = 4096;
 // Query heads of one KV head handled together by a decode wave (16 per MFMA
@@ -73,5 +94,8 @@ constexpr int kPrefillMaxSplits = 64;
 hipError_t launch_prefill(const PrefillArgs &a, int D, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int D, int waves, hipStream_t s);
 hipError_t decode_waves_per_cu(int D, int GW, bool q8, int *out);
+hipError_t launch_backward(const BackwardArgs &a, int D, hipStream_t s);
+// Query heads handled together by one workgroup of the dq kernel.
+int backward_dq_heads(int G);
 
 }  // namespace attn

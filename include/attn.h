@@ -68,7 +68,7 @@ typedef enum {
   ATTN_ERR_SHAPE = -2,    /* a negative size, Lk = 0 with Lq > 0, causal with Lq > Lk,
                              Lmax < 1, T outside 1..Lmax, or a size whose element count
                              overflows */
-  ATTN_ERR_HEADDIM = -3,  /* D not in {64, 128, 256} */
+  ATTN_ERR_HEADDIM = -3,  /* D not in {64, 128, 256} (attn_backward: not in {64, 128}) */
   ATTN_ERR_GQA = -4,      /* Hq < 1, Hkv < 1 or Hq % Hkv != 0 */
   ATTN_ERR_SCALE = -5,    /* scale is NaN or infinite */
   ATTN_ERR_HIP = -6,      /* a HIP call or kernel launch failed */
@@ -271,6 +271,49 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Lmax, int D, int 
  * arguments or when no device is available.
  */
 int attn_decode_waves(int B, int Hq, int Hkv, int Lmax, int D, int split_keys);
+
+/*
+ * attn_backward -- gradients dq, dk, dv of attn_prefill(_ex) from its out and
+ * lse and the upstream gradient dout.
+ *
+ * Pages: the cost guide, section "eager 어텐션 메모리, 길이에 따라 얼마나
+ * 커지나" (training keeps a score table per layer for the backward pass; the
+ * tiled method keeps only per-row statistics, from which the weights are
+ * recomputed here).  The gradients are those of the forward definition:
+ * with p_ij = exp(scale <q_i, k_j> - lse_i) over the visible keys,
+ *   dv_j = sum_i p_ij dout_i,   ds_ij = p_ij (<dout_i, v_j> - <dout_i, out_i>),
+ *   dq_i = scale sum_j ds_ij k_j,   dk_j = scale sum_i ds_ij q_i,
+ * with dk and dv of a KV head summed over its G = Hq / Hkv query heads.
+ *
+ *   q, out, dout, dq  [B][Hq][Lq][D] bf16     lse [B][Hq][Lq] fp32 (natural log,
+ *                                              as attn_prefill writes it)
+ *   k, v, dk, dv      [B][Hkv][Lk][D] bf16
+ *
+ * causal and window as attn_prefill_ex (the same mask must be given as in
+ * the forward call that produced out and lse).  D must be 64 or 128 (else
+ * ATTN_ERR_HEADDIM).  Every row must see a key: Lk = 0 with Lq > 0, Lq = 0
+ * with Lk > 0 and causal with Lq > Lk are ATTN_ERR_SHAPE; B = 0 or
+ * Lq = Lk = 0 is an empty call (ATTN_OK, nothing touched, pointers may be
+ * NULL).  Every pointer is required otherwise (ATTN_ERR_NULL).  dq, dk and dv
+ * are fully overwritten (not accumulated into) and must not overlap the
+ * inputs.  Accumulation is fp32; the three outputs are rounded to bf16.
+ *
+ * workspace: NULL (taken from HIP's stream-ordered allocator on `stream` and
+ * released there) or at least attn_backward_workspace_bytes(B, Hq, Lq) bytes
+ * of device memory (else ATTN_ERR_WORKSPACE), 256-byte aligned, not used by
+ * other work until the call's kernels have finished.  Three kernels are
+ * enqueued on `stream`; the call does not synchronise.
+ */
+int attn_backward(const void *q, const void *k, const void *v, const void *out, const void *dout,
+                  const float *lse, void *dq, void *dk, void *dv, int B, int Hq, int Hkv, int Lq, int Lk,
+                  int D, int causal, int window, float scale, void *workspace, size_t workspace_bytes,
+                  void *stream);
+
+/*
+ * attn_backward_workspace_bytes -- bytes of workspace attn_backward needs
+ * (two fp32 values per query row); 0 for an empty call or invalid sizes.
+ */
+size_t attn_backward_workspace_bytes(int B, int Hq, int Lq);
 
 /* attn_status_string -- static, NUL-terminated text for a status code. */
 const char *attn_status_string(int status);

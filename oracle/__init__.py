@@ -27,9 +27,12 @@ from .reference import (visible_mask, kv_head_of, attention, attention_rows, dec
                         attention_probs)
 from .brute import brute_attention
 from .quant import dequantize_q8, round_to_bf16, half_bits_to_f64
-from .backward import attention_backward, attention_backward_sampled, delta_rows
+from .backward import (attention_backward, attention_backward_sampled, attention_backward_from_forward,
+                       attention_backward_from_forward_sampled, delta_rows)
 from . import accounting
 
 __all__ = ["visible_mask", "kv_head_of", "attention", "attention_rows", "decode", "combine_partials",
            "attention_probs", "brute_attention", "dequantize_q8", "round_to_bf16", "half_bits_to_f64",
-           "attention_backward", "attention_backward_sampled", "delta_rows", "accounting"]
+           "attention_backward", "attention_backward_sampled", "attention_backward_from_forward",
+           "attention_backward_from_forward_sampled", "delta_rows",
+           "accounting"]

@@ -113,9 +113,77 @@ def attention_backward_sampled(q, k, v, dout, causal: bool, scale: float, qrows,
     return dq, dk, dv
 
 
+def attention_backward_from_forward(q, k, v, out, dout, lse, causal: bool, scale: float, window: int = 0):
+    """The gradients as a backward pass computes them from a forward's saved
+    out and lse: p_ij = exp(scale s_ij - lse_i) over the visible keys and
+    delta_i = <dout_i, out_i> with the given out and lse (instead of the
+    exact softmax and its own sum_l p_il dp_il).  With the exact out and lse
+    this is ``attention_backward``; with an out rounded to bf16 it is what a
+    kernel that receives that out computes, before its own rounding."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    out = np.asarray(out, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    B, Hq, Hkv, Lq, Lk, D = _check(q, k, v)
+    keep = visible_mask(Lq, Lk, causal, "bottom_right", window)
+    sc = np.float64(scale)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    delta = delta_rows(out, dout)
+    for b in range(B):
+        for h in range(Hq):
+            hk = kv_head_of(h, Hq, Hkv)
+            p = np.where(keep, np.exp(sc * (q[b, h] @ k[b, hk].T) - lse[b, h][:, None]), 0.0)
+            dv[b, hk] += p.T @ dout[b, h]
+            dp = dout[b, h] @ v[b, hk].T
+            ds = p * (dp - delta[b, h][:, None])
+            dq[b, h] = sc * (ds @ k[b, hk])
+            dk[b, hk] += sc * (ds.T @ q[b, h])
+    return dq, dk, dv
+
+
+def attention_backward_from_forward_sampled(q, k, v, out, dout, lse, causal: bool, scale: float, qrows, krows,
+                                            window: int = 0):
+    """``attention_backward_from_forward`` at selected query rows (dq) and key
+    positions (dk, dv) only.  With the saved out and lse given, every weight
+    p_ij is known without a pass over the row, so dq_i needs row i only and
+    dk_j, dv_j need column j only (over every row that sees key j)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    B, Hq, Hkv, Lq, Lk, D = _check(q, k, v)
+    qrows = np.asarray(qrows, dtype=np.int64)
+    krows = np.asarray(krows, dtype=np.int64)
+    keep = visible_mask(Lq, Lk, causal, "bottom_right", window)
+    sc = np.float64(scale)
+    delta = delta_rows(out, dout)
+    dq = np.zeros((B, Hq, len(qrows), D))
+    dk = np.zeros((B, Hkv, len(krows), D))
+    dv = np.zeros((B, Hkv, len(krows), D))
+    for b in range(B):
+        for h in range(Hq):
+            hk = kv_head_of(h, Hq, Hkv)
+            # rows qrows, all keys
+            p = np.where(keep[qrows], np.exp(sc * (q[b, h, qrows] @ k[b, hk].T) - lse[b, h, qrows][:, None]), 0.0)
+            ds = p * (dout[b, h, qrows] @ v[b, hk].T - delta[b, h, qrows][:, None])
+            dq[b, h] = sc * (ds @ k[b, hk])
+            # all rows, keys krows
+            p = np.where(keep[:, krows], np.exp(sc * (q[b, h] @ k[b, hk, krows].T) - lse[b, h][:, None]), 0.0)
+            ds = p * (dout[b, h] @ v[b, hk, krows].T - delta[b, h][:, None])
+            dk[b, hk] += sc * (ds.T @ q[b, h])
+            dv[b, hk] += p.T @ dout[b, h]
+    return dq, dk, dv
+
+
 def delta_rows(out, dout):
     """sum_l p_il dp_il written as <dout_i, out_i> (the same number)."""
     return (np.asarray(out, dtype=np.float64) * np.asarray(dout, dtype=np.float64)).sum(axis=-1)
 
 
-__all__ = ["attention_backward", "attention_backward_sampled", "delta_rows", "kv_head_of"]
+__all__ = ["attention_backward", "attention_backward_sampled", "attention_backward_from_forward",
+           "attention_backward_from_forward_sampled", "delta_rows", "kv_head_of"]

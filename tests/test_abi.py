@@ -198,3 +198,25 @@ def test_decode_q8_validation(attn):
     assert q8(D=96) == -3
     need = attn.decode_multi_workspace_bytes(2, 8, 2, 1, 64, 128)
     assert q8(ws=P, ws_bytes=need - 1) == -8
+
+
+def test_backward_validation_and_sizes(attn):
+    def bwd(B=1, Hq=4, Hkv=2, Lq=64, Lk=64, D=128, causal=1, window=0, scale=0.1, q=P, ws=N, ws_bytes=0):
+        return attn.lib.attn_backward(q, P, P, P, P, P, P, P, P, B, Hq, Hkv, Lq, Lk, D, causal, window,
+                                      ctypes.c_float(scale), ws, ws_bytes, None)
+    assert bwd(Hq=3) == -4
+    assert bwd(D=256) == -3            # backward covers head dims 64 and 128
+    assert bwd(D=96) == -3
+    assert bwd(scale=math.inf) == -5
+    assert bwd(Lq=65, Lk=64) == -2      # causal rows past the keys
+    assert bwd(Lq=0, Lk=5) == -2
+    assert bwd(Lq=5, Lk=0) == -2
+    assert bwd(window=4, causal=0) == -2
+    assert bwd(window=-1) == -2
+    assert bwd(q=N) == -1
+    assert bwd(B=0, q=N) == 0
+    assert bwd(Lq=0, Lk=0, q=N) == 0
+    need = attn.backward_workspace_bytes(1, 4, 64)
+    assert need == 2 * ((64 * 4 * 4 + 255) // 256 * 256)
+    assert bwd(ws=P, ws_bytes=need - 1) == -8
+    assert attn.backward_workspace_bytes(0, 4, 64) == 0

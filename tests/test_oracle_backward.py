@@ -177,3 +177,31 @@ def test_backward_planted_mistakes_are_caught():
     for slip in ({"no_delta": True}, {"no_scale_dk": True}, {"wrong_group": True}):
         bad = grads(**slip)
         assert not all(np.allclose(a, b, atol=2e-7) for a, b in zip(bad, (fq, fk, fv))), slip
+
+
+@pytest.mark.parametrize("causal,window", [(True, 0), (False, 0), (True, 6)])
+def test_backward_from_forward_with_exact_forward_is_the_gradient(causal, window):
+    """Given the exact out and lse, the saved-statistics form equals the
+    gradient pinned above; given a perturbed out, only dq and dk move."""
+    q, k, v, dout = _inputs(2, 4, 2, 13, 21, 6, [47, causal, window])
+    out, lse = oracle.attention(q, k, v, causal, 0.4, window=window)
+    want = bw.attention_backward(q, k, v, dout, causal, 0.4, window=window)
+    got = bw.attention_backward_from_forward(q, k, v, out, dout, lse, causal, 0.4, window=window)
+    for g, w in zip(got, want):
+        np.testing.assert_allclose(g, w, rtol=0, atol=1e-12)
+    bent = bw.attention_backward_from_forward(q, k, v, out * (1 + 1e-3), dout, lse, causal, 0.4, window=window)
+    assert np.array_equal(bent[2], got[2])
+    assert not np.allclose(bent[0], got[0], atol=1e-9)
+
+
+@pytest.mark.parametrize("causal,window", [(True, 0), (False, 0), (True, 29)])
+def test_backward_from_forward_sampled_equals_full(causal, window):
+    q, k, v, dout = _inputs(2, 4, 2, 150, 230, 8, [48, causal, window])
+    out, lse = oracle.attention(q, k, v, causal, 0.3, window=window)
+    out = out + 1e-3 * np.sin(np.arange(out.size)).reshape(out.shape)     # any saved out, not the exact one
+    full = bw.attention_backward_from_forward(q, k, v, out, dout, lse, causal, 0.3, window=window)
+    qr, kr = np.array([0, 7, 100, 149]), np.array([0, 1, 80, 229])
+    got = bw.attention_backward_from_forward_sampled(q, k, v, out, dout, lse, causal, 0.3, qr, kr, window=window)
+    np.testing.assert_allclose(got[0], full[0][:, :, qr], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got[1], full[1][:, :, kr], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got[2], full[2][:, :, kr], rtol=0, atol=1e-12)
