@@ -94,32 +94,48 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BackwardArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kBwdWaves = 4;
 constexpr int kBwdKeys = 32 * kBwdWaves;   // keys per dk/dv workgroup
-constexpr int kBwdRows = 32;               // query rows per tile of the dk/dv loop
+constexpr int kBwdRows = 64;               // query rows per stage of the dk/dv loop (two halves of 32)
+
+typedef __attribute__((address_space(3))) void bwd_lds_t;
+typedef __attribute__((address_space(1))) void bwd_glb_t;
+
+// s_waitcnt vmcnt(n) for n < 16 (expcnt and lgkmcnt left alone)
+#define ATTN_BWD_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void bwd_dkdv_kernel(BackwardArgs a) {
-  constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  constexpr int TILE = kBwdRows * D;         // elements of a q (or dout) tile
-  constexpr int LPT = TILE / 8 / 256;        // 16-byte chunks per thread per tile
-  static_assert(LPT >= 1, "tile too small");
-  __shared__ __attribute__((aligned(16))) uint16_t qs[2][TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t ds_[2][TILE];
-  __shared__ float lse_s[2][kBwdRows];
-  __shared__ float del_s[2][kBwdRows];
+  constexpr int TILE = kBwdRows * D;          // elements of a q (or dout) stage
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int RPB = 512 / D;                // rows per 1 KiB direct load
+  constexpr int BPW = TILE * 2 / 1024 / kBwdWaves;   // 1 KiB blocks per wave per tensor and stage
+  static_assert(BPW * kBwdWaves * 1024 == TILE * 2, "stage must split evenly over the waves");
+  // three stages, each its own array (so that reads of one stage never wait
+  // for the direct loads still filling another): q, dout, and the rows'
+  // lse * log2(e) (floats 0..63) and delta (floats 64..127)
+  __shared__ __attribute__((aligned(1024))) uint16_t qa[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t qb[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t qc[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t da[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t db_[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t dc[TILE];
+  __shared__ __attribute__((aligned(256))) float sa[2 * kBwdRows];
+  __shared__ __attribute__((aligned(256))) float sb[2 * kBwdRows];
+  __shared__ __attribute__((aligned(256))) float sc_[2 * kBwdRows];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int ql = lane & 31, hh = lane >> 5, g16 = lane >> 4, j16 = lane & 15;
 
-  // workgroup -> (b, hkv, key block); key blocks in ascending order, so the
-  // blocks with the most visible query rows (causal) start first
-  const int nkb = (a.Lk + kBwdKeys - 1) / kBwdKeys;
+  // workgroup -> (key block, b, hkv): the key blocks with the most visible
+  // query rows (causal: the first ones) of every head start first
+  const int nbh = a.B * a.Hkv;
   const int t = blockIdx.x;
-  const int kbk = t % nkb;
-  const int bh = t / nkb;                     // b * Hkv + hkv
+  const int kbk = t / nbh;
+  const int bh = t - kbk * nbh;                // b * Hkv + hkv
   const int b = bh / a.Hkv, hkv = bh - b * a.Hkv;
   const int j0 = kbk * kBwdKeys;
-  const int kw0 = j0 + 32 * w;                // this wave's first key
-  const int key = kw0 + ql;                   // this lane's key (column)
+  const int kw0 = j0 + 32 * w;                 // this wave's first key
+  const int key = kw0 + ql;                    // this lane's key (column)
   const int off = a.Lk - a.Lq;
   const int win = a.window;
 
@@ -139,19 +155,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
     }
   }
 
-  // query rows that see some key of this workgroup (per head: the same)
+  // query rows that see some key of this workgroup (the same for every head)
   int qlo = 0, qhi = a.Lq;
   if (a.causal) {
     qlo = max(0, j0 - off);
     if (win) qhi = min(a.Lq, j0 + kBwdKeys - 1 - off + win);
   }
-  qlo = qlo / kBwdRows * kBwdRows;
+  qlo = qlo / 32 * 32;
   const int ntile_h = qhi > qlo ? (qhi - qlo + kBwdRows - 1) / kBwdRows : 0;
   const int ntile = ntile_h * a.G;
 
   // per-lane LDS offsets: b128 operand (row ql, chunk 2 ks + hh) and the
   // transposed operand (rows 4 hh + (j16 >> 2) [+8], 4 columns at
-  // 32 db + 16 (g16 & 1) + 4 (j16 & 3)); the 16-row chunk qc adds 16 D.
+  // 32 db + 16 (g16 & 1) + 4 (j16 & 3)); a 16-row step adds 16 D.
   int roff[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) roff[ks] = toff<D>(ql, 2 * ks + hh);
@@ -160,9 +176,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
     const int r = 4 * hh + (j16 >> 2);
     const int c = 2 * (g16 & 1) + ((j16 & 3) >> 1);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      tlo[db] = toff<D>(r, 4 * db + c) + 4 * (j16 & 1);
-      thi[db] = toff<D>(r + 8, 4 * db + c) + 4 * (j16 & 1);
+    for (int dd = 0; dd < D / 32; ++dd) {
+      tlo[dd] = toff<D>(r, 4 * dd + c) + 4 * (j16 & 1);
+      thi[dd] = toff<D>(r + 8, 4 * dd + c) + 4 * (j16 & 1);
     }
   }
 
@@ -173,123 +189,135 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
     dv[i] = f32x16{};
   }
 
-  // staging of one tile (head hq, rows i0 ..): q and dout rows -> registers
-  u32x4 rq[LPT], rd[LPT];
-  float rl = 0.f, rdel = 0.f;
-  auto fetch = [&](int tt) __attribute__((always_inline)) {
+  // Stage tile tt (head, 64 rows) straight from global memory into LDS: each
+  // wave moves BPW blocks of 1 KiB of q and of dout (lane i fills bytes
+  // [16 i, 16 i + 16) of a block, so it fetches the logical chunk that the
+  // swizzle puts there; rows past the end are read from the last row and
+  // masked in compute), and waves 0 and 1 move the rows' lse and delta
+  // (one float per lane).  Per tile a wave issues 2 BPW loads (+1 for waves
+  // 0 and 1).
+  auto issue = [&](int tt, uint16_t *qd, uint16_t *dd, float *sd) __attribute__((always_inline)) {
     const int hq = hkv * a.G + tt / ntile_h;
     const int i0 = qlo + (tt % ntile_h) * kBwdRows;
     const size_t rowbase = ((size_t)b * a.Hq + hq) * a.Lq;
 #pragma unroll
-    for (int n = 0; n < LPT; ++n) {
-      const int u = tid + 256 * n;
-      const int r = u / CPR, c = u % CPR;
-      const int i = i0 + r;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      rq[n] = i < a.Lq ? ld16(a.q + (rowbase + i) * D + 8 * c) : z;
-      rd[n] = i < a.Lq ? ld16(a.dout + (rowbase + i) * D + 8 * c) : z;
+    for (int i = 0; i < BPW; ++i) {
+      const int blk = wu * BPW + i;
+      const int row = blk * RPB + lane / CPR;
+      const int c = (lane % CPR) ^ tswz<D>(row);
+      const size_t grow = rowbase + min(i0 + row, a.Lq - 1);
+      __builtin_amdgcn_global_load_lds((bwd_glb_t *)(a.q + grow * D + 8 * c), (bwd_lds_t *)(qd + blk * 512), 16, 0,
+                                       0);
+      __builtin_amdgcn_global_load_lds((bwd_glb_t *)(a.dout + grow * D + 8 * c), (bwd_lds_t *)(dd + blk * 512), 16,
+                                       0, 0);
     }
-    if (tid < kBwdRows) {
-      const int i = i0 + tid;
-      // rows past the end: lse = +inf gives p = 0
-      rl = i < a.Lq ? a.lse2[rowbase + i] : __builtin_inff();
-      rdel = i < a.Lq ? a.delta[rowbase + i] : 0.f;
+    if (wu < 2) {
+      const float *src = wu == 0 ? a.lse2 : a.delta;
+      const size_t grow = rowbase + min(i0 + lane, a.Lq - 1);
+      __builtin_amdgcn_global_load_lds((bwd_glb_t *)(src + grow), (bwd_lds_t *)(sd + 64 * wu), 4, 0, 0);
     }
   };
-  auto stash = [&](int p) __attribute__((always_inline)) {
-#pragma unroll
-    for (int n = 0; n < LPT; ++n) {
-      const int u = tid + 256 * n;
-      const int r = u / CPR, c = u % CPR;
-      st16(&qs[p][toff<D>(r, c)], rq[n]);
-      st16(&ds_[p][toff<D>(r, c)], rd[n]);
-    }
-    if (tid < kBwdRows) {
-      lse_s[p][tid] = rl;
-      del_s[p][tid] = rdel;
+  auto wait_tile = [&](bool younger) __attribute__((always_inline)) {
+    if (younger) {
+      if (wu < 2) ATTN_BWD_WAIT_VM(2 * BPW + 1);
+      else ATTN_BWD_WAIT_VM(2 * BPW);
+    } else {
+      ATTN_BWD_WAIT_VM(0);
     }
   };
 
   const float c = a.c;
-  auto compute = [&](int tt, int p) __attribute__((always_inline)) {
-    const int i0 = qlo + (tt % ntile_h) * kBwdRows;
-    // tiles no row of which sees a key of this wave
+  // one half (32 rows) of a staged tile
+  auto half = [&](const uint16_t *qt, const uint16_t *dt, const float *st, int i0h, int rb) __attribute__((
+                                                                                              always_inline)) {
+    // skip: the half lies past the rows, or no row of it sees a key of this wave
+    if (i0h >= a.Lq) return;
     if (a.causal) {
-      if (i0 + kBwdRows - 1 + off < kw0) return;                   // all keys after every row's diagonal
-      if (win && i0 + off - win + 1 > kw0 + 31) return;             // all keys before every row's window
+      if (i0h + 31 + off < kw0) return;
+      if (win && i0h + off - win + 1 > kw0 + 31) return;
     }
-    const uint16_t *qt = qs[p];
-    const uint16_t *dt = ds_[p];
+    qt += rb * 32 * D;
+    dt += rb * 32 * D;
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(qt + roff[ks])), kf[ks], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(dt + roff[ks])), vf[ks], dp, 0, 0, 0);
     }
-    // this lane: key column `key`, query rows 8 (rr >> 2) + 4 hh + (rr & 3)
-    const bool crosses = a.causal && (i0 + off < kw0 + 31 || (win && i0 + kBwdRows - 1 + off - win + 1 > kw0));
+    // this lane: key column `key`, rows i0h + 8 (rr >> 2) + 4 hh + (rr & 3)
+    const bool crosses = i0h + 31 >= a.Lq ||
+                         (a.causal && (i0h + off < kw0 + 31 || (win && i0h + 31 + off - win + 1 > kw0)));
     float pv[16], dsv[16];
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       const int r = 8 * (rr >> 2) + 4 * hh + (rr & 3);
-      float pe = fast_exp2(__builtin_fmaf(s[rr], c, -lse_s[p][r]));
+      float pe = fast_exp2(__builtin_fmaf(s[rr], c, -st[32 * rb + r]));
       if (crosses) {
-        const int lim = i0 + r + off;
-        const bool vis = key <= lim && (!win || key > lim - win);
+        const int i = i0h + r;
+        const int lim = i + off;
+        const bool vis = i < a.Lq && (!a.causal || (key <= lim && (!win || key > lim - win)));
         pe = vis ? pe : 0.f;
       }
       pv[rr] = pe;
-      dsv[rr] = pe * (dp[rr] - del_s[p][r]);
+      dsv[rr] = pe * (dp[rr] - st[kBwdRows + 32 * rb + r]);
     }
-    bf16x8 pb[2], sb[2];
+    bf16x8 pb[2], sb2[2];
 #pragma unroll
-    for (int qc = 0; qc < 2; ++qc) {
-      pb[qc] = pack8(pv[8 * qc], pv[8 * qc + 1], pv[8 * qc + 2], pv[8 * qc + 3], pv[8 * qc + 4], pv[8 * qc + 5],
-                     pv[8 * qc + 6], pv[8 * qc + 7]);
-      sb[qc] = pack8(dsv[8 * qc], dsv[8 * qc + 1], dsv[8 * qc + 2], dsv[8 * qc + 3], dsv[8 * qc + 4],
-                     dsv[8 * qc + 5], dsv[8 * qc + 6], dsv[8 * qc + 7]);
+    for (int qh = 0; qh < 2; ++qh) {
+      pb[qh] = pack8(pv[8 * qh], pv[8 * qh + 1], pv[8 * qh + 2], pv[8 * qh + 3], pv[8 * qh + 4], pv[8 * qh + 5],
+                     pv[8 * qh + 6], pv[8 * qh + 7]);
+      sb2[qh] = pack8(dsv[8 * qh], dsv[8 * qh + 1], dsv[8 * qh + 2], dsv[8 * qh + 3], dsv[8 * qh + 4],
+                      dsv[8 * qh + 5], dsv[8 * qh + 6], dsv[8 * qh + 7]);
     }
-    // dV^T += dO^T P,  dK^T += Q^T dS  (k = the tile's query rows)
+    // dV^T += dO^T P,  dK^T += Q^T dS  (k = the half's query rows)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int dd = 0; dd < D / 32; ++dd) {
 #pragma unroll
-      for (int qc = 0; qc < 2; ++qc) {
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            tr_operand(dt + 16 * qc * D + tlo[db], dt + 16 * qc * D + thi[db]), pb[qc], dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            tr_operand(qt + 16 * qc * D + tlo[db], qt + 16 * qc * D + thi[db]), sb[qc], dk[db], 0, 0, 0);
+      for (int qh = 0; qh < 2; ++qh) {
+        dv[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            tr_operand(dt + 16 * qh * D + tlo[dd], dt + 16 * qh * D + thi[dd]), pb[qh], dv[dd], 0, 0, 0);
+        dk[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            tr_operand(qt + 16 * qh * D + tlo[dd], qt + 16 * qh * D + thi[dd]), sb2[qh], dk[dd], 0, 0, 0);
       }
     }
   };
+  auto step = [&](int tt, const uint16_t *qt, const uint16_t *dt, const float *st, uint16_t *qn, uint16_t *dn,
+                  float *sn) __attribute__((always_inline)) {
+    wait_tile(tt + 1 < ntile);
+    __syncthreads();
+    if (tt + 2 < ntile) issue(tt + 2, qn, dn, sn);
+    const int i0 = qlo + (tt % ntile_h) * kBwdRows;
+    half(qt, dt, st, i0, 0);
+    half(qt, dt, st, i0 + 32, 1);
+  };
 
   if (ntile > 0) {
-    fetch(0);
-    stash(0);
-    __syncthreads();
-    for (int tt = 0; tt < ntile; ++tt) {
-      const int p = tt & 1;
-      if (tt + 1 < ntile) fetch(tt + 1);
-      compute(tt, p);
-      if (tt + 1 < ntile) stash(p ^ 1);
-      __syncthreads();
+    issue(0, qa, da, sa);
+    if (ntile > 1) issue(1, qb, db_, sb);
+    for (int tt = 0; tt < ntile; tt += 3) {
+      step(tt, qa, da, sa, qc, dc, sc_);
+      if (tt + 1 >= ntile) break;
+      step(tt + 1, qb, db_, sb, qa, da, sa);
+      if (tt + 2 >= ntile) break;
+      step(tt + 2, qc, dc, sc_, qb, db_, sb);
     }
   }
 
-  // dk = scale dK, dv = dV; lane: key column, dims 32 db + 8 j + 4 hh + (0..3)
+  // dk = scale dK, dv = dV; lane: key column, dims 32 dd + 8 j + 4 hh + (0..3)
   if (key < a.Lk) {
     uint16_t *kp = a.dk + kvbase + (size_t)key * D;
     uint16_t *vp = a.dv + kvbase + (size_t)key * D;
-    const float sc = a.scale;
+    const float scl = a.scale;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int dd = 0; dd < D / 32; ++dd)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int d = 32 * db + 8 * j + 4 * hh;
+        const int d = 32 * dd + 8 * j + 4 * hh;
         bf16x4 kk4, vv4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          kk4[i] = (__bf16)(dk[db][4 * j + i] * sc);
-          vv4[i] = (__bf16)(dv[db][4 * j + i]);
+          kk4[i] = (__bf16)(dk[dd][4 * j + i] * scl);
+          vv4[i] = (__bf16)(dv[dd][4 * j + i]);
         }
         *reinterpret_cast<bf16x4 *>(kp + d) = kk4;
         *reinterpret_cast<bf16x4 *>(vp + d) = vv4;
