@@ -335,28 +335,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   constexpr int CPR = D / 8;
   constexpr int BK = kBwdQKeys;
   constexpr int TILE = BK * D;
-  constexpr int LPT = TILE / 8 / 256;
-  static_assert(LPT >= 1, "tile too small");
-  __shared__ __attribute__((aligned(16))) uint16_t ks_[2][TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t vs_[2][TILE];
+  constexpr int RPB = 512 / D;                       // rows per 1 KiB direct load
+  constexpr int BPW = TILE * 2 / 1024 / kBwdWaves;   // 1 KiB blocks per wave per tensor and tile
+  static_assert(BPW * kBwdWaves * 1024 == TILE * 2, "tile must split evenly over the waves");
+  // three stages of K and V tiles, each its own array
+  __shared__ __attribute__((aligned(1024))) uint16_t ka[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t kb_[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t kc[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t va[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t vb[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t vc[TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int ql = lane & 31, hh = lane >> 5, g16 = lane >> 4, j16 = lane & 15;
 
-  // workgroup -> (b, hkv, head group, row block); waves: hpw heads x wph row
-  // sub-blocks of 32 rows.  Row blocks in descending order (causal: the rows
-  // that see the most keys start first).
+  // workgroup -> (row block, head group, b, hkv): waves are hpw heads x wph
+  // row sub-blocks of 32 rows.  Row blocks in descending order (causal: the
+  // rows that see the most keys start first), all heads of a row block
+  // together.
   const int hpw = a.dq_hpw, wph = kBwdWaves / hpw;
   const int rows_wg = 32 * wph;
   const int nrb = (a.Lq + rows_wg - 1) / rows_wg;
   const int ngrp = a.G / hpw;
-  int t = blockIdx.x;
-  const int rbk = nrb - 1 - t % nrb;
-  t /= nrb;
-  const int grp = t % ngrp;
-  t /= ngrp;
-  const int hkv = t % a.Hkv;
-  const int b = t / a.Hkv;
+  const int nu = ngrp * a.Hkv * a.B;
+  const int t = blockIdx.x;
+  const int rbk = nrb - 1 - t / nu;
+  int u = t % nu;
+  const int grp = u % ngrp;
+  u /= ngrp;
+  const int hkv = u % a.Hkv;
+  const int b = u / a.Hkv;
   const int hq = hkv * a.G + grp * hpw + w / wph;
   const int r0w = rbk * rows_wg + 32 * (w % wph);   // this wave's first row
   const int qrow = r0w + ql;                        // this lane's query row
@@ -403,9 +412,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
     const int r = 4 * hh + (j16 >> 2);
     const int c = 2 * (g16 & 1) + ((j16 & 3) >> 1);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      tlo[db] = toff<D>(r, 4 * db + c) + 4 * (j16 & 1);
-      thi[db] = toff<D>(r + 8, 4 * db + c) + 4 * (j16 & 1);
+    for (int dd = 0; dd < D / 32; ++dd) {
+      tlo[dd] = toff<D>(r, 4 * dd + c) + 4 * (j16 & 1);
+      thi[dd] = toff<D>(r + 8, 4 * dd + c) + 4 * (j16 & 1);
     }
   }
 
@@ -413,36 +422,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) dq[i] = f32x16{};
 
-  const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)a.Lk * D;
-  u32x4 rk[LPT], rv[LPT];
-  auto fetch = [&](int jj) __attribute__((always_inline)) {
+  // Tile jj of K and V straight from global memory into LDS (as the dk/dv
+  // kernel stages q and dout); keys past the end are read from the last key
+  // and masked.  Per tile a wave issues 2 BPW loads.
+  const size_t kvrow = ((size_t)b * a.Hkv + hkv) * (size_t)a.Lk;   // first key row of this KV head
+  auto issue = [&](int jj, uint16_t *kd, uint16_t *vd) __attribute__((always_inline)) {
     const int k0 = (jbeg + jj) * BK;
 #pragma unroll
-    for (int n = 0; n < LPT; ++n) {
-      const int u = tid + 256 * n;
-      const int r = u / CPR, c = u % CPR;
-      const int kk = k0 + r;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      rk[n] = kk < a.Lk ? ld16(a.k + kvbase + (size_t)kk * D + 8 * c) : z;
-      rv[n] = kk < a.Lk ? ld16(a.v + kvbase + (size_t)kk * D + 8 * c) : z;
-    }
-  };
-  auto stash = [&](int p) __attribute__((always_inline)) {
-#pragma unroll
-    for (int n = 0; n < LPT; ++n) {
-      const int u = tid + 256 * n;
-      const int r = u / CPR, c = u % CPR;
-      st16(&ks_[p][toff<D>(r, c)], rk[n]);
-      st16(&vs_[p][toff<D>(r, c)], rv[n]);
+    for (int i = 0; i < BPW; ++i) {
+      const int blk = wu * BPW + i;
+      const int row = blk * RPB + lane / CPR;
+      const int c = (lane % CPR) ^ tswz<D>(row);
+      const size_t grow = kvrow + min(k0 + row, a.Lk - 1);
+      __builtin_amdgcn_global_load_lds((bwd_glb_t *)(a.k + grow * D + 8 * c), (bwd_lds_t *)(kd + blk * 512), 16, 0,
+                                       0);
+      __builtin_amdgcn_global_load_lds((bwd_glb_t *)(a.v + grow * D + 8 * c), (bwd_lds_t *)(vd + blk * 512), 16, 0,
+                                       0);
     }
   };
 
   const float c = a.c;
-  auto compute = [&](int jj, int p) __attribute__((always_inline)) {
+  auto compute = [&](int jj, const uint16_t *kt, const uint16_t *vt) __attribute__((always_inline)) {
     const int k0 = (jbeg + jj) * BK;
     if (k0 >= kend_w || k0 + BK <= kbeg_w) return;
-    const uint16_t *kt = ks_[p];
-    const uint16_t *vt = vs_[p];
     f32x16 s[BK / 32], dp[BK / 32];
 #pragma unroll
     for (int rb = 0; rb < BK / 32; ++rb) {
@@ -478,37 +480,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
     }
     // dQ^T += K^T dS^T  (k = the tile's keys)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int dd = 0; dd < D / 32; ++dd)
 #pragma unroll
-      for (int kc = 0; kc < BK / 16; ++kc)
-        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            tr_operand(kt + 16 * kc * D + tlo[db], kt + 16 * kc * D + thi[db]), sb[kc], dq[db], 0, 0, 0);
+      for (int kc2 = 0; kc2 < BK / 16; ++kc2)
+        dq[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            tr_operand(kt + 16 * kc2 * D + tlo[dd], kt + 16 * kc2 * D + thi[dd]), sb[kc2], dq[dd], 0, 0, 0);
+  };
+  auto step = [&](int jj, const uint16_t *kt, const uint16_t *vt, uint16_t *kn, uint16_t *vn)
+      __attribute__((always_inline)) {
+    if (jj + 1 < nt) ATTN_BWD_WAIT_VM(2 * BPW);
+    else ATTN_BWD_WAIT_VM(0);
+    __syncthreads();
+    if (jj + 2 < nt) issue(jj + 2, kn, vn);
+    compute(jj, kt, vt);
   };
 
   if (nt > 0) {
-    fetch(0);
-    stash(0);
-    __syncthreads();
-    for (int jj = 0; jj < nt; ++jj) {
-      const int p = jj & 1;
-      if (jj + 1 < nt) fetch(jj + 1);
-      compute(jj, p);
-      if (jj + 1 < nt) stash(p ^ 1);
-      __syncthreads();
+    issue(0, ka, va);
+    if (nt > 1) issue(1, kb_, vb);
+    for (int jj = 0; jj < nt; jj += 3) {
+      step(jj, ka, va, kc, vc);
+      if (jj + 1 >= nt) break;
+      step(jj + 1, kb_, vb, ka, va);
+      if (jj + 2 >= nt) break;
+      step(jj + 2, kc, vc, kb_, vb);
     }
   }
 
   if (qrow < a.Lq) {
     uint16_t *qp = a.dq + rowi * D;
-    const float sc = a.scale;
+    const float scl = a.scale;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int dd = 0; dd < D / 32; ++dd)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         bf16x4 v4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v4[i] = (__bf16)(dq[db][4 * j + i] * sc);
-        *reinterpret_cast<bf16x4 *>(qp + 32 * db + 8 * j + 4 * hh) = v4;
+        for (int i = 0; i < 4; ++i) v4[i] = (__bf16)(dq[dd][4 * j + i] * scl);
+        *reinterpret_cast<bf16x4 *>(qp + 32 * dd + 8 * j + 4 * hh) = v4;
       }
   }
 }
