@@ -227,6 +227,29 @@ def all_configs(iters: int):
                           "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}), flush=True)
         del q, k, v, out, lse
 
+    # backward (dq, dk, dv from the forward's out and lse) at the Qwen3-8B
+    # shapes; work counted as 2.5 x the forward's (five matrix products over
+    # the visible pairs: QK^T, dO V^T, P^T dO, dS^T Q, dS K)
+    for pc in (ai.QWEN_4K, ai.QWEN_16K):
+        q, k, v = to_dev(pc.q_bits(), dev), to_dev(pc.k_bits(), dev), to_dev(pc.v_bits(), dev)
+        g = to_dev(pc.dout_bits(), dev)
+        out, lse = attn.prefill(q, k, v, causal=True, scale=pc.scale)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(attn.backward_workspace_bytes(pc.B, pc.Hq, pc.Lq), dtype=torch.uint8, device=dev)
+        fn = lambda: attn.backward(q, k, v, out, g, lse, causal=True, scale=pc.scale, dq=dq, dk=dk, dv=dv,  # noqa: E731
+                                   workspace=ws)
+        for _ in range(2):
+            fn()
+        ms = _time_ms(fn, iters, stream)
+        fl = 5 * acc.prefill_flops(pc.B, pc.Hq, pc.D, pc.Lq, pc.Lk, True) // 2
+        tf = fl / (ms * 1e-3) / 1e12
+        print(json.dumps({"config": pc.name.replace("prefill", "backward"), "kind": "backward", "B": pc.B,
+                          "Hq": pc.Hq, "Hkv": pc.Hkv, "Lq": pc.Lq, "Lk": pc.Lk, "D": pc.D, "causal": True,
+                          "ms": round(ms, 4), "flops": fl, "TFLOP/s": round(tf, 1),
+                          "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}), flush=True)
+        del q, k, v, g, out, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+
     # several new rows per sequence (speculative verification) over the ragged cache
     dc = ai.RAGGED_DECODE
     lens = dc.kv_lens()
