@@ -67,12 +67,15 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "launches": 3}), flush=True)
 
 
+# the sources of the kernels the default bench step launches (and of their launch shapes)
+BENCH_SOURCES = ("api.hip", "common.h", "decode.hip", "kernels.h", "prefill.hip")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_attention_30_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in BENCH_SOURCES:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
