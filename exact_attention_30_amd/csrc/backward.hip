@@ -61,7 +61,33 @@ ATTN_DEV bf16x8 tr_operand(const uint16_t *lo, const uint16_t *hi) {
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// Scheduling of a run of N MFMAs that each take R operands read from LDS:
+// the first AHEAD MFMAs' reads go first, then every MFMA is followed by the
+// reads of the MFMA AHEAD places later, so that LDS latency hides behind
+// matrix work (AHEAD = 0: left to the compiler).
+template <int N, int R, int AHEAD>
+ATTN_DEV void sched_reads_ahead() {
+  if constexpr (AHEAD > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x100, R * AHEAD, 0);
+#pragma unroll
+    for (int i = 0; i < N - AHEAD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+  }
+}
+
 }  // namespace
+
+//  ATTN_BWD_QK_AHEAD   operand reads of the S / dP products issued this many MFMAs ahead
+//  ATTN_BWD_TR_AHEAD   transposed operand reads of the dV / dK / dQ products, likewise
+#ifndef ATTN_BWD_QK_AHEAD
+#define ATTN_BWD_QK_AHEAD 6
+#endif
+#ifndef ATTN_BWD_TR_AHEAD
+#define ATTN_BWD_TR_AHEAD 4
+#endif
 
 // ---------------------------------------------------------------------------
 // delta_i = <dout_i, out_i> (fp32), and lse_i * log2(e); one wave per row.
@@ -96,11 +122,19 @@ constexpr int kBwdWaves = 4;
 constexpr int kBwdKeys = 32 * kBwdWaves;   // keys per dk/dv workgroup
 constexpr int kBwdRows = 64;               // query rows per stage of the dk/dv loop (two halves of 32)
 
-typedef __attribute__((address_space(3))) void bwd_lds_t;
-typedef __attribute__((address_space(1))) void bwd_glb_t;
 
 // s_waitcnt vmcnt(n) for n < 16 (expcnt and lgkmcnt left alone)
 #define ATTN_BWD_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
+
+// One direct global->LDS load of 16 (or 4) bytes per lane: lane i writes
+// bytes [size i, size (i + 1)) after the wave-uniform LDS address `lds`.
+template <int SIZE>
+ATTN_DEV void dma_to_lds(const void *g, void *lds) {
+  auto *gp = (__attribute__((address_space(1))) void *)const_cast<void *>(g);
+  auto *lp = (__attribute__((address_space(3))) void *)lds;
+  if constexpr (SIZE == 16) __builtin_amdgcn_global_load_lds(gp, lp, 16, 0, 0);
+  else __builtin_amdgcn_global_load_lds(gp, lp, 4, 0, 0);
+}
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void bwd_dkdv_kernel(BackwardArgs a) {
@@ -206,15 +240,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
       const int row = blk * RPB + lane / CPR;
       const int c = (lane % CPR) ^ tswz<D>(row);
       const size_t grow = rowbase + min(i0 + row, a.Lq - 1);
-      __builtin_amdgcn_global_load_lds((bwd_glb_t *)(a.q + grow * D + 8 * c), (bwd_lds_t *)(qd + blk * 512), 16, 0,
-                                       0);
-      __builtin_amdgcn_global_load_lds((bwd_glb_t *)(a.dout + grow * D + 8 * c), (bwd_lds_t *)(dd + blk * 512), 16,
-                                       0, 0);
+      dma_to_lds<16>(a.q + grow * D + 8 * c, qd + blk * 512);
+      dma_to_lds<16>(a.dout + grow * D + 8 * c, dd + blk * 512);
     }
     if (wu < 2) {
       const float *src = wu == 0 ? a.lse2 : a.delta;
       const size_t grow = rowbase + min(i0 + lane, a.Lq - 1);
-      __builtin_amdgcn_global_load_lds((bwd_glb_t *)(src + grow), (bwd_lds_t *)(sd + 64 * wu), 4, 0, 0);
+      dma_to_lds<4>(src + grow, sd + 64 * wu);
     }
   };
   auto wait_tile = [&](bool younger) __attribute__((always_inline)) {
@@ -244,6 +276,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(qt + roff[ks])), kf[ks], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(dt + roff[ks])), vf[ks], dp, 0, 0, 0);
     }
+    sched_reads_ahead<2 * (D / 16), 1, ATTN_BWD_QK_AHEAD>();
     // this lane: key column `key`, rows i0h + 8 (rr >> 2) + 4 hh + (rr & 3)
     const bool crosses = i0h + 31 >= a.Lq ||
                          (a.causal && (i0h + off < kw0 + 31 || (win && i0h + 31 + off - win + 1 > kw0)));
@@ -280,6 +313,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
             tr_operand(qt + 16 * qh * D + tlo[dd], qt + 16 * qh * D + thi[dd]), sb2[qh], dk[dd], 0, 0, 0);
       }
     }
+    sched_reads_ahead<4 * (D / 32), 2, ATTN_BWD_TR_AHEAD>();
   };
   auto step = [&](int tt, const uint16_t *qt, const uint16_t *dt, const float *st, uint16_t *qn, uint16_t *dn,
                   float *sn) __attribute__((always_inline)) {
@@ -291,6 +325,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
     half(qt, dt, st, i0 + 32, 1);
   };
 
+  // the k/v operand loads complete before any staged load is issued, so no
+  // wait for them is left inside the loop (where it would also drain the
+  // stages in flight)
+  ATTN_BWD_WAIT_VM(0);
   if (ntile > 0) {
     issue(0, qa, da, sa);
     if (ntile > 1) issue(1, qb, db_, sb);
@@ -434,10 +472,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
       const int row = blk * RPB + lane / CPR;
       const int c = (lane % CPR) ^ tswz<D>(row);
       const size_t grow = kvrow + min(k0 + row, a.Lk - 1);
-      __builtin_amdgcn_global_load_lds((bwd_glb_t *)(a.k + grow * D + 8 * c), (bwd_lds_t *)(kd + blk * 512), 16, 0,
-                                       0);
-      __builtin_amdgcn_global_load_lds((bwd_glb_t *)(a.v + grow * D + 8 * c), (bwd_lds_t *)(vd + blk * 512), 16, 0,
-                                       0);
+      dma_to_lds<16>(a.k + grow * D + 8 * c, kd + blk * 512);
+      dma_to_lds<16>(a.v + grow * D + 8 * c, vd + blk * 512);
     }
   };
 
@@ -458,6 +494,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
                                                          dp[rb], 0, 0, 0);
       }
     }
+    sched_reads_ahead<2 * (BK / 32) * (D / 16), 1, ATTN_BWD_QK_AHEAD>();
     // this lane: query row qrow, keys k0 + 32 rb + 8 (rr >> 2) + 4 hh + (rr & 3)
     const bool crosses = k0 + BK > kfull || k0 < klo_until;
     const int lim = a.causal ? qrow + off : a.Lk - 1;
@@ -485,6 +522,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
       for (int kc2 = 0; kc2 < BK / 16; ++kc2)
         dq[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             tr_operand(kt + 16 * kc2 * D + tlo[dd], kt + 16 * kc2 * D + thi[dd]), sb[kc2], dq[dd], 0, 0, 0);
+    sched_reads_ahead<(D / 32) * (BK / 16), 2, ATTN_BWD_TR_AHEAD>();
   };
   auto step = [&](int jj, const uint16_t *kt, const uint16_t *vt, uint16_t *kn, uint16_t *vn)
       __attribute__((always_inline)) {
@@ -495,6 +533,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
     compute(jj, kt, vt);
   };
 
+  // the q/dout operand loads complete before any staged load is issued (see
+  // the dk/dv kernel)
+  ATTN_BWD_WAIT_VM(0);
   if (nt > 0) {
     issue(0, ka, va);
     if (nt > 1) issue(1, kb_, vb);
