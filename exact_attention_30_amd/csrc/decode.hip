@@ -134,13 +134,15 @@ struct DecodeRaw<D, false> {
 template <int D>
 struct DecodeRaw<D, true> {
   // K: piece i of a lane in group g holds the 16 codes of dims 64 i + 16 g ...,
-  // all inside one 32-element block (2 i + g / 2), so one scale per piece
+  // all inside one 32-element block (2 i + g / 2)
   static constexpr int KQ = D / 64;
   static constexpr int VU = (D / 2 + 63) / 64;
+  static constexpr int SW = D / 64;   // dwords of one row's D/32 binary16 scales
   u32x4 kq[2][KQ];
-  uint16_t ksc[2][KQ];
   u32x2 vq[VU][8];
-  uint16_t vsc[VU][8];
+  // the block's scale rows, one per lane: lanes 0..31 the K rows of keys
+  // kb + lane, lanes 32..63 the V rows of keys kb + lane - 32
+  uint32_t sc[SW];
 };
 
 template <int D, int NCB, bool Q8>
@@ -151,6 +153,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
   constexpr int VU = (VUN + 63) / 64;    // units per lane
   constexpr int VTS = 40;                // V^T row stride in LDS (bf16): 32 keys + pad
   __shared__ __attribute__((aligned(16))) uint16_t vt[D * VTS];
+  // int8 caches: the block's K and V scale rows ([2][32 keys][D / 32] binary16)
+  __shared__ __attribute__((aligned(16))) uint16_t sct[Q8 ? 2 * 32 * (D / 32) : 2];
 
   const int lane = threadIdx.x;
   const int ql = lane & 15, g = lane >> 4;
@@ -245,20 +249,35 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
     auto load = [&](Raw &raw, int kb) {
       if constexpr (Q8) {
         // K: 16 codes of dims 64 i + 16 g ... per piece (each instruction reads
-        // 64 contiguous bytes of a row), and the scale of their block
+        // 64 contiguous bytes of a row)
   #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           const int key = kb + 16 * rb + ql;
           const bool in = key < k1 && key >= kmin;
           const int8_t *p = kq8 + (size_t)key * D + 16 * g;
-          const uint16_t *ps = ksg + (size_t)key * (D / 32) + (g >> 1);
   #pragma unroll
-          for (int i = 0; i < Raw::KQ; ++i) {
-            raw.kq[rb][i] = in ? ld16_stream(p + 64 * i) : zero4;
-            raw.ksc[rb][i] = in ? ps[2 * i] : (uint16_t)0;
+          for (int i = 0; i < Raw::KQ; ++i) raw.kq[rb][i] = in ? ld16_stream(p + 64 * i) : zero4;
+        }
+        // scales: one row per lane (K rows on lanes 0..31, V rows on 32..63),
+        // one load instead of a small load per element group
+        {
+          const int key = kb + (lane & 31);
+          const bool in = key < k1 && key >= kmin;
+          const uint16_t *ps = (lane < 32 ? ksg : vsg) + (size_t)(in ? key : kmin) * (D / 32);
+          if constexpr (Raw::SW == 1) {
+            raw.sc[0] = in ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(ps)) : 0u;
+          } else if constexpr (Raw::SW == 2) {
+            const u32x2 v2 =
+                in ? __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(ps)) : u32x2{zero2, zero2};
+            raw.sc[0] = v2[0];
+            raw.sc[1] = v2[1];
+          } else {
+            const u32x4 v4 = in ? ld16_stream(ps) : zero4;
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) raw.sc[j] = v4[j];
           }
         }
-        // V: 8 codes (one 8-dim chunk) of 8 keys per unit, and the scale of each
+        // V: 8 codes (one 8-dim chunk) of 8 keys per unit
   #pragma unroll
         for (int iu = 0; iu < VU; ++iu) {
           const int u = lane + 64 * iu;
@@ -270,7 +289,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
               const bool in = key < k1 && key >= kmin;
               const u32x2 *pv = reinterpret_cast<const u32x2 *>(vq8 + (size_t)key * D + 8 * c);
               raw.vq[iu][kk] = in ? __builtin_nontemporal_load(pv) : u32x2{zero2, zero2};
-              raw.vsc[iu][kk] = in ? vsg[(size_t)key * (D / 32) + c / 4] : (uint16_t)0;
             }
           }
         }
@@ -308,20 +326,32 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
       u32x4 kr[NKR];
       u32x4 vr[VU][8];
       if constexpr (Q8) {
+        // the scale rows through LDS; each lane then reads the scales it needs
+  #pragma unroll
+        for (int j = 0; j < Raw::SW; ++j)
+          *reinterpret_cast<uint32_t *>(sct + lane * (D / 32) + 2 * j) = raw.sc[j];
+        __syncthreads();
   #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
   #pragma unroll
           for (int ks = 0; ks < KST; ++ks) {
-            // chunk ks = dims 64 (ks / 2) + 16 g + 8 (ks % 2): half of piece ks / 2
+            // chunk ks = dims 64 (ks / 2) + 16 g + 8 (ks % 2): half of piece ks / 2,
+            // in block 2 (ks / 2) + g / 2 of key row 16 rb + ql
             const int i = ks >> 1, h = ks & 1;
-            kr[rb * KST + ks] =
-                dequant8(raw.kq[rb][i][2 * h], raw.kq[rb][i][2 * h + 1], half_bits_to_float(raw.ksc[rb][i]));
+            const uint16_t sk = sct[(16 * rb + ql) * (D / 32) + 2 * i + (g >> 1)];
+            kr[rb * KST + ks] = dequant8(raw.kq[rb][i][2 * h], raw.kq[rb][i][2 * h + 1], half_bits_to_float(sk));
           }
   #pragma unroll
-        for (int iu = 0; iu < VU; ++iu)
+        for (int iu = 0; iu < VU; ++iu) {
+          const int u = lane + 64 * iu;
+          const int c = u % (D / 8), gg = u / (D / 8);
   #pragma unroll
-          for (int kk = 0; kk < 8; ++kk)
-            vr[iu][kk] = dequant8(raw.vq[iu][kk][0], raw.vq[iu][kk][1], half_bits_to_float(raw.vsc[iu][kk]));
+          for (int kk = 0; kk < 8; ++kk) {
+            const int row = kk < 4 ? 4 * gg + kk : 16 + 4 * gg + kk - 4;
+            const uint16_t sv = sct[(32 + row) * (D / 32) + c / 4];
+            vr[iu][kk] = dequant8(raw.vq[iu][kk][0], raw.vq[iu][kk][1], half_bits_to_float(sv));
+          }
+        }
       } else {
   #pragma unroll
         for (int i = 0; i < NKR; ++i) kr[i] = raw.kr[i];
