@@ -78,8 +78,34 @@ ATTN_DEV void sched_reads_ahead() {
   }
 }
 
+// The same, with V VALU instructions placed after every MFMA of the run
+// (work of another stage that does not feed these MFMAs).
+template <int N, int R, int AHEAD, int V>
+ATTN_DEV void sched_interleave() {
+  __builtin_amdgcn_sched_group_barrier(0x100, R * AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+  }
+}
+
 }  // namespace
 
+//  ATTN_BWD_PIPE       dk/dv: both halves of an unmasked stage software-pipelined
+//  ATTN_BWD_VALU_PER   VALU instructions scheduled after each MFMA there
+#ifndef ATTN_BWD_PIPE
+#define ATTN_BWD_PIPE 1
+#endif
+#ifndef ATTN_BWD_VALU_PER
+#define ATTN_BWD_VALU_PER 6
+#endif
 //  ATTN_BWD_QK_AHEAD   operand reads of the S / dP products issued this many MFMAs ahead
 //  ATTN_BWD_TR_AHEAD   transposed operand reads of the dV / dK / dQ products, likewise
 #ifndef ATTN_BWD_QK_AHEAD
@@ -259,27 +285,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   };
 
   const float c = a.c;
-  // one half (32 rows) of a staged tile
-  auto half = [&](const uint16_t *qt, const uint16_t *dt, const float *st, int i0h, int rb) __attribute__((
-                                                                                              always_inline)) {
-    // skip: the half lies past the rows, or no row of it sees a key of this wave
-    if (i0h >= a.Lq) return;
-    if (a.causal) {
-      if (i0h + 31 + off < kw0) return;
-      if (win && i0h + off - win + 1 > kw0 + 31) return;
-    }
-    qt += rb * 32 * D;
-    dt += rb * 32 * D;
-    f32x16 s = f32x16{}, dp = f32x16{};
+  // A half (32 rows starting at i0h) of a staged tile: skipped when it lies
+  // past the rows or no row of it sees a key of this wave; masked per
+  // element when it crosses a mask boundary or the end of the rows.
+  auto skip_half = [&](int i0h) __attribute__((always_inline)) {
+    if (i0h >= a.Lq) return true;
+    return a.causal && (i0h + 31 + off < kw0 || (win && i0h + off - win + 1 > kw0 + 31));
+  };
+  auto cross_half = [&](int i0h) __attribute__((always_inline)) {
+    return i0h + 31 >= a.Lq || (a.causal && (i0h + off < kw0 + 31 || (win && i0h + 31 + off - win + 1 > kw0)));
+  };
+  // S = Q K^T and dP = dO V^T of one half (qt, dt at the half's first row)
+  auto sdp = [&](const uint16_t *qt, const uint16_t *dt, f32x16 &s, f32x16 &dp) __attribute__((always_inline)) {
+    s = f32x16{};
+    dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(qt + roff[ks])), kf[ks], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(dt + roff[ks])), vf[ks], dp, 0, 0, 0);
     }
-    sched_reads_ahead<2 * (D / 16), 1, ATTN_BWD_QK_AHEAD>();
-    // this lane: key column `key`, rows i0h + 8 (rr >> 2) + 4 hh + (rr & 3)
-    const bool crosses = i0h + 31 >= a.Lq ||
-                         (a.causal && (i0h + off < kw0 + 31 || (win && i0h + 31 + off - win + 1 > kw0)));
+  };
+  // p and ds of one half as bf16 B operands; this lane: key column `key`,
+  // rows i0h + 8 (rr >> 2) + 4 hh + (rr & 3)
+  auto soft = [&](const float *st, int rb, int i0h, const f32x16 &s, const f32x16 &dp, bf16x8(&pb)[2],
+                  bf16x8(&sb)[2], bool crosses) __attribute__((always_inline)) {
     float pv[16], dsv[16];
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
@@ -294,15 +323,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
       pv[rr] = pe;
       dsv[rr] = pe * (dp[rr] - st[kBwdRows + 32 * rb + r]);
     }
-    bf16x8 pb[2], sb2[2];
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
       pb[qh] = pack8(pv[8 * qh], pv[8 * qh + 1], pv[8 * qh + 2], pv[8 * qh + 3], pv[8 * qh + 4], pv[8 * qh + 5],
                      pv[8 * qh + 6], pv[8 * qh + 7]);
-      sb2[qh] = pack8(dsv[8 * qh], dsv[8 * qh + 1], dsv[8 * qh + 2], dsv[8 * qh + 3], dsv[8 * qh + 4],
-                      dsv[8 * qh + 5], dsv[8 * qh + 6], dsv[8 * qh + 7]);
+      sb[qh] = pack8(dsv[8 * qh], dsv[8 * qh + 1], dsv[8 * qh + 2], dsv[8 * qh + 3], dsv[8 * qh + 4],
+                     dsv[8 * qh + 5], dsv[8 * qh + 6], dsv[8 * qh + 7]);
     }
-    // dV^T += dO^T P,  dK^T += Q^T dS  (k = the half's query rows)
+  };
+  // dV^T += dO^T P,  dK^T += Q^T dS  (k = the half's query rows)
+  auto upd = [&](const uint16_t *qt, const uint16_t *dt, const bf16x8(&pb)[2], const bf16x8(&sb)[2])
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int dd = 0; dd < D / 32; ++dd) {
 #pragma unroll
@@ -310,9 +341,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
         dv[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             tr_operand(dt + 16 * qh * D + tlo[dd], dt + 16 * qh * D + thi[dd]), pb[qh], dv[dd], 0, 0, 0);
         dk[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            tr_operand(qt + 16 * qh * D + tlo[dd], qt + 16 * qh * D + thi[dd]), sb2[qh], dk[dd], 0, 0, 0);
+            tr_operand(qt + 16 * qh * D + tlo[dd], qt + 16 * qh * D + thi[dd]), sb[qh], dk[dd], 0, 0, 0);
       }
     }
+  };
+  // one half on its own
+  auto half = [&](const uint16_t *qt, const uint16_t *dt, const float *st, int i0h, int rb) __attribute__((
+                                                                                              always_inline)) {
+    if (skip_half(i0h)) return;
+    qt += rb * 32 * D;
+    dt += rb * 32 * D;
+    f32x16 s, dp;
+    sdp(qt, dt, s, dp);
+    sched_reads_ahead<2 * (D / 16), 1, ATTN_BWD_QK_AHEAD>();
+    bf16x8 pb[2], sb2[2];
+    soft(st, rb, i0h, s, dp, pb, sb2, cross_half(i0h));
+    upd(qt, dt, pb, sb2);
+    sched_reads_ahead<4 * (D / 32), 2, ATTN_BWD_TR_AHEAD>();
+  };
+  // both halves, neither masked: software-pipelined so that the exponentials
+  // of one half run beside the MFMAs of the other
+  auto both = [&](const uint16_t *qt, const uint16_t *dt, const float *st, int i0, bool m0, bool m1)
+      __attribute__((always_inline)) {
+    f32x16 s0, dp0, s1, dp1;
+    bf16x8 pb0[2], sb0[2], pb1[2], sb1[2];
+    sdp(qt, dt, s0, dp0);
+    sched_reads_ahead<2 * (D / 16), 1, ATTN_BWD_QK_AHEAD>();
+    sdp(qt + 32 * D, dt + 32 * D, s1, dp1);
+    soft(st, 0, i0, s0, dp0, pb0, sb0, m0);
+    sched_interleave<2 * (D / 16), 1, ATTN_BWD_QK_AHEAD, ATTN_BWD_VALU_PER>();
+    upd(qt, dt, pb0, sb0);
+    soft(st, 1, i0 + 32, s1, dp1, pb1, sb1, m1);
+    sched_interleave<4 * (D / 32), 2, ATTN_BWD_TR_AHEAD, ATTN_BWD_VALU_PER>();
+    upd(qt + 32 * D, dt + 32 * D, pb1, sb1);
     sched_reads_ahead<4 * (D / 32), 2, ATTN_BWD_TR_AHEAD>();
   };
   auto step = [&](int tt, const uint16_t *qt, const uint16_t *dt, const float *st, uint16_t *qn, uint16_t *dn,
@@ -321,8 +382,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
     __syncthreads();
     if (tt + 2 < ntile) issue(tt + 2, qn, dn, sn);
     const int i0 = qlo + (tt % ntile_h) * kBwdRows;
-    half(qt, dt, st, i0, 0);
-    half(qt, dt, st, i0 + 32, 1);
+    if (ATTN_BWD_PIPE && !skip_half(i0) && !skip_half(i0 + 32) && !cross_half(i0) && !cross_half(i0 + 32)) {
+      both(qt, dt, st, i0, false, false);
+    } else {
+      half(qt, dt, st, i0, 0);
+      half(qt, dt, st, i0 + 32, 1);
+    }
   };
 
   // the k/v operand loads complete before any staged load is issued, so no
