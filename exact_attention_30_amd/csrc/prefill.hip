@@ -71,9 +71,23 @@
 
 namespace attn {
 
+//  ATTN_PF_NW256         waves per workgroup for D = 256 (8: two per SIMD; 4: one
+//                       per SIMD, which leaves room for its O accumulators and Q
+//                       operands without spilling)
+#ifndef ATTN_PF_NW256
+#define ATTN_PF_NW256 4
+#endif
+//  ATTN_PF_BK256        key-tile size for D = 256
+#ifndef ATTN_PF_BK256
+#define ATTN_PF_BK256 64
+#endif
+
+template <int D>
+constexpr int kPfThreads = (D == 256 ? ATTN_PF_NW256 : 8) * 64;
+
 template <int D, int BK>
 struct PrefillCfg {
-  static constexpr int NW = 8;
+  static constexpr int NW = kPfThreads<D> / 64;
   static constexpr int NT = NW * 64;
   static constexpr int CPR = D / 8;                   // 16-byte chunks per K/V row
   static constexpr int RPD = 512 / D;                 // rows per 1 KiB direct-to-LDS load
@@ -100,7 +114,7 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 #define ATTN_WAIT_VMEM() __builtin_amdgcn_s_waitcnt(0x0F70)
 
 template <int D, int BK>
-__global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
   using C = PrefillCfg<D, BK>;
   // four separate arrays, so that reads of one buffer never wait for the
   // direct loads still filling another
@@ -172,7 +186,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
     constexpr bool V = decltype(is_v)::value;
 #pragma unroll
     for (int i = 0; i < 2 * C::DPW; ++i) {
-      const int blk = (wu & 3) * 2 * C::DPW + i;
+      const int blk = (wu % (C::NW / 2)) * 2 * C::DPW + i;
       const int row = blk * C::RPD + lane / C::CPR;
       const int c = (lane % C::CPR) ^ (V ? vswz<D>(row) : kswz<D>(row));
       const int grow = min(j * BK + row, a.Lk - 1);
@@ -495,12 +509,11 @@ static hipError_t launch_t(const PrefillArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-int prefill_tile_keys(int D) { return D == 256 ? 32 : (D == 128 ? ATTN_PF_BK128 : 64); }
+int prefill_tile_keys(int D) { return D == 256 ? ATTN_PF_BK256 : (D == 128 ? ATTN_PF_BK128 : 64); }
 
 // Query-row packing of the kernel above: 8 waves x 32 rows per workgroup.
 bool prefill_plan(PrefillArgs &a, int D) {
-  (void)D;
-  const int nw = 8;
+  const int nw = D == 256 ? PrefillCfg<256, ATTN_PF_BK256>::NW : 8;
   const int rows = 32;
   int g = a.G, x = nw;
   while (x) {
@@ -523,7 +536,7 @@ hipError_t launch_prefill(const PrefillArgs &a, int D, hipStream_t s) {
   switch (D) {
     case 64: return launch_t<64, 64>(a, s);
     case 128: return launch_t<128, ATTN_PF_BK128>(a, s);
-    case 256: return launch_t<256, 32>(a, s);
+    case 256: return launch_t<256, ATTN_PF_BK256>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
