@@ -121,6 +121,11 @@ ATTN_DEV u32x4 dequant8(uint32_t lo, uint32_t hi, float s) {
 }
 ATTN_DEV float half_bits_to_float(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
+// Largest column-block count that keeps two register sets of K/V in flight.
+#ifndef ATTN_DEC_DBUF_NCB
+#define ATTN_DEC_DBUF_NCB 2
+#endif
+
 // Registers of one 32-key block in flight: bf16 K operands and V rows, or
 // (Q8) the int8 codes and scales they are dequantized from.
 template <int D, bool Q8>
@@ -463,7 +468,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
     };
 
     const int nblk = (k1 - k0 + 31) / 32;
-    if constexpr (D <= 128) {
+    if constexpr (D <= 128 && NCB <= ATTN_DEC_DBUF_NCB) {
       // two register sets: block i+1 is in flight while block i is computed
       Raw rA, rB;
       load(rA, k0);
@@ -475,7 +480,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
         compute(rB, k0 + 32 * (bi + 1));
       }
     } else {
-      // D = 256: one register set (a second would not fit next to the accumulators)
+      // D = 256, or four column blocks: one register set (a second would not
+      // fit next to the accumulators)
       Raw rA;
       for (int bi = 0; bi < nblk; ++bi) {
         load(rA, k0 + 32 * bi);
