@@ -146,6 +146,7 @@ CASES = [
     ai.PrefillCase("bwd_one_row_D128_Lk300", 66, B=2, Hq=8, Hkv=2, Lq=1, Lk=300, D=128),
     ai.PrefillCase("bwd_G8_D128_L640", 67, B=1, Hq=8, Hkv=1, Lq=640, Lk=640, D=128),
     ai.PrefillCase("bwd_full_G4_D64_Lq33_Lk70", 68, B=1, Hq=4, Hkv=1, Lq=33, Lk=70, D=64, causal=False),
+    ai.PrefillCase("bwd_full_G2_D128_Lq300_Lk50", 70, B=1, Hq=4, Hkv=2, Lq=300, Lk=50, D=128, causal=False),
 ]
 
 
