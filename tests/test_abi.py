@@ -220,3 +220,19 @@ def test_backward_validation_and_sizes(attn):
     assert need == 2 * ((64 * 4 * 4 + 255) // 256 * 256)
     assert bwd(ws=P, ws_bytes=need - 1) == -8
     assert attn.backward_workspace_bytes(0, 4, 64) == 0
+
+
+def test_package_without_library_fails_loudly(tmp_path):
+    """A copy of the package with no libattn.so must refuse to import: there
+    is no fallback path of any kind."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = os.path.join(ROOT, "exact_attention_30_amd")
+    dst = tmp_path / "exact_attention_30_amd"
+    shutil.copytree(pkg, dst, ignore=shutil.ignore_patterns("*.so", "_build", "__pycache__"))
+    assert not any(p.name.endswith(".so") for p in dst.iterdir())
+    r = subprocess.run([sys.executable, "-c", "import exact_attention_30_amd"], cwd=tmp_path,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "libattn.so is missing" in r.stderr
