@@ -34,7 +34,13 @@
 //    byte permutes, 16-byte LDS writes) so that O^T += V^T P^T runs on MFMA
 //    with P^T taken directly from the S^T accumulators.
 //  * The next 32-key block's K and V loads are issued before the current
-//    block is computed (two register sets), keeping 16 KiB per wave in flight.
+//    block is computed (two register sets, 16 KiB per wave in flight; one set
+//    for D = 256 or four query-column blocks, where a second would spill).
+//  * int8 caches (q8_0-style: one binary16 scale per 32-element block of a
+//    row, element = scale * code rounded to bf16): the same kernel with the
+//    codes loaded instead of bf16 rows, each block's scale rows in one load per
+//    lane handed out through LDS, and the codes turned into the bf16 MFMA
+//    operands in registers once they arrive.
 //  * Lazy max update as in the prefill kernel.
 //  * The combine kernel (one wave per query row) merges the partials of the
 //    segments that were split between waves.
@@ -105,8 +111,6 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a) {
   if (t == 1023) a.pre[a.B] = part[1023];
 }
 
-// One query-column block: two waves per SIMD (256 registers each); more
-// column blocks need the whole register file.
 // int8 -> bf16 for 8 codes (two dwords) of one 32-element block with scale s:
 // the codes are biased to unsigned bytes (xor 0x80), converted exactly, and
 // x = s * (u - 128) is rounded to bf16 (nearest even).
@@ -150,6 +154,8 @@ struct DecodeRaw<D, true> {
   uint32_t sc[SW];
 };
 
+// One query-column block: two waves per SIMD (256 registers each); more
+// column blocks need the whole register file.
 template <int D, int NCB, bool Q8>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2 : 1))) void decode_main_kernel(DecodeArgs a) {
   constexpr int KST = D / 32;            // 32-dim MFMA steps over the head dim
