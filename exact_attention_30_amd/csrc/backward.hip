@@ -15,17 +15,20 @@
 //    lse (one exp2 per element), as the forward never stored it.
 //  * dk/dv kernel: a wave owns 32 keys of one KV head and keeps their k and v
 //    rows as MFMA operands in registers; the workgroup (4 waves, 128 keys)
-//    walks the query tiles (32 rows) of all G query heads that read the KV
-//    head, staging q, dout, lse and delta in LDS.  Per tile and wave, four
+//    walks 64-row stages of all G query heads that read the KV head, moving
+//    q, dout, lse and delta straight from global memory into LDS (direct
+//    loads, three stages in flight).  Per 32-row half and wave, four
 //    v_mfma_f32_32x32x16_bf16 chains: S = Q K^T and dP = dO V^T (queries on
 //    M, keys on N), then dV^T += dO^T P and dK^T += Q^T dS, where P and dS
 //    come straight from the S / dP accumulators (a lane holds one key column)
-//    and dO^T, Q^T are read with ds_read_b64_tr_b16.  dk and dv of a KV head
-//    are complete in one workgroup: no atomics.
+//    and dO^T, Q^T are read with ds_read_b64_tr_b16.  The two halves of an
+//    unmasked stage are software-pipelined.  dk and dv of a KV head are
+//    complete in one workgroup: no atomics.
 //  * dq kernel: a wave owns 32 query rows (q and dout rows as operands in
-//    registers) and walks the key tiles (64 keys) in reach of its rows:
-//    S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T with K^T read
-//    transposed from the same LDS tile.
+//    registers) and walks the key tiles (64 keys, three in flight) in reach
+//    of its rows: S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T with K^T
+//    read transposed from the same LDS tile.
+//  * LDS operand reads are issued several MFMAs ahead of their use.
 //  * A tile that is read both row-wise (b128) and transposed (tr16) is stored
 //    with a 16-byte-chunk XOR swizzle that keeps both access patterns free of
 //    bank conflicts (tswz).
