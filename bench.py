@@ -231,9 +231,10 @@ def all_configs(iters: int):
         del q, k, v, out, lse
 
     # backward (dq, dk, dv from the forward's out and lse) at the Qwen3-8B
-    # shapes; work counted as 2.5 x the forward's (five matrix products over
-    # the visible pairs: QK^T, dO V^T, P^T dO, dS^T Q, dS K)
-    for pc in (ai.QWEN_4K, ai.QWEN_16K):
+    # shapes and the head-dim-256 shape; work counted as 2.5 x the forward's
+    # (five matrix products over the visible pairs: QK^T, dO V^T, P^T dO,
+    # dS^T Q, dS K)
+    for pc in (ai.QWEN_4K, ai.QWEN_16K, ai.D256):
         q, k, v = to_dev(pc.q_bits(), dev), to_dev(pc.k_bits(), dev), to_dev(pc.v_bits(), dev)
         g = to_dev(pc.dout_bits(), dev)
         out, lse = attn.prefill(q, k, v, causal=True, scale=pc.scale)

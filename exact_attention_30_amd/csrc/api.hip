@@ -321,7 +321,7 @@ int attn_backward(const void *q, const void *k, const void *v, const void *out, 
                   void *dq, void *dk, void *dv, int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, int window,
                   float scale, void *workspace, size_t workspace_bytes, void *stream) {
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_GQA;
-  if (D != 64 && D != 128) return ATTN_ERR_HEADDIM;
+  if (!head_dim_ok(D)) return ATTN_ERR_HEADDIM;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
   if (B < 0 || Lq < 0 || Lk < 0 || window < 0 || (window > 0 && !causal)) return ATTN_ERR_SHAPE;
   if (B == 0 || (Lq == 0 && Lk == 0)) return ATTN_OK;

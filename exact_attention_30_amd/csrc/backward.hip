@@ -117,6 +117,11 @@ ATTN_DEV void sched_interleave() {
 #ifndef ATTN_BWD_TR_AHEAD
 #define ATTN_BWD_TR_AHEAD 4
 #endif
+// D = 256 leaves fewer registers for reads in flight
+template <int D>
+constexpr int kQkAhead = D == 256 ? 2 : ATTN_BWD_QK_AHEAD;
+template <int D>
+constexpr int kTrAhead = D == 256 ? 1 : ATTN_BWD_TR_AHEAD;
 
 // ---------------------------------------------------------------------------
 // delta_i = <dout_i, out_i> (fp32), and lse_i * log2(e); one wave per row.
@@ -149,7 +154,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BackwardArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kBwdWaves = 4;
 constexpr int kBwdKeys = 32 * kBwdWaves;   // keys per dk/dv workgroup
-constexpr int kBwdRows = 64;               // query rows per stage of the dk/dv loop (two halves of 32)
+// query rows per stage of the dk/dv loop: two halves of 32 (D = 256: one half,
+// so that three stages fit in LDS)
+template <int D>
+constexpr int kBwdRows = D == 256 ? 32 : 64;
 
 
 // s_waitcnt vmcnt(n) for n < 16 (expcnt and lgkmcnt left alone)
@@ -167,7 +175,8 @@ ATTN_DEV void dma_to_lds(const void *g, void *lds) {
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void bwd_dkdv_kernel(BackwardArgs a) {
-  constexpr int TILE = kBwdRows * D;          // elements of a q (or dout) stage
+  constexpr int ROWS = kBwdRows<D>;
+  constexpr int TILE = ROWS * D;              // elements of a q (or dout) stage
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
   constexpr int RPB = 512 / D;                // rows per 1 KiB direct load
   constexpr int BPW = TILE * 2 / 1024 / kBwdWaves;   // 1 KiB blocks per wave per tensor and stage
@@ -181,9 +190,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   __shared__ __attribute__((aligned(1024))) uint16_t da[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t db_[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t dc[TILE];
-  __shared__ __attribute__((aligned(256))) float sa[2 * kBwdRows];
-  __shared__ __attribute__((aligned(256))) float sb[2 * kBwdRows];
-  __shared__ __attribute__((aligned(256))) float sc_[2 * kBwdRows];
+  __shared__ __attribute__((aligned(256))) float sa[2 * ROWS];
+  __shared__ __attribute__((aligned(256))) float sb[2 * ROWS];
+  __shared__ __attribute__((aligned(256))) float sc_[2 * ROWS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -225,7 +234,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
     if (win) qhi = min(a.Lq, j0 + kBwdKeys - 1 - off + win);
   }
   qlo = qlo / 32 * 32;
-  const int ntile_h = qhi > qlo ? (qhi - qlo + kBwdRows - 1) / kBwdRows : 0;
+  const int ntile_h = qhi > qlo ? (qhi - qlo + ROWS - 1) / ROWS : 0;
   const int ntile = ntile_h * a.G;
 
   // per-lane LDS offsets: b128 operand (row ql, chunk 2 ks + hh) and the
@@ -252,7 +261,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
     dv[i] = f32x16{};
   }
 
-  // Stage tile tt (head, 64 rows) straight from global memory into LDS: each
+  // Stage tile tt (head, ROWS rows) straight from global memory into LDS: each
   // wave moves BPW blocks of 1 KiB of q and of dout (lane i fills bytes
   // [16 i, 16 i + 16) of a block, so it fetches the logical chunk that the
   // swizzle puts there; rows past the end are read from the last row and
@@ -261,7 +270,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   // 0 and 1).
   auto issue = [&](int tt, uint16_t *qd, uint16_t *dd, float *sd) __attribute__((always_inline)) {
     const int hq = hkv * a.G + tt / ntile_h;
-    const int i0 = qlo + (tt % ntile_h) * kBwdRows;
+    const int i0 = qlo + (tt % ntile_h) * ROWS;
     const size_t rowbase = ((size_t)b * a.Hq + hq) * a.Lq;
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
@@ -273,9 +282,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
       dma_to_lds<16>(a.dout + grow * D + 8 * c, dd + blk * 512);
     }
     if (wu < 2) {
+      // one float per lane (ROWS lanes)
       const float *src = wu == 0 ? a.lse2 : a.delta;
       const size_t grow = rowbase + min(i0 + lane, a.Lq - 1);
-      dma_to_lds<4>(src + grow, sd + 64 * wu);
+      if (ROWS == 64 || lane < ROWS) dma_to_lds<4>(src + grow, sd + ROWS * wu);
     }
   };
   auto wait_tile = [&](bool younger) __attribute__((always_inline)) {
@@ -324,7 +334,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
         pe = vis ? pe : 0.f;
       }
       pv[rr] = pe;
-      dsv[rr] = pe * (dp[rr] - st[kBwdRows + 32 * rb + r]);
+      dsv[rr] = pe * (dp[rr] - st[ROWS + 32 * rb + r]);
     }
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
@@ -356,11 +366,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
     dt += rb * 32 * D;
     f32x16 s, dp;
     sdp(qt, dt, s, dp);
-    sched_reads_ahead<2 * (D / 16), 1, ATTN_BWD_QK_AHEAD>();
+    sched_reads_ahead<2 * (D / 16), 1, kQkAhead<D>>();
     bf16x8 pb[2], sb2[2];
     soft(st, rb, i0h, s, dp, pb, sb2, cross_half(i0h));
     upd(qt, dt, pb, sb2);
-    sched_reads_ahead<4 * (D / 32), 2, ATTN_BWD_TR_AHEAD>();
+    sched_reads_ahead<4 * (D / 32), 2, kTrAhead<D>>();
   };
   // both halves, neither masked: software-pipelined so that the exponentials
   // of one half run beside the MFMAs of the other
@@ -369,23 +379,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
     f32x16 s0, dp0, s1, dp1;
     bf16x8 pb0[2], sb0[2], pb1[2], sb1[2];
     sdp(qt, dt, s0, dp0);
-    sched_reads_ahead<2 * (D / 16), 1, ATTN_BWD_QK_AHEAD>();
+    sched_reads_ahead<2 * (D / 16), 1, kQkAhead<D>>();
     sdp(qt + 32 * D, dt + 32 * D, s1, dp1);
     soft(st, 0, i0, s0, dp0, pb0, sb0, m0);
-    sched_interleave<2 * (D / 16), 1, ATTN_BWD_QK_AHEAD, ATTN_BWD_VALU_PER>();
+    sched_interleave<2 * (D / 16), 1, kQkAhead<D>, ATTN_BWD_VALU_PER>();
     upd(qt, dt, pb0, sb0);
     soft(st, 1, i0 + 32, s1, dp1, pb1, sb1, m1);
-    sched_interleave<4 * (D / 32), 2, ATTN_BWD_TR_AHEAD, ATTN_BWD_VALU_PER>();
+    sched_interleave<4 * (D / 32), 2, kTrAhead<D>, ATTN_BWD_VALU_PER>();
     upd(qt + 32 * D, dt + 32 * D, pb1, sb1);
-    sched_reads_ahead<4 * (D / 32), 2, ATTN_BWD_TR_AHEAD>();
+    sched_reads_ahead<4 * (D / 32), 2, kTrAhead<D>>();
   };
   auto step = [&](int tt, const uint16_t *qt, const uint16_t *dt, const float *st, uint16_t *qn, uint16_t *dn,
                   float *sn) __attribute__((always_inline)) {
     wait_tile(tt + 1 < ntile);
     __syncthreads();
     if (tt + 2 < ntile) issue(tt + 2, qn, dn, sn);
-    const int i0 = qlo + (tt % ntile_h) * kBwdRows;
-    if (ATTN_BWD_PIPE && !skip_half(i0) && !skip_half(i0 + 32) && !cross_half(i0) && !cross_half(i0 + 32)) {
+    const int i0 = qlo + (tt % ntile_h) * ROWS;
+    if constexpr (ROWS == 32) {
+      half(qt, dt, st, i0, 0);
+    } else if (ATTN_BWD_PIPE && !skip_half(i0) && !skip_half(i0 + 32) && !cross_half(i0) && !cross_half(i0 + 32)) {
       both(qt, dt, st, i0, false, false);
     } else {
       half(qt, dt, st, i0, 0);
@@ -434,12 +446,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
 // ---------------------------------------------------------------------------
 // dq
 // ---------------------------------------------------------------------------
-constexpr int kBwdQKeys = 64;   // keys per tile of the dq loop
+// keys per tile of the dq loop (D = 256: 32, so that three tiles fit in LDS)
+template <int D>
+constexpr int kBwdQKeys = D == 256 ? 32 : 64;
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void bwd_dq_kernel(BackwardArgs a) {
   constexpr int CPR = D / 8;
-  constexpr int BK = kBwdQKeys;
+  constexpr int BK = kBwdQKeys<D>;
   constexpr int TILE = BK * D;
   constexpr int RPB = 512 / D;                       // rows per 1 KiB direct load
   constexpr int BPW = TILE * 2 / 1024 / kBwdWaves;   // 1 KiB blocks per wave per tensor and tile
@@ -562,7 +576,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
                                                          dp[rb], 0, 0, 0);
       }
     }
-    sched_reads_ahead<2 * (BK / 32) * (D / 16), 1, ATTN_BWD_QK_AHEAD>();
+    sched_reads_ahead<2 * (BK / 32) * (D / 16), 1, kQkAhead<D>>();
     // this lane: query row qrow, keys k0 + 32 rb + 8 (rr >> 2) + 4 hh + (rr & 3)
     const bool crosses = k0 + BK > kfull || k0 < klo_until;
     const int lim = a.causal ? qrow + off : a.Lk - 1;
@@ -590,7 +604,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
       for (int kc2 = 0; kc2 < BK / 16; ++kc2)
         dq[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             tr_operand(kt + 16 * kc2 * D + tlo[dd], kt + 16 * kc2 * D + thi[dd]), sb[kc2], dq[dd], 0, 0, 0);
-    sched_reads_ahead<(D / 32) * (BK / 16), 2, ATTN_BWD_TR_AHEAD>();
+    sched_reads_ahead<(D / 32) * (BK / 16), 2, kTrAhead<D>>();
   };
   auto step = [&](int jj, const uint16_t *kt, const uint16_t *vt, uint16_t *kn, uint16_t *vn)
       __attribute__((always_inline)) {
@@ -655,6 +669,7 @@ hipError_t launch_backward(const BackwardArgs &a, int D, hipStream_t s) {
   switch (D) {
     case 64: return launch_bwd_t<64>(a, s);
     case 128: return launch_bwd_t<128>(a, s);
+    case 256: return launch_bwd_t<256>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

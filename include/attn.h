@@ -68,7 +68,7 @@ typedef enum {
   ATTN_ERR_SHAPE = -2,    /* a negative size, Lk = 0 with Lq > 0, causal with Lq > Lk,
                              Lmax < 1, T outside 1..Lmax, or a size whose element count
                              overflows */
-  ATTN_ERR_HEADDIM = -3,  /* D not in {64, 128, 256} (attn_backward: not in {64, 128}) */
+  ATTN_ERR_HEADDIM = -3,  /* D not in {64, 128, 256} */
   ATTN_ERR_GQA = -4,      /* Hq < 1, Hkv < 1 or Hq % Hkv != 0 */
   ATTN_ERR_SCALE = -5,    /* scale is NaN or infinite */
   ATTN_ERR_HIP = -6,      /* a HIP call or kernel launch failed */
@@ -290,7 +290,7 @@ int attn_decode_waves(int B, int Hq, int Hkv, int Lmax, int D, int split_keys);
  *   k, v, dk, dv      [B][Hkv][Lk][D] bf16
  *
  * causal and window as attn_prefill_ex (the same mask must be given as in
- * the forward call that produced out and lse).  D must be 64 or 128 (else
+ * the forward call that produced out and lse).  D is 64, 128 or 256 (else
  * ATTN_ERR_HEADDIM).  Every row must see a key: Lk = 0 with Lq > 0, Lq = 0
  * with Lk > 0 and causal with Lq > Lk are ATTN_ERR_SHAPE; B = 0 or
  * Lq = Lk = 0 is an empty call (ATTN_OK, nothing touched, pointers may be

@@ -205,8 +205,8 @@ def test_backward_validation_and_sizes(attn):
         return attn.lib.attn_backward(q, P, P, P, P, P, P, P, P, B, Hq, Hkv, Lq, Lk, D, causal, window,
                                       ctypes.c_float(scale), ws, ws_bytes, None)
     assert bwd(Hq=3) == -4
-    assert bwd(D=256) == -3            # backward covers head dims 64 and 128
     assert bwd(D=96) == -3
+    assert bwd(D=32) == -3
     assert bwd(scale=math.inf) == -5
     assert bwd(Lq=65, Lk=64) == -2      # causal rows past the keys
     assert bwd(Lq=0, Lk=5) == -2

@@ -147,6 +147,8 @@ CASES = [
     ai.PrefillCase("bwd_G8_D128_L640", 67, B=1, Hq=8, Hkv=1, Lq=640, Lk=640, D=128),
     ai.PrefillCase("bwd_full_G4_D64_Lq33_Lk70", 68, B=1, Hq=4, Hkv=1, Lq=33, Lk=70, D=64, causal=False),
     ai.PrefillCase("bwd_full_G2_D128_Lq300_Lk50", 70, B=1, Hq=4, Hkv=2, Lq=300, Lk=50, D=128, causal=False),
+    ai.PrefillCase("bwd_G2_D256_Lq150_Lk260", 71, B=1, Hq=4, Hkv=2, Lq=150, Lk=260, D=256),
+    ai.PrefillCase("bwd_full_G1_D256_L70", 72, B=2, Hq=2, Hkv=2, Lq=70, Lk=70, D=256, causal=False),
 ]
 
 
@@ -155,7 +157,7 @@ def test_backward_parity(attn, case):
     run(attn, case)
 
 
-@pytest.mark.parametrize("window,idx", [(1, 0), (100, 1), (37, 3), (64, 6), (1000, 6)])
+@pytest.mark.parametrize("window,idx", [(1, 0), (100, 1), (37, 3), (64, 6), (1000, 6), (40, 9)])
 def test_backward_window(attn, window, idx):
     run(attn, CASES[idx], window=window)
 
