@@ -10,32 +10,40 @@
 // быстрее…", section on group size (G query heads read one KV head).
 //
 // gfx950 design
-//  * One workgroup = 8 wave64s (two per SIMD) = 256 query rows of up to 8
-//    query heads that share one KV head; every K/V tile it stages in LDS
-//    serves all of them (256 FLOP per byte staged).
-//  * Each wave owns 32 query rows and computes the transposed score block
-//    S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys on the M side, queries on
-//    the N side).  In the accumulator layout a lane holds one query column and
+//  * A workgroup of 8 wave64s (D = 256: 4, one per SIMD, for registers) covers
+//    32 query rows per wave of up to 8 query heads that share one KV head;
+//    every K/V tile it stages in LDS serves all of them.
+//  * Each wave computes the transposed score block S^T = K Q^T with
+//    v_mfma_f32_32x32x16_bf16 (keys on the M side, queries on the N side, Q in
+//    registers).  In the accumulator layout a lane holds one query column and
 //    16 keys per 32-key block, so the row max and row sum are lane-local plus
 //    one v_permlane32_swap between the two wave halves.
 //  * P^T (bf16, round to nearest even) feeds O^T += V^T P^T straight from
 //    those registers.  V stays row-major in LDS; its V^T operand is read with
 //    ds_read_b64_tr_b16 (a 4 x 16 transpose per 16-lane group), two reads per
 //    MFMA, in the key order the P^T registers hold.
-//  * LDS rows are padded (K: 16 B, V: 64 B) so that the b128 K reads and the
-//    transposing V reads hit all 64 banks without conflicts.  Tiles are
-//    staged through registers and double-buffered: the next tile's global
-//    loads are in flight while the current tile is computed.
+//  * Tiles move HBM -> LDS with global_load_lds_dwordx4 (no registers, no
+//    ds_write).  Rows are unpadded; a row's 16-byte chunks are XOR-swizzled so
+//    that the b128 K reads and the transposing V reads are free of bank
+//    conflicts.  K and V are double-buffered in four separate LDS arrays.
 //  * Softmax in the log2 domain: p = exp2(s*c - m) with c = scale*log2(e);
 //    the running maximum is raised lazily (ATTN_RESCALE_SLACK), so the O
 //    rescale is skipped on almost every tile.  The row sum adds the fp32
 //    exponentials (before their rounding to bf16), so that the log-sum-exp
 //    is that of the true normaliser.
-//  * Causal: tiles past a wave's last visible key are skipped, the mask is
-//    evaluated only on tiles that cross the diagonal or the end of the keys.
-//    Workgroups are issued heaviest first, and consecutive workgroup ids are
-//    spread over the 8 XCDs so that each XCD works on one KV head at a time
-//    (its K/V stay in that XCD's L2).
+//  * Two schedules.  prefill_kernel pairs the waves of a SIMD in two groups
+//    that alternate matrix work and softmax (one group's exponentials run
+//    beside the other group's MFMAs).  prefill_iw_kernel runs one schedule in
+//    every wave and interleaves each wave's own exponentials and row sums
+//    with its own MFMAs (sched_group_barrier); it is the faster one for
+//    D = 64 and for D = 256 (one wave per SIMD), the ping-pong for D = 128.
+//  * Causal: tiles past the workgroup's last visible key are skipped, the
+//    mask is evaluated only on tiles that cross the diagonal, the end of the
+//    keys or a window's lower edge.  Workgroups are issued heaviest first, and
+//    consecutive workgroup ids are spread over the 8 XCDs so that each XCD
+//    works on one KV head at a time (its K/V stay in that XCD's L2).
+//  * Small grids split each query block's keys over several workgroups and
+//    merge the partial results with their log-sum-exps (combine kernel).
 #include <type_traits>
 
 #include "common.h"
@@ -63,6 +71,25 @@
 #endif
 #ifndef ATTN_PF_ADMA
 #define ATTN_PF_ADMA 0
+#endif
+//  ATTN_PF_IW           head dims that use prefill_iw_kernel (in-wave pipelined)
+//                       rather than the two-group ping-pong prefill_kernel, as a
+//                       bit mask: 1 = D 64, 2 = D 128, 4 = D 256
+//  ATTN_PF_IW_V1/V2     vector instructions placed after each MFMA of bracket 1 / 2
+#ifndef ATTN_PF_IW
+#define ATTN_PF_IW 5
+#endif
+#ifndef ATTN_PF_IW_V1
+#define ATTN_PF_IW_V1 5
+#endif
+#ifndef ATTN_PF_IW_V2
+#define ATTN_PF_IW_V2 2
+#endif
+//  ATTN_PF_ORDER        1: consecutive MFMAs share their B operand (Q^T in S^T,
+//                       P^T in O^T), so one operand of the matrix core stays
+//                       unchanged across them
+#ifndef ATTN_PF_ORDER
+#define ATTN_PF_ORDER 0
 #endif
 //  ATTN_PF_BK128        key-tile size for D = 128
 #ifndef ATTN_PF_BK128
@@ -233,15 +260,14 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
   // transposing reads
   auto pv = [&](const uint16_t *vs_) __attribute__((always_inline)) {
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-      for (int kb = 0; kb < BK / 16; ++kb) {
-        const uint16_t *vp = vs_ + 16 * kb * D + voff(db);
-        const bf16x4 lo = lds_tr16(vp);
-        const bf16x4 hi = lds_tr16(vp + 8 * D);
-        const bf16x8 vop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[kb], o[db], 0, 0, 0);
-      }
+    for (int i = 0; i < (D / 32) * (BK / 16); ++i) {
+      const int db = ATTN_PF_ORDER ? i % (D / 32) : i / (BK / 16);
+      const int kb = ATTN_PF_ORDER ? i / (D / 32) : i % (BK / 16);
+      const uint16_t *vp = vs_ + 16 * kb * D + voff(db);
+      const bf16x4 lo = lds_tr16(vp);
+      const bf16x4 hi = lds_tr16(vp + 8 * D);
+      const bf16x8 vop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[kb], o[db], 0, 0, 0);
     }
     // keep the transposing reads ATTN_PF_PV_AHEAD MFMAs ahead of their use
     constexpr int N = (D / 32) * (BK / 16);
@@ -341,12 +367,13 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
     if (!ATTN_PF_QKFIRST && active(jj - 1)) pv(vs_);
     if (active(jj)) {
 #pragma unroll
-      for (int rb = 0; rb < BK / 32; ++rb) {
-        s[rb] = f32x16{};
+      for (int rb = 0; rb < BK / 32; ++rb) s[rb] = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-          s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(ks_ + 32 * rb * D + koff(ks))), qf[ks],
-                                                          s[rb], 0, 0, 0);
+      for (int i = 0; i < (BK / 32) * (D / 16); ++i) {
+        const int rb = ATTN_PF_ORDER ? i % (BK / 32) : i / (D / 16);
+        const int ks = ATTN_PF_ORDER ? i / (BK / 32) : i % (D / 16);
+        s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(ks_ + 32 * rb * D + koff(ks))), qf[ks], s[rb],
+                                                        0, 0, 0);
       }
       // K operand reads ATTN_PF_QK_AHEAD MFMAs ahead of their use
       constexpr int N = (BK / 32) * (D / 16);
@@ -460,6 +487,314 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
   }
 }
 
+// In-wave pipelined variant.  Every wave runs the same schedule; per tile j
+// (keys of tile j in S^T registers `cur`):
+//   barrier; direct loads of K(j+2) and V(j+1) into the buffers freed by the
+//   barrier; mask and tile maximum of tile j, running-max raise;
+//   bracket 1: MFMA  S^T(j+1) = K(j+1) Q^T             VALU  P(j) = exp2(S c - m)
+//   bracket 2: MFMA  O^T += V(j)^T P(j)^T               VALU  row sum of P(j)
+// Within a bracket the matrix and vector work are independent, and
+// sched_group_barrier interleaves them, so the exponentials run while the
+// matrix core works on the same wave's products; the second wave of the SIMD
+// fills what is left.  K(t) sits in kb[t % 2], V(t) in vb[t % 2].
+template <int D, int BK>
+__global__ __launch_bounds__(kPfThreads<D>) void prefill_iw_kernel(PrefillArgs a) {
+  using C = PrefillCfg<D, BK>;
+  __shared__ __attribute__((aligned(1024))) uint16_t kb0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t kb1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t vb0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t vb1[C::TILE];
+
+  // ---- which tile: XCD-grouped, heaviest q-block first -------------------
+  const int bid = blockIdx.x;
+  int t = bid;
+  const int tf = a.total & ~7;
+  if (bid < tf) t = (bid & 7) * (tf >> 3) + (bid >> 3);
+  const int sp = t % a.nsplit;
+  t /= a.nsplit;
+  int unit = t / a.n_qblk;
+  const int r = t - unit * a.n_qblk;
+  const int qblk = a.causal ? (a.n_qblk - 1 - r) : r;
+  const int hg = unit % a.n_hg;
+  unit /= a.n_hg;
+  const int hkv = unit % a.Hkv;
+  const int b = unit / a.Hkv;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int ql = lane & 31, hh = lane >> 5;
+  const int head = hkv * a.G + hg * a.hpw + w / a.wph;
+  const int q0w = qblk * a.Bq + (w % a.wph) * 32;
+  const int qrow = q0w + ql;
+  const int off = a.Lk - a.Lq;
+
+  const int qlast_wg = min(qblk * a.Bq + a.Bq, a.Lq) - 1;
+  const int kend_wg = a.causal ? min(a.Lk, qlast_wg + off + 1) : a.Lk;
+  const int kmask_from = a.causal ? min(a.Lk, q0w + off + 1) : a.Lk;
+  const int win = a.window;
+  const int kbeg_wg = win ? max(0, qblk * a.Bq + off - win + 1) : 0;
+  const int klo_until = win ? q0w + 31 + off - win + 1 : 0;
+  const int qlo = win ? qrow + off - win + 1 : -0x7fffffff;
+  const int jbeg = kbeg_wg / BK;
+  const int nt_all = (kend_wg + BK - 1) / BK - jbeg;
+  const int j0 = jbeg + (int)((long long)nt_all * sp / a.nsplit);
+  const int nt = jbeg + (int)((long long)nt_all * (sp + 1) / a.nsplit) - j0;
+
+  const int qr = min(qrow, a.Lq - 1);
+  const uint16_t *qp = a.q + (((size_t)b * a.Hq + head) * a.Lq + qr) * D;
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) qf[ks] = as_bf16x8(ld16(qp + 16 * ks + 8 * hh));
+
+  const size_t kvoff = ((size_t)b * a.Hkv + hkv) * (size_t)a.Lk * D;
+  const uint16_t *kg = a.k + kvoff;
+  const uint16_t *vg = a.v + kvoff;
+
+  // tile j of K or V into LDS: every wave moves DPW blocks of 1 KiB
+  auto dma = [&](const uint16_t *g, uint16_t *dst, int j, auto is_v) __attribute__((always_inline)) {
+    constexpr bool V = decltype(is_v)::value;
+#pragma unroll
+    for (int i = 0; i < C::DPW; ++i) {
+      const int blk = wu * C::DPW + i;
+      const int row = blk * C::RPD + lane / C::CPR;
+      const int c = (lane % C::CPR) ^ (V ? vswz<D>(row) : kswz<D>(row));
+      const int grow = min(j * BK + row, a.Lk - 1);
+      __builtin_amdgcn_global_load_lds((glb_void_t *)(g + (size_t)grow * D + 8 * c),
+                                       (lds_void_t *)(dst + blk * 512), 16, 0, 0);
+    }
+  };
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
+  // The running maximum starts at the lowest finite float, not -inf, so that
+  // a tile whose scores are all hidden gives exp2(-inf - m) = 0 rather than
+  // NaN: every tile of the workgroup's range goes through the same steps,
+  // and one a row does not see contributes exactly zero.  The first visible
+  // score raises it (any finite value exceeds it).
+  float m_run = -3.40282347e38f;
+  float l_run = 0.f;
+  // A hidden score is -inf (c > 0) or +inf (c < 0), so exp2(s c - m) is
+  // exactly 0 for it with no select.  c = 0 would give 0 * inf = NaN; the
+  // smallest normal float stands in for it: every visible weight
+  // exp2(s c - m) still rounds to exactly 1.
+  const float cexp = a.c == 0.f ? 1.17549435e-38f : a.c;
+  const bool cpos = cexp >= 0.f;
+  const float maskval = cpos ? -__builtin_inff() : __builtin_inff();
+
+  const int g16 = lane >> 4, j16 = lane & 15;
+  constexpr int NKO = D / 16 < 8 ? D / 16 : 8;
+  constexpr int NVO = D / 32 < 4 ? D / 32 : 4;
+  int koffs[NKO];
+#pragma unroll
+  for (int ks = 0; ks < NKO; ++ks) koffs[ks] = ql * D + 8 * ((2 * ks + hh) ^ kswz<D>(ql));
+  int voffs[NVO];
+  {
+    const int vr = 4 * hh + (j16 >> 2);
+    const int tv = vswz<D>(vr) >> 2;
+    const int cin = 2 * (g16 & 1) + ((j16 & 3) >> 1);
+#pragma unroll
+    for (int db = 0; db < NVO; ++db) voffs[db] = vr * D + 8 * (4 * (db ^ tv) + cin) + 4 * (j16 & 1);
+  }
+  auto koff = [&](int ks) __attribute__((always_inline)) { return koffs[ks % NKO] + (ks / NKO) * 128; };
+  auto voff = [&](int db) __attribute__((always_inline)) { return voffs[db % NVO] + (db / NVO) * 128; };
+
+  bf16x8 pb[BK / 16];
+  constexpr int NQK = (BK / 32) * (D / 16);  // MFMAs of S^T per tile
+  constexpr int NPV = (D / 32) * (BK / 16);  // MFMAs of O^T per tile
+
+  auto qk_ops = [&](f32x16(&s)[BK / 32], const uint16_t *ks_) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < BK / 32; ++rb) s[rb] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < (BK / 32) * (D / 16); ++i) {
+      const int rb = ATTN_PF_ORDER ? i % (BK / 32) : i / (D / 16);
+      const int ks = ATTN_PF_ORDER ? i / (BK / 32) : i % (D / 16);
+      s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(ks_ + 32 * rb * D + koff(ks))), qf[ks], s[rb],
+                                                      0, 0, 0);
+    }
+  };
+  auto pv_ops = [&](const uint16_t *vs_) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < (D / 32) * (BK / 16); ++i) {
+      const int db = ATTN_PF_ORDER ? i % (D / 32) : i / (BK / 16);
+      const int kb = ATTN_PF_ORDER ? i / (D / 32) : i % (BK / 16);
+      const uint16_t *vp = vs_ + 16 * kb * D + voff(db);
+      const bf16x4 lo = lds_tr16(vp);
+      const bf16x4 hi = lds_tr16(vp + 8 * D);
+      const bf16x8 vop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[kb], o[db], 0, 0, 0);
+    }
+  };
+  // P = exp2(s c - m) in place (s keeps the fp32 values for the row sum), packed to bf16 in pb
+  auto expo = [&](f32x16(&s)[BK / 32]) __attribute__((always_inline)) {
+    const float nm = -m_run;
+#pragma unroll
+    for (int rb = 0; rb < BK / 32; ++rb) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) s[rb][rr] = fast_exp2(__builtin_fmaf(s[rb][rr], cexp, nm));
+      pb[2 * rb] = pack8(s[rb][0], s[rb][1], s[rb][2], s[rb][3], s[rb][4], s[rb][5], s[rb][6], s[rb][7]);
+      pb[2 * rb + 1] = pack8(s[rb][8], s[rb][9], s[rb][10], s[rb][11], s[rb][12], s[rb][13], s[rb][14], s[rb][15]);
+    }
+  };
+  auto rsum = [&](const f32x16(&s)[BK / 32]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < BK / 32; ++rb) {
+      float t8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t8[i] = s[rb][i] + s[rb][i + 8];
+      l_run += ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
+    }
+  };
+  // hidden scores of tile j set to maskval (tiles that cross the diagonal, the
+  // end of the keys or the window's lower edge)
+  auto mask_tile = [&](f32x16(&s)[BK / 32], int jj) __attribute__((always_inline)) {
+    const int k0 = (j0 + jj) * BK;
+    if (!(k0 + BK > kmask_from || k0 < klo_until)) return;
+    const int lim = a.causal ? min(a.Lk - 1, qrow + off) : a.Lk - 1;
+#pragma unroll
+    for (int rb = 0; rb < BK / 32; ++rb)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int key = k0 + 32 * rb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+        s[rb][rr] = (key <= lim && key >= qlo) ? s[rb][rr] : maskval;
+      }
+  };
+  // raise the running maximum to the tile's if it exceeds it by more than the slack
+  auto raise = [&](const f32x16(&s)[BK / 32]) __attribute__((always_inline)) {
+    float red;
+    if (cpos) {
+      red = s[0][0];
+#pragma unroll
+      for (int rb = 0; rb < BK / 32; ++rb)
+#pragma unroll
+        for (int g = 0; g < 16; g += 2) {
+          if (rb == 0 && g == 0) red = __builtin_fmaxf(s[0][0], s[0][1]);
+          else red = fmax3(red, s[rb][g], s[rb][g + 1]);
+        }
+      red = pair_max(red);
+    } else {
+      red = s[0][0];
+#pragma unroll
+      for (int rb = 0; rb < BK / 32; ++rb)
+#pragma unroll
+        for (int g = 0; g < 16; g += 2) {
+          if (rb == 0 && g == 0) red = __builtin_fminf(s[0][0], s[0][1]);
+          else red = fmin3(red, s[rb][g], s[rb][g + 1]);
+        }
+      red = pair_min(red);
+    }
+    const float mt = red * cexp;
+    const bool need = mt > m_run + ATTN_RESCALE_SLACK;
+    if (wave_any(need)) {
+      const float mnew = need ? mt : m_run;
+      const float alpha = need ? fast_exp2(m_run - mnew) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+      m_run = mnew;
+    }
+  };
+
+  // interleave orders: K reads ATTN_PF_QK_AHEAD ahead, V^T reads ATTN_PF_PV_AHEAD ahead
+  auto sched_b1 = [&]() __attribute__((always_inline)) {
+    constexpr int A = ATTN_PF_QK_AHEAD;
+    __builtin_amdgcn_sched_group_barrier(0x100, A, 0);
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, ATTN_PF_IW_V1, 0);
+      if (i < NQK - A) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  auto sched_b2 = [&]() __attribute__((always_inline)) {
+    constexpr int A = ATTN_PF_PV_AHEAD;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * A, 0);
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, ATTN_PF_IW_V2, 0);
+      if (i < NPV - A) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  };
+
+  // one tile: see the comment above the kernel
+  auto iter = [&](int j, auto parity, f32x16(&cur)[BK / 32], f32x16(&nxt)[BK / 32]) __attribute__((always_inline)) {
+    constexpr int P = decltype(parity)::value;
+    uint16_t *kread = P ? kb0 : kb1;  // K(j+1)
+    uint16_t *kfill = P ? kb1 : kb0;  // K(j+2)
+    uint16_t *vread = P ? vb1 : vb0;  // V(j)
+    uint16_t *vfill = P ? vb0 : vb1;  // V(j+1)
+    ATTN_WAIT_VMEM();
+    __syncthreads();
+    if (j + 2 < nt) dma(kg, kfill, j0 + j + 2, std::false_type{});
+    if (j + 1 < nt) dma(vg, vfill, j0 + j + 1, std::true_type{});
+    mask_tile(cur, j);
+    raise(cur);
+    // bracket 1: exponentials of tile j beside the products of tile j+1 (past
+    // the last tile those products are not used)
+    expo(cur);
+    qk_ops(nxt, kread);
+    sched_b1();
+    __builtin_amdgcn_sched_barrier(0);
+    // bracket 2: P.V of tile j beside its row sums
+    pv_ops(vread);
+    rsum(cur);
+    sched_b2();
+  };
+
+  f32x16 sa[BK / 32], sb[BK / 32];
+  if (nt > 0) {
+    dma(kg, kb0, j0, std::false_type{});
+    dma(vg, vb0, j0, std::true_type{});
+    if (nt > 1) dma(kg, kb1, j0 + 1, std::false_type{});
+  }
+  ATTN_WAIT_VMEM();
+  __syncthreads();
+  qk_ops(sa, kb0);
+  for (int j = 0; j < nt; j += 2) {
+    iter(j, std::integral_constant<int, 0>{}, sa, sb);
+    if (j + 1 >= nt) break;
+    iter(j + 1, std::integral_constant<int, 1>{}, sb, sa);
+  }
+
+  // ---- epilogue: out = O / l, lse = m ln2 + ln l -------------------------
+  const float lt = pair_sum(l_run);
+  if (qrow < a.Lq && a.nsplit == 1) {
+    const float inv = 1.f / lt;
+    uint16_t *op = a.out + (((size_t)b * a.Hq + head) * a.Lq + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4 v4;
+        v4[0] = (__bf16)(o[db][4 * g4 + 0] * inv);
+        v4[1] = (__bf16)(o[db][4 * g4 + 1] * inv);
+        v4[2] = (__bf16)(o[db][4 * g4 + 2] * inv);
+        v4[3] = (__bf16)(o[db][4 * g4 + 3] * inv);
+        *reinterpret_cast<bf16x4 *>(op + 32 * db + 8 * g4 + 4 * hh) = v4;
+      }
+    }
+    if (a.lse != nullptr && hh == 0)
+      a.lse[((size_t)b * a.Hq + head) * a.Lq + qrow] = m_run * ATTN_LN2 + __logf(lt);
+  } else if (qrow < a.Lq) {
+    const size_t row = ((size_t)b * a.Hq + head) * a.Lq + qrow;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    float *po = a.part_o + (row * a.nsplit + sp) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 v4 = {o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv, o[db][4 * g4 + 2] * inv,
+                          o[db][4 * g4 + 3] * inv};
+        *reinterpret_cast<f32x4 *>(po + 32 * db + 8 * g4 + 4 * hh) = v4;
+      }
+    }
+    if (hh == 0) a.part_lse[row * a.nsplit + sp] = lt > 0.f ? m_run * ATTN_LN2 + __logf(lt) : -__builtin_inff();
+  }
+}
+
 // Merge of the key ranges of one query row (one wave per row, nsplit <= 64):
 // lse = log sum_s exp(lse_s), out = sum_s exp(lse_s - lse) out_s.  This is the
 // softmax sum split over disjoint key sets.
@@ -501,7 +836,10 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a, lon
 
 template <int D, int BK>
 static hipError_t launch_t(const PrefillArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((prefill_kernel<D, BK>), dim3(a.total), dim3(PrefillCfg<D, BK>::NT), 0, s, a);
+  if (ATTN_PF_IW & (D == 64 ? 1 : D == 128 ? 2 : 4))
+    hipLaunchKernelGGL((prefill_iw_kernel<D, BK>), dim3(a.total), dim3(PrefillCfg<D, BK>::NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, BK>), dim3(a.total), dim3(PrefillCfg<D, BK>::NT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   const long long rows = (long long)a.B * a.Hq * a.Lq;
