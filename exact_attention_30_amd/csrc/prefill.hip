@@ -79,6 +79,11 @@
 #ifndef ATTN_PF_IW
 #define ATTN_PF_IW 5
 #endif
+//  ATTN_PF_IW_SPREAD    head dims (bit mask as above) for which prefill_iw_kernel
+//                       spreads its direct loads over the MFMAs
+#ifndef ATTN_PF_IW_SPREAD
+#define ATTN_PF_IW_SPREAD 4
+#endif
 #ifndef ATTN_PF_IW_V1
 #define ATTN_PF_IW_V1 5
 #endif
@@ -697,7 +702,13 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_iw_kernel(PrefillArgs a
     }
   };
 
-  // interleave orders: K reads ATTN_PF_QK_AHEAD ahead, V^T reads ATTN_PF_PV_AHEAD ahead
+  // interleave orders: K reads ATTN_PF_QK_AHEAD ahead, V^T reads ATTN_PF_PV_AHEAD ahead;
+  // bracket 1 also carries the direct loads of the next tiles, one every SP
+  // MFMAs (a direct load holds its wave until the CU's address unit takes it,
+  // about 1 KiB per 16 cycles per CU, so loads issued together stall every wave)
+  constexpr bool SPREAD = (ATTN_PF_IW_SPREAD & (D == 64 ? 1 : D == 128 ? 2 : 4)) != 0;
+  constexpr int NLD = SPREAD ? 2 * C::DPW : 0;
+  constexpr int SP = NLD ? (NQK / NLD > 0 ? NQK / NLD : 1) : 1;
   auto sched_b1 = [&]() __attribute__((always_inline)) {
     constexpr int A = ATTN_PF_QK_AHEAD;
     __builtin_amdgcn_sched_group_barrier(0x100, A, 0);
@@ -705,6 +716,7 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_iw_kernel(PrefillArgs a
     for (int i = 0; i < NQK; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x402, ATTN_PF_IW_V1, 0);
+      if (NLD && i % SP == 0 && i / SP < NLD) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
       if (i < NQK - A) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
@@ -728,14 +740,21 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_iw_kernel(PrefillArgs a
     uint16_t *vfill = P ? vb0 : vb1;  // V(j+1)
     ATTN_WAIT_VMEM();
     __syncthreads();
-    if (j + 2 < nt) dma(kg, kfill, j0 + j + 2, std::false_type{});
-    if (j + 1 < nt) dma(vg, vfill, j0 + j + 1, std::true_type{});
+    if (!SPREAD) {
+      if (j + 2 < nt) dma(kg, kfill, j0 + j + 2, std::false_type{});
+      if (j + 1 < nt) dma(vg, vfill, j0 + j + 1, std::true_type{});
+    }
     mask_tile(cur, j);
     raise(cur);
     // bracket 1: exponentials of tile j beside the products of tile j+1 (past
-    // the last tile those products are not used)
+    // the last tile those products are not used) and the direct loads of
+    // K(j+2) and V(j+1) (past the last tile they repeat it: never read)
     expo(cur);
     qk_ops(nxt, kread);
+    if (SPREAD) {
+      dma(kg, kfill, j0 + min(j + 2, nt - 1), std::false_type{});
+      dma(vg, vfill, j0 + min(j + 1, nt - 1), std::true_type{});
+    }
     sched_b1();
     __builtin_amdgcn_sched_barrier(0);
     // bracket 2: P.V of tile j beside its row sums
