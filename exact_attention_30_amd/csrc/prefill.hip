@@ -81,6 +81,11 @@
 #endif
 //  ATTN_PF_IW_SPREAD    head dims (bit mask as above) for which prefill_iw_kernel
 //                       spreads its direct loads over the MFMAs
+//  ATTN_PF_AQKDMA       1: prefill_kernel's group A moves both K(j+1) and V(j),
+//                       its direct loads spread over its QK MFMAs
+#ifndef ATTN_PF_AQKDMA
+#define ATTN_PF_AQKDMA 1
+#endif
 #ifndef ATTN_PF_IW_SPREAD
 #define ATTN_PF_IW_SPREAD 4
 #endif
@@ -368,9 +373,14 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
   auto active = [&](int jj) __attribute__((always_inline)) {
     return jj >= 0 && jj < nt && (j0 + jj) * BK < kend_w && (j0 + jj + 1) * BK > kbeg_w;
   };
-  auto gemm = [&](int jj, const uint16_t *ks_, const uint16_t *vs_) __attribute__((always_inline)) {
+  // LOADS (NLD direct loads, NLD > 0) go among the QK MFMAs, which then run
+  // whether or not this wave sees tile jj (every wave must move its share of
+  // the tiles; the scores of a tile it does not see are not used)
+  auto gemm = [&](int jj, const uint16_t *ks_, const uint16_t *vs_, auto loads, auto nld)
+      __attribute__((always_inline)) {
+    constexpr int NLD = decltype(nld)::value;
     if (!ATTN_PF_QKFIRST && active(jj - 1)) pv(vs_);
-    if (active(jj)) {
+    if (NLD > 0 || active(jj)) {
 #pragma unroll
       for (int rb = 0; rb < BK / 32; ++rb) s[rb] = f32x16{};
 #pragma unroll
@@ -380,16 +390,19 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
         s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(ks_ + 32 * rb * D + koff(ks))), qf[ks], s[rb],
                                                         0, 0, 0);
       }
-      // K operand reads ATTN_PF_QK_AHEAD MFMAs ahead of their use
+      loads();
+      // K operand reads ATTN_PF_QK_AHEAD MFMAs ahead of their use, a direct
+      // load after every SP-th MFMA
       constexpr int N = (BK / 32) * (D / 16);
       constexpr int A = ATTN_PF_QK_AHEAD;
+      constexpr int SP = NLD > 0 && N / NLD > 0 ? N / NLD : 1;
       __builtin_amdgcn_sched_group_barrier(0x100, A, 0);
 #pragma unroll
-      for (int i = 0; i < N - A; ++i) {
+      for (int i = 0; i < N; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (NLD > 0 && i % SP == 0 && i / SP < NLD) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+        if (i < N - A) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
     }
     if (ATTN_PF_QKFIRST && active(jj - 1)) pv(vs_);
   };
@@ -412,11 +425,12 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
   };
 
   // One tile step j (P = j % 2): K(j) is in kb[P], V(j-1) in vb[1-P].
-  // Group A runs its matrix work G(j) = [P.V of tile j-1, QK of tile j], then
-  // fetches K(j+1) into kb[1-P] and runs the softmax of tile j.  Group B
-  // fetches V(j) into vb[P], runs the softmax of tile j-1, then G(j).  So the
-  // exponentials of one wave execute next to the MFMAs of its SIMD
-  // neighbour.  Both target buffers were last read in step j-1.  A group's
+  // Group A runs its matrix work G(j) = [P.V of tile j-1, QK of tile j], with
+  // the direct loads of K(j+1) into kb[1-P] and V(j) into vb[P] spread over
+  // its QK MFMAs, then the softmax of tile j.  Group B runs the softmax of
+  // tile j-1, then G(j).  So the exponentials of one wave execute next to the
+  // MFMAs of its SIMD neighbour, and no wave stalls on a burst of loads (a
+  // direct load holds its wave until the CU's address unit takes it).  Both target buffers were last read in step j-1.  A group's
   // direct loads are complete before its next LDS reads (those loads and the
   // LDS reads would otherwise share one wait counter), and the step ends with
   // every wave's loads complete and a workgroup barrier, which publishes them.
@@ -426,19 +440,30 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
     uint16_t *knext = P ? kb0 : kb1;
     uint16_t *vprev = P ? vb0 : vb1;
     uint16_t *vcur = P ? vb1 : vb0;
+    auto none = []() __attribute__((always_inline)) {};
+    constexpr auto n0 = std::integral_constant<int, 0>{};
     if (grpA) {
       if (ATTN_PF_PRIO) __builtin_amdgcn_s_setprio(1);
-      gemm(j, kcur, vprev);
+      if (ATTN_PF_AQKDMA) {
+        // K(j+1) and V(j) among the QK MFMAs (past the last tile: a repeat of
+        // it, never read)
+        gemm(j, kcur, vprev, [&]() __attribute__((always_inline)) {
+          dma(kg, knext, j0 + max(0, min(j + 1, nt - 1)), std::false_type{});
+          dma(vg, vcur, j0 + max(0, min(j, nt - 1)), std::true_type{});
+        }, std::integral_constant<int, 4 * C::DPW>{});
+      } else {
+        gemm(j, kcur, vprev, none, n0);
+      }
       if (ATTN_PF_PRIO) __builtin_amdgcn_s_setprio(0);
-      if (j + 1 < nt) dma(kg, knext, j0 + j + 1, std::false_type{});
-      if (ATTN_PF_ADMA && j < nt) dma(vg, vcur, j0 + j, std::true_type{});
+      if (!ATTN_PF_AQKDMA && j + 1 < nt) dma(kg, knext, j0 + j + 1, std::false_type{});
+      if (!ATTN_PF_AQKDMA && ATTN_PF_ADMA && j < nt) dma(vg, vcur, j0 + j, std::true_type{});
       soft(j);
     } else {
-      if (!ATTN_PF_ADMA && j < nt) dma(vg, vcur, j0 + j, std::true_type{});
+      if (!ATTN_PF_AQKDMA && !ATTN_PF_ADMA && j < nt) dma(vg, vcur, j0 + j, std::true_type{});
       soft(j - 1);
-      if (!ATTN_PF_ADMA) ATTN_WAIT_VMEM();
+      if (!ATTN_PF_AQKDMA && !ATTN_PF_ADMA) ATTN_WAIT_VMEM();
       if (ATTN_PF_PRIO) __builtin_amdgcn_s_setprio(1);
-      gemm(j, kcur, vprev);
+      gemm(j, kcur, vprev, none, n0);
       if (ATTN_PF_PRIO) __builtin_amdgcn_s_setprio(0);
     }
     ATTN_WAIT_VMEM();
