@@ -83,6 +83,10 @@
 //                       spreads its direct loads over the MFMAs
 //  ATTN_PF_AQKDMA       1: prefill_kernel's group A moves both K(j+1) and V(j),
 //                       its direct loads spread over its QK MFMAs
+//  ATTN_PF_AQK_SP       MFMAs between two of those loads (0: spread over all of QK)
+#ifndef ATTN_PF_AQK_SP
+#define ATTN_PF_AQK_SP 0
+#endif
 #ifndef ATTN_PF_AQKDMA
 #define ATTN_PF_AQKDMA 1
 #endif
@@ -395,7 +399,7 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
       // load after every SP-th MFMA
       constexpr int N = (BK / 32) * (D / 16);
       constexpr int A = ATTN_PF_QK_AHEAD;
-      constexpr int SP = NLD > 0 && N / NLD > 0 ? N / NLD : 1;
+      constexpr int SP = ATTN_PF_AQK_SP > 0 ? ATTN_PF_AQK_SP : (NLD > 0 && N / NLD > 0 ? N / NLD : 1);
       __builtin_amdgcn_sched_group_barrier(0x100, A, 0);
 #pragma unroll
       for (int i = 0; i < N; ++i) {
