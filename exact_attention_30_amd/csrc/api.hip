@@ -1,6 +1,7 @@
 // The C ABI of libattn.so: argument checks, launch shapes, workspace.
 // The public contract (types, layouts, ownership, errors) is in include/attn.h.
 #include <math.h>
+#include <cstdlib>
 #include <mutex>
 
 #include "../../include/attn.h"
@@ -70,9 +71,28 @@ void decode_workspace(int B, int Hq, int Hkv, int T, int D, DecodeShape *ds) {
 // with split_keys, enough waves that no wave gets more than split_keys keys
 // when every sequence has Lmax keys (capped at kDecodeMaxWaves).
 std::mutex g_occ_mu;
-int g_occ_cache[64][3][3][2];
+int g_occ_cache[64][3][3][2][2];
 
-int device_waves(int D, int GT, bool q8, int *waves) {
+// 32-key blocks of a decode, bounded from the shapes: every sequence at Lmax
+// keys (with a window, the keys its rows can see)
+long long decode_block_bound(int B, int Hkv, int GT, int T, int window, int Lmax) {
+  const long long n_hg = (GT + attn::kDecodeGroup - 1) / attn::kDecodeGroup;
+  long long keys = Lmax;
+  if (window > 0 && (long long)window + T + 31 < keys) keys = (long long)window + T + 31;
+  return (long long)B * Hkv * n_hg * ((keys + 31) / 32);
+}
+
+// Whether a decode takes the wide-group kernel.  The environment variable
+// ATTN_DECODE_WIDE overrides the choice: 0 never, 1 whenever the shape allows
+// it (any cache size), unset or anything else: by the block bound.
+bool decode_pick_wide(int D, int GT, bool q8, int B, int Hkv, int T, int window, int Lmax) {
+  const char *e = getenv("ATTN_DECODE_WIDE");
+  if (e != nullptr && e[0] == '0' && e[1] == 0) return false;
+  if (e != nullptr && e[0] == '1' && e[1] == 0) return attn::decode_use_wide(D, GT, q8, attn::kDecodeWideMinBlocks);
+  return attn::decode_use_wide(D, GT, q8, decode_block_bound(B, Hkv, GT, T, window, Lmax));
+}
+
+int device_waves(int D, int GT, bool q8, bool wide, int *waves) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return ATTN_ERR_HIP;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return ATTN_ERR_HIP;
@@ -80,16 +100,16 @@ int device_waves(int D, int GT, bool q8, int *waves) {
   const int ci = (gw + 15) / 16 >= 3 ? 2 : (gw + 15) / 16 - 1;
   const int di = D == 64 ? 0 : (D == 128 ? 1 : 2);
   std::lock_guard<std::mutex> lk(g_occ_mu);
-  int &occ = g_occ_cache[dev][di][ci][q8 ? 1 : 0];
-  if (occ == 0 && attn::decode_waves_per_cu(D, gw, q8, &occ) != hipSuccess) return ATTN_ERR_HIP;
+  int &occ = g_occ_cache[dev][di][ci][q8 ? 1 : 0][wide ? 1 : 0];
+  if (occ == 0 && attn::decode_waves_per_cu(D, gw, q8, wide, &occ) != hipSuccess) return ATTN_ERR_HIP;
   const long long w = (long long)cus * (occ > 0 ? occ : 1);
   *waves = (int)(w < attn::kDecodeMaxWaves ? w : attn::kDecodeMaxWaves);
   return ATTN_OK;
 }
 
-int decode_waves(int B, int Hq, int Hkv, int T, int Lmax, int D, int split_keys, bool q8, int *waves) {
+int decode_waves(int B, int Hq, int Hkv, int T, int Lmax, int D, int split_keys, bool q8, bool wide, int *waves) {
   const int GT = (Hq / Hkv) * T;
-  if (split_keys == 0) return device_waves(D, GT, q8, waves);
+  if (split_keys == 0) return device_waves(D, GT, q8, wide, waves);
   const double keys = (double)B * Hkv * ((GT + attn::kDecodeGroup - 1) / attn::kDecodeGroup) *
                       (double)((Lmax + 31) / 32) * 32.0;
   double w = keys / split_keys;
@@ -129,7 +149,8 @@ int run_decode(const void *q, const void *kc, const void *vc, const int32_t *len
   decode_workspace(B, Hq, Hkv, T, D, &ds);
   if (ws != nullptr && ws_bytes < ds.total) return ATTN_ERR_WORKSPACE;
   if (B == 0) return ATTN_OK;
-  st = decode_waves(B, Hq, Hkv, T, Lmax, D, split_keys, q8, &ds.waves);
+  const bool wide = decode_pick_wide(D, (Hq / Hkv) * T, q8, B, Hkv, T, window < Lmax ? window : 0, Lmax);
+  st = decode_waves(B, Hq, Hkv, T, Lmax, D, split_keys, q8, wide, &ds.waves);
   if (st != ATTN_OK) return st;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -163,6 +184,7 @@ int run_decode(const void *q, const void *kc, const void *vc, const int32_t *len
   a.window = window < Lmax ? window : 0;   // a window of Lmax or more keys hides nothing
   a.n_hg = (a.G * T + attn::kDecodeGroup - 1) / attn::kDecodeGroup;
   a.c = scale * kLog2e;
+  a.wide = wide ? 1 : 0;
   hipError_t e = attn::launch_decode(a, D, ds.waves, s);
   if (owned) {
     hipError_t f = hipFreeAsync(mem, s);
@@ -419,7 +441,8 @@ int attn_decode_waves(int B, int Hq, int Hkv, int Lmax, int D, int split_keys) {
   if (B <= 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || !head_dim_ok(D) || Lmax < 1) return 0;
   if (split_keys != 0 && (split_keys < 0 || split_keys % 128 != 0)) return 0;
   int w = 0;
-  return decode_waves(B, Hq, Hkv, 1, Lmax, D, split_keys, false, &w) == ATTN_OK ? w : 0;
+  const bool wide = decode_pick_wide(D, Hq / Hkv, false, B, Hkv, 1, 0, Lmax);
+  return decode_waves(B, Hq, Hkv, 1, Lmax, D, split_keys, false, wide, &w) == ATTN_OK ? w : 0;
 }
 
 const char *attn_status_string(int status) {

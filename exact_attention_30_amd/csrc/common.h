@@ -85,3 +85,16 @@ ATTN_DEV bf16x4 lds_tr16(const uint16_t *p) {
   return __builtin_bit_cast(bf16x4, r);
 }
 
+// Address spaces of the direct global -> LDS loads (global_load_lds_dwordx4).
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// LDS row swizzles.  A tile row is stored unpadded; its 16-byte chunk c sits
+// at chunk c ^ swz(row).  K: the b128 operand reads (16 rows, one chunk) then
+// hit 16 distinct bank groups.  V: the swizzle moves whole 64-byte groups, so
+// each transposing read still finds its 4 chunks together, and 4 consecutive
+// rows land in 4 distinct bank quarters.
+template <int D>
+ATTN_DEV int kswz(int r) { return D == 64 ? ((r >> 1) & 7) : (r & 15); }
+template <int D>
+ATTN_DEV int vswz(int r) { return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3); }

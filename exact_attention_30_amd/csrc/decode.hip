@@ -125,6 +125,11 @@ ATTN_DEV u32x4 dequant8(uint32_t lo, uint32_t hi, float s) {
 }
 ATTN_DEV float half_bits_to_float(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
+// head dims (bit mask: 1 = D 64, 2 = D 128) for which wide row groups may
+// take decode_wide_kernel (D = 256 would spill its registers)
+#ifndef ATTN_DEC_WIDE
+#define ATTN_DEC_WIDE 3
+#endif
 // Largest column-block count that keeps two register sets of K/V in flight.
 #ifndef ATTN_DEC_DBUF_NCB
 #define ATTN_DEC_DBUF_NCB 2
@@ -543,6 +548,320 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
   }
 }
 
+// s_waitcnt vmcnt(n) (n < 64), other counters left alone
+#define ATTN_DEC_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | ((((n) >> 4) & 3) << 14))
+// s_waitcnt lgkmcnt(0), other counters left alone
+#define ATTN_DEC_WAIT_LDS() __builtin_amdgcn_s_waitcnt(0xC07F)
+
+// Wide row groups (17 to 64 query rows of a KV head: G * T > 16): the same
+// flat split, pieces and combine as decode_main_kernel, with the matrix work
+// of the prefill kernel.  NC blocks of 32 query rows per wave; per 32-key
+// block:
+//  * K and V rows move HBM -> LDS with direct loads (no registers), two
+//    blocks in flight, rows outside the piece's keys read from its edge (and
+//    masked), K rows XOR-swizzled for the b128 operand reads, V rows for the
+//    transposing reads;
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (32 keys x 32 rows; each K
+//    operand read serves every row block), so a lane holds one query row and
+//    16 keys: row max and sum are lane-local plus one v_permlane32_swap;
+//  * O^T += V^T P^T with P^T packed from the accumulators and V^T read with
+//    ds_read_b64_tr_b16.
+template <int D, int NC>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NC == 1 ? 2 : 1))) void decode_wide_kernel(DecodeArgs a) {
+  constexpr int TILE = 32 * D;            // elements of one 32-key K or V tile
+  constexpr int NBLK = TILE * 2 / 1024;   // 1 KiB direct loads per tile
+  constexpr int RPB = 512 / D;            // rows per 1 KiB
+  constexpr int CPR = D / 8;              // 16-byte chunks per row
+  constexpr int NLD = 2 * NBLK;           // direct loads per 32-key block
+  __shared__ __attribute__((aligned(1024))) uint16_t kb0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t kb1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t vb0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t vb1[TILE];
+
+  const int lane = threadIdx.x;
+  const int ql = lane & 31, hf = lane >> 5;
+  const long long W = gridDim.x, w = blockIdx.x;
+  const long long HH = (long long)a.Hkv * a.n_hg;
+  const long long total = a.pre[a.B] * HH;
+  const long long q = total / W, rem = total % W;
+  long long r = q * w + min(w, rem);
+  const long long r1 = r + q + (w < rem ? 1 : 0);
+  if (r >= r1) return;
+  int b;
+  {
+    int lo = 0, hi = a.B;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (HH * a.pre[mid] <= r) lo = mid;
+      else hi = mid;
+    }
+    b = lo;
+  }
+  long long nb = a.pre[b + 1] - a.pre[b];
+  long long off = r - HH * a.pre[b];
+  int hseg = (int)(off / nb);
+  long long blk = off - hseg * nb;
+
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  const float cexp = a.c;
+  const bool cpos = cexp >= 0.f;
+  const float maskval = cpos ? -__builtin_inff() : __builtin_inff();
+  const int GT = a.G * a.T;
+  const int GW = min(GT, kDecodeGroup);
+
+  // per-lane LDS offsets (elements) of the operands, as in the prefill
+  // kernel: K row ql, chunk 2 ks + hf; V^T rows 4 hf + (j16 >> 2) of each
+  // 16-key step
+  const int g16 = lane >> 4, j16 = lane & 15;
+  constexpr int NKO = D / 16 < 8 ? D / 16 : 8;
+  constexpr int NVO = D / 32 < 4 ? D / 32 : 4;
+  int koffs[NKO];
+#pragma unroll
+  for (int ks = 0; ks < NKO; ++ks) koffs[ks] = ql * D + 8 * ((2 * ks + hf) ^ kswz<D>(ql));
+  int voffs[NVO];
+  {
+    const int vr = 4 * hf + (j16 >> 2);
+    const int tv = vswz<D>(vr) >> 2;
+    const int cin = 2 * (g16 & 1) + ((j16 & 3) >> 1);
+#pragma unroll
+    for (int db = 0; db < NVO; ++db) voffs[db] = vr * D + 8 * (4 * (db ^ tv) + cin) + 4 * (j16 & 1);
+  }
+  auto koff = [&](int ks) __attribute__((always_inline)) { return koffs[ks % NKO] + (ks / NKO) * 128; };
+  auto voff = [&](int db) __attribute__((always_inline)) { return voffs[db % NVO] + (db / NVO) * 128; };
+
+  while (r < r1) {
+    const long long take = min(nb - blk, r1 - r);
+    const int hkv = hseg / a.n_hg, hg = hseg - hkv * a.n_hg;
+    const int gq0 = hg * kDecodeGroup;
+    const int gcnt = min(kDecodeGroup, GT - gq0);
+    const int n = max(0, min(a.lens[b], a.Lmax));
+    const int kseg = seg_begin(a, n);
+    const int kmin = a.window ? max(0, n - a.T - a.window + 1) : 0;
+    const int k0 = kseg + (int)(blk * 32);
+    const int k1 = min(n, kseg + (int)((blk + take) * 32));
+    const bool whole = (blk == 0) && (take == nb);
+    // this lane's query row in each row block and its visible keys
+    // [klo, kcol): row t of the T new rows sees keys up to n - T + t
+    int kcol[NC], klo[NC];
+#pragma unroll
+    for (int cb = 0; cb < NC; ++cb) {
+      kcol[cb] = n - a.T + 1 + (gq0 + 32 * cb + ql) % a.T;
+      klo[cb] = a.window ? kcol[cb] - a.window : -0x7fffffff;
+    }
+    const int kfull = min(k1, n - a.T + 1);
+    const int klo_all = a.window ? n - a.window : -0x7fffffff;
+    const long long slot = (long long)b * HH + hseg + w;
+
+    // Q^T operands: row 32 cb + ql, dims 16 ks + 8 hf ...
+    bf16x8 qf[NC][D / 16];
+#pragma unroll
+    for (int cb = 0; cb < NC; ++cb) {
+      const int qi = 32 * cb + ql;
+      const uint16_t *qp = a.q + (((size_t)b * a.Hq + hkv * a.G) * a.T + gq0 + min(qi, gcnt - 1)) * D + 8 * hf;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) qf[cb][ks] = as_bf16x8(qi < gcnt ? ld16(qp + 16 * ks) : zero4);
+    }
+    const size_t base = ((size_t)b * a.Hkv + hkv) * (size_t)a.Lmax * D;
+    const uint16_t *kg = a.kc + base;
+    const uint16_t *vg = a.vc + base;
+
+    f32x16 o[NC][D / 32];
+    float m_run[NC], l_run[NC];
+#pragma unroll
+    for (int cb = 0; cb < NC; ++cb) {
+      m_run[cb] = -__builtin_inff();
+      l_run[cb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[cb][db] = f32x16{};
+    }
+
+    // the 32-key block at kb into LDS (rows clamped into [kmin, k1): such
+    // rows are masked)
+    auto dma = [&](uint16_t *kd, uint16_t *vd, int kb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < NBLK; ++i) {
+        const int row = i * RPB + lane / CPR;
+        const size_t key = (size_t)min(max(kb + row, kmin), k1 - 1);
+        const int ck = (lane % CPR) ^ kswz<D>(row);
+        const int cv = (lane % CPR) ^ vswz<D>(row);
+        __builtin_amdgcn_global_load_lds((glb_void_t *)(kg + key * D + 8 * ck), (lds_void_t *)(kd + i * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((glb_void_t *)(vg + key * D + 8 * cv), (lds_void_t *)(vd + i * 512), 16, 0, 0);
+      }
+    };
+
+    auto compute = [&](const uint16_t *kt, const uint16_t *vt, int kb) __attribute__((always_inline)) {
+      // S^T = K Q^T, every K operand read serving the NC row blocks
+      f32x16 s[NC];
+#pragma unroll
+      for (int cb = 0; cb < NC; ++cb) s[cb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 kop = as_bf16x8(ld16(kt + koff(ks)));
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb) s[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[cb][ks], s[cb], 0, 0, 0);
+      }
+      {
+        constexpr int N = D / 16, A = N < 4 ? N : 4;
+        __builtin_amdgcn_sched_group_barrier(0x100, A, 0);
+#pragma unroll
+        for (int i = 0; i < N - A; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, NC, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NC * A, 0);
+      }
+      const bool partial = kb + 32 > kfull || kb < klo_all;
+      bf16x8 pb[NC][2];
+#pragma unroll
+      for (int cb = 0; cb < NC; ++cb) {
+        uint32_t vis = 0xffffu;
+        if (partial) {
+          vis = 0;
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const int key = kb + 8 * (rr >> 2) + 4 * hf + (rr & 3);
+            const bool vv = key < k1 && key < kcol[cb] && key >= klo[cb];
+            vis |= (vv ? 1u : 0u) << rr;
+            s[cb][rr] = vv ? s[cb][rr] : maskval;
+          }
+        }
+        float red;
+        if (cpos) {
+          red = fmax3(s[cb][0], s[cb][1], s[cb][2]);
+#pragma unroll
+          for (int i = 3; i < 15; i += 2) red = fmax3(red, s[cb][i], s[cb][i + 1]);
+          red = pair_max(__builtin_fmaxf(red, s[cb][15]));
+        } else {
+          red = fmin3(s[cb][0], s[cb][1], s[cb][2]);
+#pragma unroll
+          for (int i = 3; i < 15; i += 2) red = fmin3(red, s[cb][i], s[cb][i + 1]);
+          red = pair_min(__builtin_fminf(red, s[cb][15]));
+        }
+        const float mt = red * cexp;
+        const bool need = mt > m_run[cb] + ATTN_RESCALE_SLACK;
+        if (wave_any(need)) {
+          const float mnew = need ? mt : m_run[cb];
+          const float alpha = need ? fast_exp2(m_run[cb] - mnew) : 1.f;
+          l_run[cb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) o[cb][db] *= alpha;
+          m_run[cb] = mnew;
+        }
+        const float nm = -m_run[cb];
+        float p[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float e = fast_exp2(__builtin_fmaf(s[cb][i], cexp, nm));
+          // a hidden score is +-inf; with c == 0 the product would be NaN
+          if (partial) e = ((vis >> i) & 1u) ? e : 0.f;
+          p[i] = e;
+        }
+        float t8[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t8[i] = p[i] + p[i + 8];
+        l_run[cb] += ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
+        pb[cb][0] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+        pb[cb][1] = pack8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
+      }
+      // O^T += V^T P^T, every V^T operand read serving the NC row blocks
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq) {
+          const uint16_t *vp = vt + 16 * kq * D + voff(db);
+          const bf16x4 lo = lds_tr16(vp);
+          const bf16x4 hi = lds_tr16(vp + 8 * D);
+          const bf16x8 vop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+          for (int cb = 0; cb < NC; ++cb)
+            o[cb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[cb][kq], o[cb][db], 0, 0, 0);
+        }
+      }
+      {
+        constexpr int N = 2 * (D / 32), A = N < 3 ? N : 3;
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * A, 0);
+#pragma unroll
+        for (int i = 0; i < N - A; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, NC, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NC * A, 0);
+      }
+    };
+
+    // two blocks in flight: block i in (kb[i % 2], vb[i % 2]); the loads of
+    // block i + 2 go into the buffers of block i once its reads are done
+    const int nblk = (k1 - k0 + 31) / 32;
+    auto step = [&](int bi, uint16_t *kt, uint16_t *vt) __attribute__((always_inline)) {
+      if (bi + 1 < nblk) ATTN_DEC_WAIT_VM(NLD);
+      else ATTN_DEC_WAIT_VM(0);
+      compute(kt, vt, k0 + 32 * bi);
+      if (bi + 2 < nblk) {
+        ATTN_DEC_WAIT_LDS();
+        dma(kt, vt, k0 + 32 * (bi + 2));
+      }
+    };
+    ATTN_DEC_WAIT_LDS();   // the previous piece's reads of these buffers are done
+    dma(kb0, vb0, k0);
+    if (nblk > 1) dma(kb1, vb1, k0 + 32);
+    for (int bi = 0; bi < nblk; bi += 2) {
+      step(bi, kb0, vb0);
+      if (bi + 1 >= nblk) break;
+      step(bi + 1, kb1, vb1);
+    }
+
+    // ---- this piece's result: lane (row 32 cb + ql) holds dims
+    // 32 db + 8 j + 4 hf + (0..3) -----------------------------------------
+#pragma unroll
+    for (int cb = 0; cb < NC; ++cb) {
+      const float lt = pair_sum(l_run[cb]);
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const int qi = 32 * cb + ql;
+      if (qi < gcnt) {
+        const size_t row = ((size_t)b * a.Hq + hkv * a.G) * a.T + gq0 + qi;
+        const float lse_c = lt > 0.f ? m_run[cb] * ATTN_LN2 + __logf(lt) : -__builtin_inff();
+        if (whole) {
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              bf16x4 v4;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) v4[i] = (__bf16)(o[cb][db][4 * j + i] * inv);
+              *reinterpret_cast<bf16x4 *>(a.out + row * D + 32 * db + 8 * j + 4 * hf) = v4;
+            }
+          if (a.lse != nullptr && hf == 0) a.lse[row] = lse_c;
+        } else {
+          const size_t pr = (size_t)slot * GW + qi;
+          float *po = a.part_o + pr * D;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const f32x4 v4 = {o[cb][db][4 * j] * inv, o[cb][db][4 * j + 1] * inv, o[cb][db][4 * j + 2] * inv,
+                                o[cb][db][4 * j + 3] * inv};
+              *reinterpret_cast<f32x4 *>(po + 32 * db + 8 * j + 4 * hf) = v4;
+            }
+          if (hf == 0) a.part_lse[pr] = lse_c;
+        }
+      }
+    }
+
+    // ---- next segment (skipping empty sequences) --------------------------
+    r += take;
+    if (r >= r1) break;
+    blk = 0;
+    if (++hseg == HH) {
+      hseg = 0;
+      do {
+        ++b;
+      } while (b < a.B && a.pre[b + 1] == a.pre[b]);
+      if (b >= a.B) break;
+      nb = a.pre[b + 1] - a.pre[b];
+    }
+  }
+}
+
 // Merge the pieces of every (sequence, query head) whose segment was split
 // between waves; also writes out = 0 / lse = -inf for empty sequences.  One
 // wave per row: piece lse values are read one per lane (64 per round) and
@@ -623,11 +942,29 @@ static hipError_t launch_t(const DecodeArgs &a, int W, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D, int NC>
+static hipError_t launch_w(const DecodeArgs &a, int W, hipStream_t s) {
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_wide_kernel<D, NC>), dim3(W), dim3(64), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.Hq * a.T), dim3(64), 0, s, a, W);
+  return hipGetLastError();
+}
+
+template <int D>
+constexpr bool kDecodeWide = D <= 128 && (ATTN_DEC_WIDE & (D == 64 ? 1 : 2)) != 0;
+
 template <int D>
 static hipError_t launch_d(const DecodeArgs &a, int W, hipStream_t s) {
   const int gt = a.G * a.T;
   const int gw = gt < kDecodeGroup ? gt : kDecodeGroup;
   const int ncb = (gw + 15) / 16;
+  if constexpr (D <= 128) {
+    if (a.wide) return launch_w<D, 2>(a, W, s);
+  }
   if (ncb == 1) return launch_t<D, 1>(a, W, s);
   if (ncb == 2) return launch_t<D, 2>(a, W, s);
   return launch_t<D, 4>(a, W, s);
@@ -644,10 +981,22 @@ hipError_t launch_decode(const DecodeArgs &a, int D, int W, hipStream_t s) {
 
 // Resident 64-thread workgroups of the main kernel per CU for GW query rows
 // per wave group (q8: the int8-cache kernel).
-hipError_t decode_waves_per_cu(int D, int GW, bool q8, int *out) {
+bool decode_use_wide(int D, int GW, bool q8, long long blocks) {
+  const int gw = GW < kDecodeGroup ? GW : kDecodeGroup;
+  const bool built = D == 64 ? kDecodeWide<64> : D == 128 ? kDecodeWide<128> : kDecodeWide<256>;
+  return built && !q8 && gw > 32 && blocks >= kDecodeWideMinBlocks;
+}
+
+hipError_t decode_waves_per_cu(int D, int GW, bool q8, bool wide, int *out) {
   const int gw = GW < kDecodeGroup ? GW : kDecodeGroup;
   const int ncb = (gw + 15) / 16;
   const void *f = nullptr;
+  if (wide) {
+    if (D == 64) f = (const void *)&decode_wide_kernel<64, 2>;
+    else if (D == 128) f = (const void *)&decode_wide_kernel<128, 2>;
+    else return hipErrorInvalidValue;   // not built for D = 256 (its registers spill)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, f, 64, 0);
+  }
 #define ATTN_PICK(DD, NN)                                                                \
   f = q8 ? reinterpret_cast<const void *>(&decode_main_kernel<DD, NN, true>)           \
          : reinterpret_cast<const void *>(&decode_main_kernel<DD, NN, false>)

@@ -50,6 +50,7 @@ struct DecodeArgs {
   int n_hg;         // groups of up to kDecodeGroup query rows per KV head
                     // (a KV head's G * T rows; GW = min(G * T, kDecodeGroup))
   float c;          // scale * log2(e)
+  int wide;         // 1: decode_wide_kernel (see decode_use_wide)
 };
 
 struct BackwardArgs {
@@ -93,7 +94,14 @@ int prefill_tile_keys(int D);
 constexpr int kPrefillMaxSplits = 64;
 hipError_t launch_prefill(const PrefillArgs &a, int D, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int D, int waves, hipStream_t s);
-hipError_t decode_waves_per_cu(int D, int GW, bool q8, int *out);
+hipError_t decode_waves_per_cu(int D, int GW, bool q8, bool wide, int *out);
+// Whether a decode takes decode_wide_kernel: bf16 caches, more than 32 query
+// rows per row group (two 32-row blocks per wave), a head dim it is built for,
+// and at least kDecodeWideMinBlocks 32-key blocks to split (BLOCKS: an upper
+// bound from the shapes), so that every wave gets enough of them to keep its
+// two blocks of loads in flight.
+constexpr long long kDecodeWideMinBlocks = 32768;
+bool decode_use_wide(int D, int GW, bool q8, long long blocks);
 hipError_t launch_backward(const BackwardArgs &a, int D, hipStream_t s);
 // Query heads handled together by one workgroup of the dq kernel.
 int backward_dq_heads(int G);

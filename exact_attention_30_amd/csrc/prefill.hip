@@ -138,18 +138,6 @@ struct PrefillCfg {
   static_assert(BK % 32 == 0 && D % 32 == 0, "tile shape");
 };
 
-// LDS row swizzles.  A tile row is stored unpadded; its 16-byte chunk c sits
-// at chunk c ^ swz(row).  K: the b128 operand reads (16 rows, one chunk) then
-// hit 16 distinct bank groups.  V: the swizzle moves whole 64-byte groups, so
-// each transposing read still finds its 4 chunks together, and 4 consecutive
-// rows land in 4 distinct bank quarters.
-template <int D>
-ATTN_DEV int kswz(int r) { return D == 64 ? ((r >> 1) & 7) : (r & 15); }
-template <int D>
-ATTN_DEV int vswz(int r) { return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3); }
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
 
 // s_waitcnt vmcnt(0), other counters left alone (expcnt 7, lgkmcnt 15)
 #define ATTN_WAIT_VMEM() __builtin_amdgcn_s_waitcnt(0x0F70)

@@ -220,6 +220,13 @@ int attn_decode_ex(const void *q, const void *kcache, const void *vcache, const 
  * are chosen as attn_decode does; workspace as attn_decode_ex (NULL: taken
  * from the stream-ordered allocator), sized by
  * attn_decode_multi_workspace_bytes.
+ *
+ * Groups of 33 to 64 rows over a large cache (at least 32768 32-key blocks
+ * by the shapes, D 64 or 128, bf16 caches) take a second kernel with 32-row
+ * matrix blocks and K/V staged through LDS; results agree to rounding.  The
+ * environment variable ATTN_DECODE_WIDE, read at each call, overrides that
+ * choice (here and in attn_decode): "0" never, "1" whenever the group size
+ * and head dim allow it.
  */
 int attn_decode_multi(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens,
                       void *out, float *lse, int B, int Hq, int Hkv, int T, int window, int Lmax, int D,

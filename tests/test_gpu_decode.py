@@ -206,6 +206,84 @@ def test_decode_multi_parity(attn, T, case, _):
     check_lse(to_np(lse), rl, case.name)
 
 
+@pytest.fixture
+def wide_env(monkeypatch):
+    """Set ATTN_DECODE_WIDE (read by the library at each call) for one test."""
+    def set_(v):
+        if v is None:
+            monkeypatch.delenv("ATTN_DECODE_WIDE", raising=False)
+        else:
+            monkeypatch.setenv("ATTN_DECODE_WIDE", v)
+    return set_
+
+
+# the MULTI cases whose row groups have more than 32 rows (the wide kernel's domain)
+WIDE = [m for m in MULTI if m[1].Hq // m[1].Hkv * m[0] > 32]
+
+
+@pytest.mark.parametrize("mode", ["1", "0"])
+@pytest.mark.parametrize("T,case,_", WIDE, ids=lambda x: x.name if hasattr(x, "name") else str(x))
+def test_decode_multi_wide_kernel_parity(attn, wide_env, mode, T, case, _):
+    """Both kernels for wide row groups (forced on and off at small sizes)."""
+    wide_env(mode)
+    lens = case.kv_lens()
+    qb = multi_q_bits(case, T)
+    kc, vc = decode_cache_on_device(case, lens)
+    ro, rl = multi_reference(case, T, qb, lens)
+    out, lse = attn.decode_multi(to_dev(qb), kc, vc, torch.from_numpy(lens).to(DEV), scale=case.scale)
+    torch.cuda.synchronize()
+    check_out(to_np(out), ro, f"{case.name} wide={mode}")
+    check_lse(to_np(lse), rl, f"{case.name} wide={mode}")
+
+
+@pytest.mark.parametrize("T,window,idx", [(16, 100, 2), (16, 1, 1), (7, 30, 4)])
+def test_decode_multi_wide_kernel_window(attn, wide_env, T, window, idx):
+    """The wide kernel with a window: keys before the earliest window start
+    hold NaN and must not be read."""
+    wide_env("1")
+    case = MULTI[idx][1]
+    lens = case.kv_lens()
+    qb = multi_q_bits(case, T)
+    kc, vc = decode_cache_on_device(case, lens)
+    for b, n in enumerate(lens):
+        start = max(0, int(min(n, case.Lmax)) - T - window + 1)
+        if start > 0:
+            kc[b, :, :start] = float("nan")
+            vc[b, :, :start] = float("nan")
+    ro, rl = multi_reference(case, T, qb, lens, window=window)
+    out, lse = attn.decode_multi(to_dev(qb), kc, vc, torch.from_numpy(lens).to(DEV), scale=case.scale, window=window)
+    torch.cuda.synchronize()
+    check_out(to_np(out), ro, f"{case.name} window={window} wide")
+    check_lse(to_np(lse), rl, f"{case.name} window={window} wide")
+
+
+@pytest.mark.timeout(600)
+def test_decode_multi_wide_auto_at_scale(attn, wide_env):
+    """T = 16 at Qwen3-8B heads over a 32768-key ragged cache: large enough
+    that the library picks the wide kernel by itself (its bits equal the
+    forced run's and differ from the other kernel's), and it matches the
+    oracle on every sequence."""
+    T = 16
+    case = ai.DecodeCase("multi_T16_B4_L32768", 38, B=4, Hq=32, Hkv=8, Lmax=32768, D=128, lens_lo=0, lens_hi=0,
+                         fixed_lens=[32768, 1, 20000, 31])
+    lens = case.kv_lens()
+    qb = multi_q_bits(case, T)
+    kc, vc = decode_cache_on_device(case, lens)
+    q, ld = to_dev(qb), torch.from_numpy(lens).to(DEV)
+    wide_env(None)
+    o_auto, l_auto = attn.decode_multi(q, kc, vc, ld, scale=case.scale)
+    wide_env("1")
+    o_on, l_on = attn.decode_multi(q, kc, vc, ld, scale=case.scale)
+    wide_env("0")
+    o_off, _ = attn.decode_multi(q, kc, vc, ld, scale=case.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o_auto, o_on) and torch.equal(l_auto, l_on)
+    assert not torch.equal(o_on, o_off)
+    ro, rl = multi_reference(case, T, qb, lens)
+    check_out(to_np(o_auto), ro, case.name)
+    check_lse(to_np(l_auto), rl, case.name)
+
+
 def test_decode_multi_one_row_is_decode(attn):
     """T = 1 is attn_decode (same kernel path, identical bits)."""
     case = ai.DecodeCase("multi_T1", 37, B=5, Hq=8, Hkv=2, Lmax=700, D=128, lens_lo=0, lens_hi=0,
