@@ -42,6 +42,11 @@
 //    lane handed out through LDS, and the codes turned into the bf16 MFMA
 //    operands in registers once they arrive.
 //  * Lazy max update as in the prefill kernel.
+//  * Wide row groups (33 to 64 query rows per KV head, bf16 caches, large
+//    caches) take decode_wide_kernel instead: the same split and partials,
+//    with two 32-row blocks per wave on v_mfma_f32_32x32x16_bf16 (row
+//    statistics lane-local), and K/V moved to LDS by direct loads (two
+//    blocks in flight without registers) and read as in the prefill kernel.
 //  * The combine kernel (one wave per query row) merges the partials of the
 //    segments that were split between waves.
 #include "common.h"
