@@ -234,18 +234,29 @@ int prefill_setup(PrefillArgs *pa, int B, int Hq, int Hkv, int Lq, int Lk, int D
   if (!attn::prefill_plan(a, D)) return ATTN_ERR_SHAPE;
   int ns = splits;
   if (ns == 0) {
-    int cus = 0;
+    // Small grids: cut each query block's keys into ns ranges.  With S
+    // resident workgroups on the device, u workgroups of work w take
+    // ceil(u ns / S) rounds of w / ns each; every range adds a partial
+    // output to merge (a small cost per range).  Pick the cheapest ns.
+    int cus = 0, occ = 0;
     if (device_cus(&cus) != ATTN_OK) return ATTN_ERR_HIP;
+    if (attn::prefill_wgs_per_cu(D, &occ) != hipSuccess) return ATTN_ERR_HIP;
+    const long long slots = (long long)cus * (occ > 0 ? occ : 1);
     const long long units = a.total;
     ns = 1;
-    if (units < 2LL * cus) {
+    if (units < 2 * slots) {
       const int tk = attn::prefill_tile_keys(D);
       const long long keys = a.window ? (long long)a.window + a.Bq : (long long)Lk;   // per query block, at most
       long long cap = (keys + tk - 1) / tk / 8;
       if (cap > 32) cap = 32;
-      long long want = (2LL * cus + units - 1) / units;
-      if (want > cap) want = cap;
-      if (want > 1) ns = (int)want;
+      double best = (double)((units + slots - 1) / slots);
+      for (long long n = 2; n <= cap; ++n) {
+        const double cost = (double)((units * n + slots - 1) / slots) / n + 0.02 * n;
+        if (cost < best - 1e-9) {
+          best = cost;
+          ns = (int)n;
+        }
+      }
     }
   }
   a.nsplit = ns;

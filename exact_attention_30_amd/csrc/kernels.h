@@ -90,6 +90,8 @@ constexpr int kDecodeGroup = ATTN_DEC_GROUP;
 bool prefill_plan(PrefillArgs &a, int D);
 // Keys per tile of the prefill kernel for head dim D.
 int prefill_tile_keys(int D);
+// Resident workgroups per CU of the prefill kernel for head dim D.
+hipError_t prefill_wgs_per_cu(int D, int *out);
 // Largest key-split count the combine step supports.
 constexpr int kPrefillMaxSplits = 64;
 hipError_t launch_prefill(const PrefillArgs &a, int D, hipStream_t s);

@@ -906,6 +906,22 @@ bool prefill_plan(PrefillArgs &a, int D) {
   return true;
 }
 
+template <int D, int BK>
+static hipError_t wgs_per_cu_t(int *out) {
+  const void *f = (ATTN_PF_IW & (D == 64 ? 1 : D == 128 ? 2 : 4)) ? (const void *)&prefill_iw_kernel<D, BK>
+                                                                  : (const void *)&prefill_kernel<D, BK>;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, f, PrefillCfg<D, BK>::NT, 0);
+}
+
+hipError_t prefill_wgs_per_cu(int D, int *out) {
+  switch (D) {
+    case 64: return wgs_per_cu_t<64, 64>(out);
+    case 128: return wgs_per_cu_t<128, ATTN_PF_BK128>(out);
+    case 256: return wgs_per_cu_t<256, ATTN_PF_BK256>(out);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_prefill(const PrefillArgs &a, int D, hipStream_t s) {
   switch (D) {
     case 64: return launch_t<64, 64>(a, s);
