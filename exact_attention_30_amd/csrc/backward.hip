@@ -446,12 +446,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
 // ---------------------------------------------------------------------------
 // dq
 // ---------------------------------------------------------------------------
-// keys per tile of the dq loop (D = 256: 32, so that three tiles fit in LDS)
+// keys per tile of the dq loop: 32 keeps a wave within 256 registers and a
+// workgroup within 48 KiB of LDS (D <= 128), so two waves share each SIMD
+#ifndef ATTN_BWD_DQ_BK
+#define ATTN_BWD_DQ_BK 32
+#endif
 template <int D>
-constexpr int kBwdQKeys = D == 256 ? 32 : 64;
+constexpr int kBwdQKeys = D == 256 ? 32 : ATTN_BWD_DQ_BK;
+// waves per SIMD the dq kernel is built for (two need 32-key tiles: registers
+// and LDS for two workgroups per CU)
+template <int D>
+constexpr int kBwdQWaves = (D <= 128 && kBwdQKeys<D> == 32) ? 2 : 1;
 
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void bwd_dq_kernel(BackwardArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdQWaves<D>))) void bwd_dq_kernel(BackwardArgs a) {
   constexpr int CPR = D / 8;
   constexpr int BK = kBwdQKeys<D>;
   constexpr int TILE = BK * D;
