@@ -95,10 +95,12 @@ typedef enum {
  * enqueued, and the pointers may be NULL (the other arguments are still
  * checked).
  *
- * When the grid of query blocks is small (fewer than two workgroups per
- * compute unit, e.g. a chunk of a few hundred rows over a long cache), the
- * keys of each query block are cut into several ranges processed by separate
- * workgroups, and a second kernel merges their normalised partial outputs
+ * When the grid of query blocks is small (less than two rounds of the
+ * device's resident workgroups, e.g. a chunk of a few hundred rows over a
+ * long cache), the keys of each query block are cut into several ranges
+ * processed by separate workgroups (as many as make the grid fill whole
+ * rounds best, at least 8 key tiles each, at most 32), and a second kernel
+ * merges their normalised partial outputs
  * and log-sum-exps (the same merge as the decode's; see attn_prefill_ex).
  * The partials then live in a workspace taken from HIP's stream-ordered
  * allocator on `stream` and released on it.
