@@ -45,6 +45,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU seconds per oracle sample")
     p.add_argument("--all-configs", action="store_true",
                    help="time every prefill and decode configuration (one JSON line each) instead of the step")
+    p.add_argument("--only", default="",
+                   help="with --all-configs: comma-separated substrings; only configurations whose name contains one")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy three times (scale for HBM byte counters)")
     return p.parse_args()
@@ -198,8 +200,9 @@ def _time_ms(fn, iters: int, stream, between=None) -> float:
     return float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
 
-def all_configs(iters: int):
-    """Every prefill and decode shape of the workload list, timed on the GPU.
+def all_configs(iters: int, only=()):
+    """Every prefill and decode shape of the workload list, timed on the GPU
+    (ONLY: name substrings selecting some of them).
 
     Prefill inputs come from the seeded host generators; the G-sweep decode
     caches (up to 8.6 GB) are filled on the device from a seeded torch
@@ -213,9 +216,14 @@ def all_configs(iters: int):
     stream = torch.cuda.current_stream(dev)
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
 
+    def want(name):
+        return not only or any(o in name for o in only)
+
     prefills = [ai.TINY, ai.QWEN_4K, ai.QWEN_16K, ai.QWEN_32K, ai.QWEN_CHUNK, ai.D256]
     prefills += [ai.gsweep_prefill(G) for G in ai.G_SWEEP]
     for pc in prefills:
+        if not want(pc.name):
+            continue
         q, k, v = to_dev(pc.q_bits(), dev), to_dev(pc.k_bits(), dev), to_dev(pc.v_bits(), dev)
         out = torch.empty_like(q)
         lse = torch.empty((pc.B, pc.Hq, pc.Lq), dtype=torch.float32, device=dev)
@@ -235,6 +243,8 @@ def all_configs(iters: int):
     # (five matrix products over the visible pairs: QK^T, dO V^T, P^T dO,
     # dS^T Q, dS K)
     for pc in (ai.QWEN_4K, ai.QWEN_16K, ai.D256):
+        if not want(pc.name.replace("prefill", "backward")):
+            continue
         q, k, v = to_dev(pc.q_bits(), dev), to_dev(pc.k_bits(), dev), to_dev(pc.v_bits(), dev)
         g = to_dev(pc.dout_bits(), dev)
         out, lse = attn.prefill(q, k, v, causal=True, scale=pc.scale)
@@ -255,12 +265,13 @@ def all_configs(iters: int):
     torch.cuda.empty_cache()
 
     # several new rows per sequence (speculative verification) over the ragged cache
+    multi_t = [T for T in (2, 4, 8, 16) if want(f"multi_query_decode_T{T}_ragged_B64")]
     dc = ai.RAGGED_DECODE
     lens = dc.kv_lens()
-    kc, vc = build_decode_cache(dc, lens, dev)
+    kc, vc = build_decode_cache(dc, lens, dev) if multi_t else (None, None)
     dl = torch.from_numpy(lens).to(dev)
     nb = acc.decode_kv_bytes(lens, dc.Hkv, dc.D, dc.Lmax)
-    for T in (2, 4, 8, 16):
+    for T in multi_t:
         qm = to_dev(ai.normal_bf16_bits((dc.B, dc.Hq, T, dc.D), [dc.wid, 0, dc.variant, 1000 + T]), dev)
         om = torch.empty_like(qm)
         fn = lambda: attn.decode_multi(qm, kc, vc, dl, scale=dc.scale, out=om, return_lse=False)  # noqa: E731
@@ -277,40 +288,45 @@ def all_configs(iters: int):
 
     # sliding window (4096 keys): prefill at 16K and the ragged decode; work counted on visible keys
     W = 4096
-    pc = ai.QWEN_16K
-    q, k, v = to_dev(pc.q_bits(), dev), to_dev(pc.k_bits(), dev), to_dev(pc.v_bits(), dev)
-    out = torch.empty_like(q)
-    fn = lambda: attn.prefill_ex(q, k, v, causal=True, scale=pc.scale, window=W, out=out, return_lse=False)  # noqa: E731
-    for _ in range(2):
-        fn()
-    ms = _time_ms(fn, iters, stream)
-    i = np.arange(pc.Lq, dtype=np.int64)
-    vis = int(np.minimum(W, i + (pc.Lk - pc.Lq) + 1).sum())
-    fl = 4 * pc.B * pc.Hq * pc.D * vis
-    print(json.dumps({"config": f"qwen3_8b_prefill_L16384_window{W}", "kind": "prefill", "window": W, "ms": round(ms, 4),
-                      "flops": fl, "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
-                      "frac_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}), flush=True)
-    del q, k, v, out
-    dc = ai.RAGGED_DECODE
-    lens = dc.kv_lens()
-    kc, vc = build_decode_cache(dc, lens, dev)
-    dl = torch.from_numpy(lens).to(dev)
-    dq = to_dev(dc.q_bits(), dev)[:, :, None, :].contiguous()
-    dout = torch.empty_like(dq)
-    fn = lambda: attn.decode_multi(dq, kc, vc, dl, scale=dc.scale, window=W, out=dout, return_lse=False)  # noqa: E731
-    for _ in range(2):
-        fn()
-    ms = _time_ms(fn, iters, stream, between=lambda i: flush.fill_(i & 0xFF))
-    nb = int(np.minimum(lens, W).sum()) * dc.Hkv * dc.D * 2 * 2
-    print(json.dumps({"config": f"ragged_gqa_decode_B64_window{W}", "kind": "decode", "window": W, "ms": round(ms, 4),
-                      "kv_bytes": nb, "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
-                      "frac_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}), flush=True)
-    del kc, vc
+    if want(f"qwen3_8b_prefill_L16384_window{W}"):
+        pc = ai.QWEN_16K
+        q, k, v = to_dev(pc.q_bits(), dev), to_dev(pc.k_bits(), dev), to_dev(pc.v_bits(), dev)
+        out = torch.empty_like(q)
+        fn = lambda: attn.prefill_ex(q, k, v, causal=True, scale=pc.scale, window=W, out=out, return_lse=False)  # noqa: E731
+        for _ in range(2):
+            fn()
+        ms = _time_ms(fn, iters, stream)
+        i = np.arange(pc.Lq, dtype=np.int64)
+        vis = int(np.minimum(W, i + (pc.Lk - pc.Lq) + 1).sum())
+        fl = 4 * pc.B * pc.Hq * pc.D * vis
+        print(json.dumps({"config": f"qwen3_8b_prefill_L16384_window{W}", "kind": "prefill", "window": W, "ms": round(ms, 4),
+                          "flops": fl, "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
+                          "frac_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}), flush=True)
+        del q, k, v, out
+    if want(f"ragged_gqa_decode_B64_window{W}"):
+        dc = ai.RAGGED_DECODE
+        lens = dc.kv_lens()
+        kc, vc = build_decode_cache(dc, lens, dev)
+        dl = torch.from_numpy(lens).to(dev)
+        dq = to_dev(dc.q_bits(), dev)[:, :, None, :].contiguous()
+        dout = torch.empty_like(dq)
+        fn = lambda: attn.decode_multi(dq, kc, vc, dl, scale=dc.scale, window=W, out=dout, return_lse=False)  # noqa: E731
+        for _ in range(2):
+            fn()
+        ms = _time_ms(fn, iters, stream, between=lambda i: flush.fill_(i & 0xFF))
+        nb = int(np.minimum(lens, W).sum()) * dc.Hkv * dc.D * 2 * 2
+        print(json.dumps({"config": f"ragged_gqa_decode_B64_window{W}", "kind": "decode", "window": W, "ms": round(ms, 4),
+                          "kv_bytes": nb, "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
+                          "frac_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}), flush=True)
+        del kc, vc
     torch.cuda.empty_cache()
 
     decodes = [ai.RAGGED_DECODE] + [ai.gsweep_decode(G) for G in ai.G_SWEEP]
     gen = torch.Generator(device=dev)
+    bf16_ms = None
     for dc in decodes:
+        if not want(dc.name):
+            continue
         lens = dc.kv_lens()
         if dc is ai.RAGGED_DECODE:
             kc, vc = build_decode_cache(dc, lens, dev)
@@ -340,6 +356,9 @@ def all_configs(iters: int):
     # int8 (q8_0-style) caches on the ragged workload: codes uniform on
     # [-128, 127], block scales uniform on [0.5, 1.5) * sqrt(3) / 127
     dc = ai.RAGGED_DECODE
+    q8_t = [T for T in (1, 4) if want(f"q8_{dc.name}_T{T}")]
+    if not q8_t:
+        return
     lens = dc.kv_lens()
     shape = (dc.B, dc.Hkv, dc.Lmax, dc.D)
     sshape = (dc.B, dc.Hkv, dc.Lmax, dc.D // 32)
@@ -349,7 +368,7 @@ def all_configs(iters: int):
     ks = ((torch.rand(sshape, generator=gen, device=dev) + 0.5) * (3 ** 0.5 / 127)).to(torch.float16)
     vs = ((torch.rand(sshape, generator=gen, device=dev) + 0.5) * (3 ** 0.5 / 127)).to(torch.float16)
     dl = torch.from_numpy(lens).to(dev)
-    for T in (1, 4):
+    for T in q8_t:
         dq = torch.randn((dc.B, dc.Hq, T, dc.D), generator=gen, device=dev).to(torch.bfloat16)
         dout = torch.empty_like(dq)
         ws = torch.empty(attn.decode_multi_workspace_bytes(dc.B, dc.Hq, dc.Hkv, T, dc.Lmax, dc.D),
@@ -364,7 +383,7 @@ def all_configs(iters: int):
         rec = {"config": f"q8_{dc.name}_T{T}", "kind": "decode_q8", "B": dc.B, "Hq": dc.Hq, "Hkv": dc.Hkv,
                "T": T, "Lmax": dc.Lmax, "D": dc.D, "sum_lens": int(lens.sum()), "ms": round(ms, 4),
                "kv_bytes": nb, "GB/s": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
-        if T == 1:
+        if T == 1 and bf16_ms is not None:
             rec["bf16_cache_ms"] = round(bf16_ms, 4)
             rec["speedup_vs_bf16_cache"] = round(bf16_ms / ms, 3)
         print(json.dumps(rec), flush=True)
@@ -382,7 +401,7 @@ def main():
               "(the multi-GPU split is described in DESIGN.md, not built)", file=sys.stderr)
         sys.exit(2)
     if args.all_configs:
-        all_configs(max(args.steps, 5))
+        all_configs(max(args.steps, 5), tuple(o for o in args.only.split(",") if o))
         return
     import torch
     import exact_attention_30_amd as attn
