@@ -33,11 +33,6 @@ ATTN_DEV float xor16(float x) { return __shfl_xor(x, 16); }
 
 ATTN_DEV bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
-// Pack two bf16 values held in the low halves (lo16) or high halves (hi16)
-// of two 32-bit words into one word: first operand in the low half.
-ATTN_DEV uint32_t pack_lo16(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
-ATTN_DEV uint32_t pack_hi16(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
-
 // 16-byte global load / store helpers.
 ATTN_DEV u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 // Streaming load (nontemporal hint): for data read once, such as a KV cache

@@ -30,9 +30,10 @@
 //    block, two blocks per 32-key step), up to 16 query heads on the N side per
 //    column block.  K rows are loaded straight from HBM into the A-operand
 //    registers (64 contiguous bytes per lane), no LDS.
-//  * V is transposed through a per-wave LDS tile (8 keys x 8 dims per lane,
-//    byte permutes, 16-byte LDS writes) so that O^T += V^T P^T runs on MFMA
-//    with P^T taken directly from the S^T accumulators.
+//  * V rows go to a per-wave LDS tile as loaded (16-byte writes, rows padded
+//    by 32 bytes against bank conflicts); the V^T operand of O^T += V^T P^T
+//    comes back with ds_read_b64_tr_b16 in the key order of P^T, which is
+//    taken directly from the S^T accumulators.
 //  * The next 32-key block's K and V loads are issued before the current
 //    block is computed (two register sets, 16 KiB per wave in flight; one set
 //    for D = 256 or four query-column blocks, where a second would spill).
@@ -172,8 +173,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
   constexpr int NKR = 2 * KST;           // K registers (16 B each) per 32-key block
   constexpr int VUN = D / 2;             // (8 keys x 8 dims) units per 32-key block
   constexpr int VU = (VUN + 63) / 64;    // units per lane
-  constexpr int VTS = 40;                // V^T row stride in LDS (bf16): 32 keys + pad
-  __shared__ __attribute__((aligned(16))) uint16_t vt[D * VTS];
+  // the block's V rows as loaded, row stride D + 16 (a 32-byte pad, so that
+  // the 8 rows one half-wave's transposing read touches sit on 8 distinct
+  // bank groups)
+  constexpr int VRS = D + 16;
+  __shared__ __attribute__((aligned(16))) uint16_t vt[32 * VRS];
   // int8 caches: the block's K and V scale rows ([2][32 keys][D / 32] binary16)
   __shared__ __attribute__((aligned(16))) uint16_t sct[Q8 ? 2 * 32 * (D / 32) : 2];
 
@@ -381,28 +385,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
   #pragma unroll
           for (int kk = 0; kk < 8; ++kk) vr[iu][kk] = raw.vr[iu][kk];
       }
-      // V block -> V^T in LDS, keys in the order the P^T operand holds them
+      // V block -> LDS, rows as loaded
   #pragma unroll
       for (int iu = 0; iu < VU; ++iu) {
         const int u = lane + 64 * iu;
         if (VUN % 64 == 0 || u < VUN) {
           const int c = u % (D / 8), gg = u / (D / 8);
   #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int w4 = i >> 1;
-            u32x4 t;
-            if (i & 1) {
-              t[0] = pack_hi16(vr[iu][0][w4], vr[iu][1][w4]);
-              t[1] = pack_hi16(vr[iu][2][w4], vr[iu][3][w4]);
-              t[2] = pack_hi16(vr[iu][4][w4], vr[iu][5][w4]);
-              t[3] = pack_hi16(vr[iu][6][w4], vr[iu][7][w4]);
-            } else {
-              t[0] = pack_lo16(vr[iu][0][w4], vr[iu][1][w4]);
-              t[1] = pack_lo16(vr[iu][2][w4], vr[iu][3][w4]);
-              t[2] = pack_lo16(vr[iu][4][w4], vr[iu][5][w4]);
-              t[3] = pack_lo16(vr[iu][6][w4], vr[iu][7][w4]);
-            }
-            st16(vt + (8 * c + i) * VTS + 8 * gg, t);
+          for (int kk = 0; kk < 8; ++kk) {
+            const int row = kk < 4 ? 4 * gg + kk : 16 + 4 * gg + kk - 4;
+            st16(vt + row * VRS + 8 * c, vr[iu][kk]);
           }
         }
       }
@@ -475,7 +467,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
       // O^T += V^T P^T
   #pragma unroll
       for (int db = 0; db < D / 16; ++db) {
-        const bf16x8 vop = as_bf16x8(ld16(vt + (16 * db + ql) * VTS + 8 * g));
+        // V^T operand, lane (ql, g): dim 16 db + ql of key rows 4 g + 0..3 and
+        // 16 + 4 g + 0..3 (the keys of this lane's P^T elements).  The 16
+        // lanes of group g address rows 4 g + (ql >> 2), 4 dims from
+        // 16 db + 4 (ql & 3); the transposing read hands each its own dim.
+        const uint16_t *vp = vt + (4 * g + (ql >> 2)) * VRS + 16 * db + 4 * (ql & 3);
+        const bf16x4 lo = lds_tr16(vp);
+        const bf16x4 hi = lds_tr16(vp + 16 * VRS);
+        const bf16x8 vop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
           o[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[cb], o[cb][db], 0, 0, 0);

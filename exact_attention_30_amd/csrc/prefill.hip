@@ -50,10 +50,6 @@
 #include "kernels.h"
 
 // Scheduling choices (compile-time):
-//  ATTN_PF_PRIO         raise the wave priority around the MFMA sections
-#ifndef ATTN_PF_PRIO
-#define ATTN_PF_PRIO 1
-#endif
 //  ATTN_PF_PV_AHEAD     V^T operand reads issued this many MFMAs ahead
 //  ATTN_PF_QK_AHEAD     K operand reads issued this many MFMAs ahead
 #ifndef ATTN_PF_PV_AHEAD
@@ -61,16 +57,6 @@
 #endif
 #ifndef ATTN_PF_QK_AHEAD
 #define ATTN_PF_QK_AHEAD 4
-#endif
-//  ATTN_PF_QKFIRST      matrix work of a step in the order QK(j), P.V(j-1), so
-//                       the P.V MFMAs still run while the wave starts its
-//                       softmax of tile j
-//  ATTN_PF_ADMA         group A fetches both K(j+1) and V(j) (group B none)
-#ifndef ATTN_PF_QKFIRST
-#define ATTN_PF_QKFIRST 0
-#endif
-#ifndef ATTN_PF_ADMA
-#define ATTN_PF_ADMA 0
 #endif
 //  ATTN_PF_IW           head dims that use prefill_iw_kernel (in-wave pipelined)
 //                       rather than the two-group ping-pong prefill_kernel, as a
@@ -81,15 +67,6 @@
 #endif
 //  ATTN_PF_IW_SPREAD    head dims (bit mask as above) for which prefill_iw_kernel
 //                       spreads its direct loads over the MFMAs
-//  ATTN_PF_AQKDMA       1: prefill_kernel's group A moves both K(j+1) and V(j),
-//                       its direct loads spread over its QK MFMAs
-//  ATTN_PF_AQK_SP       MFMAs between two of those loads (0: spread over all of QK)
-#ifndef ATTN_PF_AQK_SP
-#define ATTN_PF_AQK_SP 0
-#endif
-#ifndef ATTN_PF_AQKDMA
-#define ATTN_PF_AQKDMA 1
-#endif
 #ifndef ATTN_PF_IW_SPREAD
 #define ATTN_PF_IW_SPREAD 4
 #endif
@@ -98,12 +75,6 @@
 #endif
 #ifndef ATTN_PF_IW_V2
 #define ATTN_PF_IW_V2 2
-#endif
-//  ATTN_PF_ORDER        1: consecutive MFMAs share their B operand (Q^T in S^T,
-//                       P^T in O^T), so one operand of the matrix core stays
-//                       unchanged across them
-#ifndef ATTN_PF_ORDER
-#define ATTN_PF_ORDER 0
 #endif
 //  ATTN_PF_BK128        key-tile size for D = 128
 #ifndef ATTN_PF_BK128
@@ -263,8 +234,7 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
   auto pv = [&](const uint16_t *vs_) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < (D / 32) * (BK / 16); ++i) {
-      const int db = ATTN_PF_ORDER ? i % (D / 32) : i / (BK / 16);
-      const int kb = ATTN_PF_ORDER ? i / (D / 32) : i % (BK / 16);
+      const int db = i / (BK / 16), kb = i % (BK / 16);
       const uint16_t *vp = vs_ + 16 * kb * D + voff(db);
       const bf16x4 lo = lds_tr16(vp);
       const bf16x4 hi = lds_tr16(vp + 8 * D);
@@ -371,14 +341,13 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
   auto gemm = [&](int jj, const uint16_t *ks_, const uint16_t *vs_, auto loads, auto nld)
       __attribute__((always_inline)) {
     constexpr int NLD = decltype(nld)::value;
-    if (!ATTN_PF_QKFIRST && active(jj - 1)) pv(vs_);
+    if (active(jj - 1)) pv(vs_);
     if (NLD > 0 || active(jj)) {
 #pragma unroll
       for (int rb = 0; rb < BK / 32; ++rb) s[rb] = f32x16{};
 #pragma unroll
       for (int i = 0; i < (BK / 32) * (D / 16); ++i) {
-        const int rb = ATTN_PF_ORDER ? i % (BK / 32) : i / (D / 16);
-        const int ks = ATTN_PF_ORDER ? i / (BK / 32) : i % (D / 16);
+        const int rb = i / (D / 16), ks = i % (D / 16);
         s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(ks_ + 32 * rb * D + koff(ks))), qf[ks], s[rb],
                                                         0, 0, 0);
       }
@@ -387,7 +356,7 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
       // load after every SP-th MFMA
       constexpr int N = (BK / 32) * (D / 16);
       constexpr int A = ATTN_PF_QK_AHEAD;
-      constexpr int SP = ATTN_PF_AQK_SP > 0 ? ATTN_PF_AQK_SP : (NLD > 0 && N / NLD > 0 ? N / NLD : 1);
+      constexpr int SP = NLD > 0 && N / NLD > 0 ? N / NLD : 1;
       __builtin_amdgcn_sched_group_barrier(0x100, A, 0);
 #pragma unroll
       for (int i = 0; i < N; ++i) {
@@ -396,7 +365,6 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
         if (i < N - A) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     }
-    if (ATTN_PF_QKFIRST && active(jj - 1)) pv(vs_);
   };
   auto soft = [&](int jj) __attribute__((always_inline)) {
     if (!active(jj)) return;
@@ -422,10 +390,9 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
   // its QK MFMAs, then the softmax of tile j.  Group B runs the softmax of
   // tile j-1, then G(j).  So the exponentials of one wave execute next to the
   // MFMAs of its SIMD neighbour, and no wave stalls on a burst of loads (a
-  // direct load holds its wave until the CU's address unit takes it).  Both target buffers were last read in step j-1.  A group's
-  // direct loads are complete before its next LDS reads (those loads and the
-  // LDS reads would otherwise share one wait counter), and the step ends with
-  // every wave's loads complete and a workgroup barrier, which publishes them.
+  // direct load holds its wave until the CU's address unit takes it).  Both
+  // target buffers were last read in step j-1.  The step ends with every
+  // wave's loads complete and a workgroup barrier, which publishes them.
   auto step = [&](int j, auto parity) __attribute__((always_inline)) {
     constexpr int P = decltype(parity)::value;
     uint16_t *kcur = P ? kb1 : kb0;
@@ -435,28 +402,20 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
     auto none = []() __attribute__((always_inline)) {};
     constexpr auto n0 = std::integral_constant<int, 0>{};
     if (grpA) {
-      if (ATTN_PF_PRIO) __builtin_amdgcn_s_setprio(1);
-      if (ATTN_PF_AQKDMA) {
-        // K(j+1) and V(j) among the QK MFMAs (past the last tile: a repeat of
-        // it, never read)
-        gemm(j, kcur, vprev, [&]() __attribute__((always_inline)) {
-          dma(kg, knext, j0 + max(0, min(j + 1, nt - 1)), std::false_type{});
-          dma(vg, vcur, j0 + max(0, min(j, nt - 1)), std::true_type{});
-        }, std::integral_constant<int, 4 * C::DPW>{});
-      } else {
-        gemm(j, kcur, vprev, none, n0);
-      }
-      if (ATTN_PF_PRIO) __builtin_amdgcn_s_setprio(0);
-      if (!ATTN_PF_AQKDMA && j + 1 < nt) dma(kg, knext, j0 + j + 1, std::false_type{});
-      if (!ATTN_PF_AQKDMA && ATTN_PF_ADMA && j < nt) dma(vg, vcur, j0 + j, std::true_type{});
+      __builtin_amdgcn_s_setprio(1);
+      // K(j+1) and V(j) among the QK MFMAs (past the last tile: a repeat of
+      // it, never read)
+      gemm(j, kcur, vprev, [&]() __attribute__((always_inline)) {
+        dma(kg, knext, j0 + max(0, min(j + 1, nt - 1)), std::false_type{});
+        dma(vg, vcur, j0 + max(0, min(j, nt - 1)), std::true_type{});
+      }, std::integral_constant<int, 4 * C::DPW>{});
+      __builtin_amdgcn_s_setprio(0);
       soft(j);
     } else {
-      if (!ATTN_PF_AQKDMA && !ATTN_PF_ADMA && j < nt) dma(vg, vcur, j0 + j, std::true_type{});
       soft(j - 1);
-      if (!ATTN_PF_AQKDMA && !ATTN_PF_ADMA) ATTN_WAIT_VMEM();
-      if (ATTN_PF_PRIO) __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_s_setprio(1);
       gemm(j, kcur, vprev, none, n0);
-      if (ATTN_PF_PRIO) __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_s_setprio(0);
     }
     ATTN_WAIT_VMEM();
     __syncthreads();
@@ -631,8 +590,7 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_iw_kernel(PrefillArgs a
     for (int rb = 0; rb < BK / 32; ++rb) s[rb] = f32x16{};
 #pragma unroll
     for (int i = 0; i < (BK / 32) * (D / 16); ++i) {
-      const int rb = ATTN_PF_ORDER ? i % (BK / 32) : i / (D / 16);
-      const int ks = ATTN_PF_ORDER ? i / (BK / 32) : i % (D / 16);
+      const int rb = i / (D / 16), ks = i % (D / 16);
       s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(ks_ + 32 * rb * D + koff(ks))), qf[ks], s[rb],
                                                       0, 0, 0);
     }
@@ -640,8 +598,7 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_iw_kernel(PrefillArgs a
   auto pv_ops = [&](const uint16_t *vs_) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < (D / 32) * (BK / 16); ++i) {
-      const int db = ATTN_PF_ORDER ? i % (D / 32) : i / (BK / 16);
-      const int kb = ATTN_PF_ORDER ? i / (D / 32) : i % (BK / 16);
+      const int db = i / (BK / 16), kb = i % (BK / 16);
       const uint16_t *vp = vs_ + 16 * kb * D + voff(db);
       const bf16x4 lo = lds_tr16(vp);
       const bf16x4 hi = lds_tr16(vp + 8 * D);
