@@ -218,3 +218,43 @@ def test_backward_qwen_4k_sampled(attn):
     size = np.sqrt(case.Lq * G)                        # typical size of those sums
     assert np.abs(sv - want_v).max() <= 2e-2 * size
     assert np.abs(sk).max() <= 2e-2 * size
+
+
+QWEN_BWD_16K = ai.PrefillCase("bwd_qwen3_8b_L16384", 70, B=1, Hq=32, Hkv=8, Lq=16384, Lk=16384, D=128)
+
+
+def test_backward_qwen_16k_sampled(attn):
+    """Qwen3-8B heads at L = 16384, the length the backward is measured at,
+    in the same launch configuration, after the GPU forward: 16 query rows and
+    16 keys (first, last and seeded others) of one KV head (its four query
+    heads) checked against the exact gradient with the one-bf16-step
+    allowance, as at L = 4096 (the fp64 forward of those four heads is the
+    oracle's cost here); every dk and dv of all heads checked against the sum
+    rules."""
+    case = QWEN_BWD_16K
+    qb, kb, vb, gb = case.q_bits(), case.k_bits(), case.v_bits(), case.dout_bits()
+    q, k, v, g = to_dev(qb), to_dev(kb), to_dev(vb), to_dev(gb)
+    out, lse = attn.prefill(q, k, v, causal=True, scale=case.scale)
+    dq, dk, dv = attn.backward(q, k, v, out, g, lse, causal=True, scale=case.scale)
+    torch.cuda.synchronize()
+    qr = ai.sample_rows(case.Lq, 16, [case.wid, 7, 0])
+    kr = ai.sample_rows(case.Lk, 16, [case.wid, 7, 1])
+    G = case.Hq // case.Hkv
+    heads = [3]
+    hq = [h for hk in heads for h in range(hk * G, (hk + 1) * G)]
+    q64, k64, v64, g64 = (ai.bf16_bits_to_f64(x) for x in (qb, kb, vb, gb))
+    q64, g64, k64, v64 = q64[:, hq], g64[:, hq], k64[:, heads], v64[:, heads]
+    ro, rl = oracle.attention(q64, k64, v64, True, case.scale)
+    wq, wk, wv = oracle.attention_backward_from_forward_sampled(q64, k64, v64, ro, g64, rl, True, case.scale, qr, kr)
+    Tq, Tk, Tv, aq, ak = term_sums(case, q64, k64, v64, g64, ro, rl, 0, qr=qr, kr=kr, one_step=True)
+    del ro, rl, q64, k64, v64, g64
+    check_grad(to_np(dq[:, hq][:, :, qr]), wq, Tq, "dq sampled", extra=aq)
+    check_grad(to_np(dk[:, heads][:, :, kr]), wk, Tk, "dk sampled", extra=ak)
+    check_grad(to_np(dv[:, heads][:, :, kr]), wv, Tv, "dv sampled")
+    g_all = ai.bf16_bits_to_f64(gb)
+    sk = dk.float().sum(dim=2).cpu().numpy()
+    sv = dv.float().sum(dim=2).cpu().numpy()
+    want_v = g_all.reshape(case.B, case.Hkv, G, case.Lq, case.D).sum(axis=(2, 3))
+    size = np.sqrt(case.Lq * G)
+    assert np.abs(sv - want_v).max() <= 2e-2 * size
+    assert np.abs(sk).max() <= 2e-2 * size
