@@ -223,3 +223,5 @@ def gsweep_prefill(G: int) -> PrefillCase:
 
 
 D256 = PrefillCase("d256_prefill_L4096", 5, B=1, Hq=16, Hkv=8, Lq=4096, Lk=4096, D=256, variant=256)
+D256_8K = PrefillCase("d256_prefill_L8192", 5, B=1, Hq=16, Hkv=8, Lq=8192, Lk=8192, D=256, variant=256)
+D64_8K = PrefillCase("d64_prefill_L8192", 5, B=1, Hq=32, Hkv=8, Lq=8192, Lk=8192, D=64)

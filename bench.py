@@ -219,7 +219,7 @@ def all_configs(iters: int, only=()):
     def want(name):
         return not only or any(o in name for o in only)
 
-    prefills = [ai.TINY, ai.QWEN_4K, ai.QWEN_16K, ai.QWEN_32K, ai.QWEN_CHUNK, ai.D256]
+    prefills = [ai.TINY, ai.QWEN_4K, ai.QWEN_16K, ai.QWEN_32K, ai.QWEN_CHUNK, ai.D256, ai.D256_8K, ai.D64_8K]
     prefills += [ai.gsweep_prefill(G) for G in ai.G_SWEEP]
     for pc in prefills:
         if not want(pc.name):
