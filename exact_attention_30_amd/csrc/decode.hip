@@ -556,6 +556,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
 #define ATTN_DEC_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | ((((n) >> 4) & 3) << 14))
 // s_waitcnt lgkmcnt(0), other counters left alone
 #define ATTN_DEC_WAIT_LDS() __builtin_amdgcn_s_waitcnt(0xC07F)
+// cache policy of decode_wide_kernel's direct loads: 2 = nontemporal (nt),
+// as for the streaming loads of decode_main_kernel: each K/V row is read once
+#ifndef ATTN_DEC_WCPOL
+#define ATTN_DEC_WCPOL 2
+#endif
 
 // Wide row groups (17 to 64 query rows of a KV head: G * T > 16): the same
 // flat split, pieces and combine as decode_main_kernel, with the matrix work
@@ -688,8 +693,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NC == 1 ? 2 
         const size_t key = (size_t)min(max(kb + row, kmin), k1 - 1);
         const int ck = (lane % CPR) ^ kswz<D>(row);
         const int cv = (lane % CPR) ^ vswz<D>(row);
-        __builtin_amdgcn_global_load_lds((glb_void_t *)(kg + key * D + 8 * ck), (lds_void_t *)(kd + i * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((glb_void_t *)(vg + key * D + 8 * cv), (lds_void_t *)(vd + i * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((glb_void_t *)(kg + key * D + 8 * ck), (lds_void_t *)(kd + i * 512), 16, 0,
+                                         ATTN_DEC_WCPOL);
+        __builtin_amdgcn_global_load_lds((glb_void_t *)(vg + key * D + 8 * cv), (lds_void_t *)(vd + i * 512), 16, 0,
+                                         ATTN_DEC_WCPOL);
       }
     };
 
