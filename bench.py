@@ -397,8 +397,8 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the multi-GPU split is described in DESIGN.md, not built)", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(a split of the work across GPUs is not implemented)", file=sys.stderr)
         sys.exit(2)
     if args.all_configs:
         all_configs(max(args.steps, 5), tuple(o for o in args.only.split(",") if o))

@@ -71,7 +71,7 @@ def test_memory_table(golden_dir):
         assert abs(kv - row["kv_cache"]) <= 0.005 + 1e-12
     rs = g["row_stats"]
     assert acc.row_stats_bytes(rs["heads"], rs["rows"]) == rs["MiB"] * acc.MiB
-    # the benchmark spec's own statement: one Qwen3-8B layer at 16K has a 16 GiB bf16 table
+    # the cost guide's own example: one Qwen3-8B layer (32 query heads) at 16K tokens has a 16 GiB bf16 table
     assert acc.score_table_bytes(1, 32, 16384, 2) == 16 * acc.GiB
 
 
