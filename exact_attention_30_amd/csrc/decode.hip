@@ -903,8 +903,10 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a, int W)
   const int np = (int)(w1 - w0 + 1);
   auto prow = [&](int c) { return ((size_t)(seg + w0 + c) * GW + qi); };
   float M = -__builtin_inff();
+  float x0 = -__builtin_inff();   // this lane's piece lse among the first 64, kept
   for (int c0 = 0; c0 < np; c0 += 64) {
     const float x = (c0 + lane < np) ? a.part_lse[prow(c0 + lane)] : -__builtin_inff();
+    if (c0 == 0) x0 = x;
     M = __builtin_fmaxf(M, x);
   }
 #pragma unroll
@@ -919,10 +921,28 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a, int W)
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) acc[i] = 0.f;
   for (int c0 = 0; c0 < np; c0 += 64) {
-    const float wl = (c0 + lane < np) ? __expf(a.part_lse[prow(c0 + lane)] - M) : 0.f;
+    const float x = c0 == 0 ? x0 : ((c0 + lane < np) ? a.part_lse[prow(c0 + lane)] : -__builtin_inff());
+    const float wl = (c0 + lane < np) ? __expf(x - M) : 0.f;
     Z += wl;
     const int cn = min(64, np - c0);
-    for (int c = 0; c < cn; ++c) {
+    int c = 0;
+    // four pieces' loads issued together, then added in piece order
+    for (; c + 4 <= cn; c += 4) {
+      float pv[4][D / 64];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float *po = a.part_o + prow(c0 + c + u) * D;
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) pv[u][i] = po[lane + 64 * i];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float wgt = __shfl(wl, c + u);
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) acc[i] = __builtin_fmaf(wgt, pv[u][i], acc[i]);
+      }
+    }
+    for (; c < cn; ++c) {
       const float wgt = __shfl(wl, c);
       const float *po = a.part_o + prow(c0 + c) * D;
 #pragma unroll
