@@ -81,6 +81,17 @@ def test_decode_edge_lengths(attn, split):
     run_case(attn, EDGE, split_keys=split)
 
 
+MANY = ai.DecodeCase("many_pieces_D128_G4", 46, B=2, Hq=8, Hkv=2, Lmax=11200, D=128, lens_lo=0, lens_hi=0,
+                     fixed_lens=[11111, 300])
+
+
+def test_decode_many_pieces_per_segment(attn):
+    """The smallest split spreads the 11,111-key sequence over well over 64
+    pieces (a few 32-key blocks each), so the merge of a row's pieces runs
+    over several rounds of lanes, with groups of four and a remainder."""
+    run_case(attn, MANY, split_keys=128)
+
+
 def test_decode_negative_length_is_empty(attn):
     c = ai.DecodeCase("neg_len", 42, B=2, Hq=4, Hkv=4, Lmax=300, D=64, lens_lo=0, lens_hi=0, fixed_lens=[-5, 300])
     lens = np.array([-5, 300], dtype=np.int32)
