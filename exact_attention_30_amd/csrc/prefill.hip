@@ -810,7 +810,25 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a, lon
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
   const float *po = a.part_o + (size_t)row * S * D + lane * PER;
-  for (int s = 0; s < S; ++s) {
+  int s = 0;
+  // four ranges' loads issued together (every range wrote its partial),
+  // then added in range order
+  for (; s + 4 <= S; s += 4) {
+    float x[4][PER];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) x[u][i] = po[(size_t)(s + u) * D + i];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float ws = __shfl(wgt, s + u);
+      if (ws != 0.f) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[i] += ws * x[u][i];
+      }
+    }
+  }
+  for (; s < S; ++s) {
     const float ws = __shfl(wgt, s);
     if (ws != 0.f) {
 #pragma unroll
