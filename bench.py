@@ -140,6 +140,17 @@ def cpu_model() -> str:
     return platform.processor()
 
 
+def host_info() -> dict:
+    """The host the oracle ran on: its logical CPUs (nproc), the CPUs this
+    process may use, and the CPU model; `cores` beside it is the BLAS thread
+    count the oracle actually used."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return {"nproc": os.cpu_count() or 1, "usable_cpus": usable, "cpu": cpu_model()}
+
+
 def cpu_prefill_baseline(case: ai.PrefillCase, qb, kb, vb, seconds: float):
     """The oracle's row mode on sampled query rows of the same prefill.
 
@@ -163,7 +174,7 @@ def cpu_prefill_baseline(case: ai.PrefillCase, qb, kb, vb, seconds: float):
         R = min(case.Lq, R * 2)
     return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
             "sample": f"{rows_done} query rows (sampled per head, all 32 heads) of the L=16384 causal prefill, "
-                      f"fp64 numpy row mode, {spent:.1f} s", "cpu": cpu_model()}
+                      f"fp64 numpy row mode, {spent:.1f} s", **host_info()}
 
 
 def cpu_decode_baseline(case: ai.DecodeCase, lens, seconds: float):
@@ -182,7 +193,8 @@ def cpu_decode_baseline(case: ai.DecodeCase, lens, seconds: float):
         if spent >= seconds:
             break
     return {"value": nbytes / spent / 1e9, "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
-            "sample": f"first {seqs} of the 64 ragged sequences, fp64 numpy, {spent:.1f} s (KV bytes counted as bf16)"}
+            "sample": f"first {seqs} of the 64 ragged sequences, fp64 numpy, {spent:.1f} s (KV bytes counted as bf16)",
+            **host_info()}
 
 
 def _time_ms(fn, iters: int, stream, between=None) -> float:

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libattn.so")
 ATTN_OK = 0
 STATUS_NAMES = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_HEADDIM",
                 -4: "ATTN_ERR_GQA", -5: "ATTN_ERR_SCALE", -6: "ATTN_ERR_HIP", -7: "ATTN_ERR_SPLIT",
-                -8: "ATTN_ERR_WORKSPACE"}
+                -8: "ATTN_ERR_WORKSPACE", -9: "ATTN_ERR_KERNEL"}
 
 
 def _load(path: str = LIB_PATH):
@@ -39,10 +39,12 @@ def _load(path: str = LIB_PATH):
     lib.attn_prefill_workspace_bytes.restype = sz
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
     lib.attn_decode.restype = i
-    lib.attn_decode_ex.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.attn_decode_ex.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.attn_decode_ex.restype = i
     lib.attn_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
     lib.attn_decode_multi.restype = i
+    lib.attn_decode_multi_ex.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.attn_decode_multi_ex.restype = i
     lib.attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp, sz, vp]
     lib.attn_backward.restype = i
     lib.attn_backward_workspace_bytes.argtypes = [i, i, i]
@@ -51,8 +53,6 @@ def _load(path: str = LIB_PATH):
     lib.attn_decode_q8.restype = i
     lib.attn_decode_multi_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.attn_decode_multi_workspace_bytes.restype = sz
-    lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
-    lib.attn_decode_workspace_bytes.restype = sz
     lib.attn_decode_waves.argtypes = [i, i, i, i, i, i]
     lib.attn_decode_waves.restype = i
     lib.attn_status_string.argtypes = [i]
@@ -167,24 +167,21 @@ def decode(q, kcache, vcache, kv_lens, scale: float | None = None, out=None):
 
 
 def decode_ex(q, kcache, vcache, kv_lens, scale: float | None = None, split_keys: int = 0, out=None,
-              return_lse: bool = True, workspace=None):
-    """attn_decode_ex: decode plus lse [B,Hq] fp32, a key-range size override and an optional workspace."""
+              return_lse: bool = True):
+    """attn_decode_ex: decode plus lse [B,Hq] fp32 and a key-range size override (0 = one range per wave)."""
     B, Hq, Hkv, Lmax, D = _decode_shapes(q, kcache, vcache, kv_lens)
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.bfloat16, 3)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if return_lse else None
     scale = default_scale(D) if scale is None else float(scale)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.attn_decode_ex(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(kv_lens), _ptr(out), _ptr(lse), B, Hq,
-                              Hkv, Lmax, D, ctypes.c_float(scale), int(split_keys), _ptr(workspace), ws_bytes,
-                              _stream(q.device)))
+                              Hkv, Lmax, D, ctypes.c_float(scale), int(split_keys), _stream(q.device)))
     return out, lse
 
 
-def decode_multi(q, kcache, vcache, kv_lens, scale: float | None = None, out=None, return_lse: bool = True,
-                 workspace=None, window: int = 0):
-    """attn_decode_multi: q [B,Hq,T,D] (the last T cached tokens of each sequence) -> (out, lse [B,Hq,T]);
-    window > 0 limits each row to its window most recent keys."""
+def _multi_args(q, kcache, vcache, kv_lens, out, return_lse):
     _need(q, "q", torch.bfloat16, 4)
     _need(kcache, "kcache", torch.bfloat16, 4)
     _need(vcache, "vcache", torch.bfloat16, 4)
@@ -198,11 +195,35 @@ def decode_multi(q, kcache, vcache, kv_lens, scale: float | None = None, out=Non
     else:
         _need(out, "out", torch.bfloat16, 4)
     lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device) if return_lse else None
+    return B, Hq, Hkv, T, Lmax, D, out, lse
+
+
+def decode_multi(q, kcache, vcache, kv_lens, scale: float | None = None, out=None, return_lse: bool = True,
+                 workspace=None, window: int = 0):
+    """attn_decode_multi: q [B,Hq,T,D] (the last T cached tokens of each sequence) -> (out, lse [B,Hq,T]);
+    window > 0 limits each row to its window most recent keys."""
+    B, Hq, Hkv, T, Lmax, D, out, lse = _multi_args(q, kcache, vcache, kv_lens, out, return_lse)
     scale = default_scale(D) if scale is None else float(scale)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.attn_decode_multi(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(kv_lens), _ptr(out), _ptr(lse), B, Hq,
                                  Hkv, T, int(window), Lmax, D, ctypes.c_float(scale), _ptr(workspace), ws_bytes,
                                  _stream(q.device)))
+    return out, lse
+
+
+DECODE_KERNELS = {"auto": 0, "main": 1, "wide": 2}
+
+
+def decode_multi_ex(q, kcache, vcache, kv_lens, scale: float | None = None, split_keys: int = 0,
+                    kernel: str = "auto", out=None, return_lse: bool = True, workspace=None, window: int = 0):
+    """attn_decode_multi_ex: decode_multi with a key-range size (0 = one range per wave) and an explicit main
+    kernel ("auto", "main": K/V in registers, "wide": 32-row blocks with K/V staged through LDS)."""
+    B, Hq, Hkv, T, Lmax, D, out, lse = _multi_args(q, kcache, vcache, kv_lens, out, return_lse)
+    scale = default_scale(D) if scale is None else float(scale)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.attn_decode_multi_ex(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(kv_lens), _ptr(out), _ptr(lse), B,
+                                    Hq, Hkv, T, int(window), Lmax, D, ctypes.c_float(scale), int(split_keys),
+                                    DECODE_KERNELS[kernel], _ptr(workspace), ws_bytes, _stream(q.device)))
     return out, lse
 
 
@@ -271,10 +292,6 @@ def decode_multi_workspace_bytes(B, Hq, Hkv, T, Lmax, D) -> int:
     return int(lib.attn_decode_multi_workspace_bytes(B, Hq, Hkv, T, Lmax, D))
 
 
-def decode_workspace_bytes(B, Hq, Hkv, Lmax, D, split_keys=0) -> int:
-    return int(lib.attn_decode_workspace_bytes(B, Hq, Hkv, Lmax, D, split_keys))
-
-
 def decode_waves(B, Hq, Hkv, Lmax, D, split_keys=0) -> int:
     return int(lib.attn_decode_waves(B, Hq, Hkv, Lmax, D, split_keys))
 
@@ -291,5 +308,6 @@ def _decode_shapes(q, kcache, vcache, kv_lens):
     return B, Hq, Hkv, Lmax, D
 
 
-__all__ = ["prefill", "prefill_ex", "prefill_splits", "prefill_workspace_bytes", "decode", "decode_ex", "decode_multi", "decode_q8", "backward", "backward_workspace_bytes", "decode_multi_workspace_bytes", "decode_workspace_bytes", "decode_waves", "AttnError", "lib",
-           "LIB_PATH", "default_scale"]
+__all__ = ["prefill", "prefill_ex", "prefill_splits", "prefill_workspace_bytes", "decode", "decode_ex",
+           "decode_multi", "decode_multi_ex", "decode_q8", "backward", "backward_workspace_bytes",
+           "decode_multi_workspace_bytes", "decode_waves", "AttnError", "lib", "LIB_PATH", "default_scale"]

@@ -1,7 +1,6 @@
 // The C ABI of libattn.so: argument checks, launch shapes, workspace.
 // The public contract (types, layouts, ownership, errors) is in include/attn.h.
 #include <math.h>
-#include <cstdlib>
 #include <mutex>
 
 #include "../../include/attn.h"
@@ -82,13 +81,12 @@ long long decode_block_bound(int B, int Hkv, int GT, int T, int window, int Lmax
   return (long long)B * Hkv * n_hg * ((keys + 31) / 32);
 }
 
-// Whether a decode takes the wide-group kernel.  The environment variable
-// ATTN_DECODE_WIDE overrides the choice: 0 never, 1 whenever the shape allows
-// it (any cache size), unset or anything else: by the block bound.
-bool decode_pick_wide(int D, int GT, bool q8, int B, int Hkv, int T, int window, int Lmax) {
-  const char *e = getenv("ATTN_DECODE_WIDE");
-  if (e != nullptr && e[0] == '0' && e[1] == 0) return false;
-  if (e != nullptr && e[0] == '1' && e[1] == 0) return attn::decode_use_wide(D, GT, q8, attn::kDecodeWideMinBlocks);
+// Whether a decode takes the wide-group kernel: kernel 0 chooses by the
+// block bound, 1 never, 2 always (the caller has checked that the shape
+// allows it).
+bool decode_pick_wide(int D, int GT, bool q8, int B, int Hkv, int T, int window, int Lmax, int kernel = 0) {
+  if (kernel == 1) return false;
+  if (kernel == 2) return true;
   return attn::decode_use_wide(D, GT, q8, decode_block_bound(B, Hkv, GT, T, window, Lmax));
 }
 
@@ -136,20 +134,26 @@ int decode_check(const void *q, const void *kc, const void *vc, const int32_t *l
 
 // kscale / vscale: per-block fp16 scales of int8 caches (both null for bf16
 // caches; q8 says which the caller meant, so a missing scale is an error).
+// kernel: 0 automatic, 1 decode_main_kernel, 2 decode_wide_kernel (must be
+// able to serve the shape, else ATTN_ERR_KERNEL).
 int run_decode(const void *q, const void *kc, const void *vc, const int32_t *lens, void *out, float *lse, int B,
                int Hq, int Hkv, int T, int window, int Lmax, int D, float scale, int split_keys, void *ws,
                size_t ws_bytes, void *stream, bool q8 = false, const void *kscale = nullptr,
-               const void *vscale = nullptr) {
+               const void *vscale = nullptr, int kernel = 0) {
   int st = decode_check(q, kc, vc, lens, out, B, Hq, Hkv, T, Lmax, D, scale);
   if (st != ATTN_OK) return st;
   if (q8 && B > 0 && (kscale == nullptr || vscale == nullptr)) return ATTN_ERR_NULL;
   if (window < 0) return ATTN_ERR_SHAPE;
   if (split_keys != 0 && (split_keys < 0 || split_keys % 128 != 0)) return ATTN_ERR_SPLIT;
+  if (kernel < 0 || kernel > 2) return ATTN_ERR_KERNEL;
+  if (kernel == 2 && !attn::decode_use_wide(D, (Hq / Hkv) * T, q8, attn::kDecodeWideMinBlocks))
+    return ATTN_ERR_KERNEL;
   DecodeShape ds;
   decode_workspace(B, Hq, Hkv, T, D, &ds);
   if (ws != nullptr && ws_bytes < ds.total) return ATTN_ERR_WORKSPACE;
   if (B == 0) return ATTN_OK;
-  const bool wide = decode_pick_wide(D, (Hq / Hkv) * T, q8, B, Hkv, T, window < Lmax ? window : 0, Lmax);
+  const bool wide =
+      decode_pick_wide(D, (Hq / Hkv) * T, q8, B, Hkv, T, window < Lmax ? window : 0, Lmax, kernel);
   st = decode_waves(B, Hq, Hkv, T, Lmax, D, split_keys, q8, wide, &ds.waves);
   if (st != ATTN_OK) return st;
 
@@ -413,10 +417,9 @@ int attn_decode(const void *q, const void *kcache, const void *vcache, const int
 }
 
 int attn_decode_ex(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens, void *out,
-                   float *lse, int B, int Hq, int Hkv, int Lmax, int D, float scale, int split_keys,
-                   void *workspace, size_t workspace_bytes, void *stream) {
-  return run_decode(q, kcache, vcache, kv_lens, out, lse, B, Hq, Hkv, 1, 0, Lmax, D, scale, split_keys, workspace,
-                    workspace_bytes, stream);
+                   float *lse, int B, int Hq, int Hkv, int Lmax, int D, float scale, int split_keys, void *stream) {
+  return run_decode(q, kcache, vcache, kv_lens, out, lse, B, Hq, Hkv, 1, 0, Lmax, D, scale, split_keys, nullptr, 0,
+                    stream);
 }
 
 int attn_decode_multi(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens, void *out,
@@ -424,6 +427,13 @@ int attn_decode_multi(const void *q, const void *kcache, const void *vcache, con
                       void *workspace, size_t workspace_bytes, void *stream) {
   return run_decode(q, kcache, vcache, kv_lens, out, lse, B, Hq, Hkv, T, window, Lmax, D, scale, 0, workspace,
                     workspace_bytes, stream);
+}
+
+int attn_decode_multi_ex(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens, void *out,
+                         float *lse, int B, int Hq, int Hkv, int T, int window, int Lmax, int D, float scale,
+                         int split_keys, int kernel, void *workspace, size_t workspace_bytes, void *stream) {
+  return run_decode(q, kcache, vcache, kv_lens, out, lse, B, Hq, Hkv, T, window, Lmax, D, scale, split_keys,
+                    workspace, workspace_bytes, stream, false, nullptr, nullptr, kernel);
 }
 
 int attn_decode_q8(const void *q, const void *kq, const void *kscale, const void *vq, const void *vscale,
@@ -437,14 +447,6 @@ size_t attn_decode_multi_workspace_bytes(int B, int Hq, int Hkv, int T, int Lmax
   if (B <= 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || !head_dim_ok(D) || Lmax < 1 || T < 1 || T > Lmax) return 0;
   DecodeShape ds;
   decode_workspace(B, Hq, Hkv, T, D, &ds);
-  return ds.total;
-}
-
-size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Lmax, int D, int split_keys) {
-  if (B <= 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || !head_dim_ok(D) || Lmax < 1) return 0;
-  if (split_keys != 0 && (split_keys < 0 || split_keys % 128 != 0)) return 0;
-  DecodeShape ds;
-  decode_workspace(B, Hq, Hkv, 1, D, &ds);
   return ds.total;
 }
 
@@ -466,7 +468,8 @@ const char *attn_status_string(int status) {
     case ATTN_ERR_SCALE: return "scale must be finite";
     case ATTN_ERR_HIP: return "a HIP call or kernel launch failed";
     case ATTN_ERR_SPLIT: return "split_keys must be 0 or a positive multiple of 128";
-    case ATTN_ERR_WORKSPACE: return "workspace smaller than attn_decode_workspace_bytes()";
+    case ATTN_ERR_WORKSPACE: return "workspace smaller than the matching *_workspace_bytes()";
+    case ATTN_ERR_KERNEL: return "kernel choice not 0, 1 or 2, or the chosen kernel cannot serve this shape";
     default: return "unknown status";
   }
 }

@@ -74,7 +74,9 @@ typedef enum {
   ATTN_ERR_HIP = -6,      /* a HIP call or kernel launch failed */
   ATTN_ERR_SPLIT = -7,    /* decode split_keys not 0 and not a positive multiple of 128, or
                              prefill splits outside 0..64 */
-  ATTN_ERR_WORKSPACE = -8 /* workspace given but smaller than the matching *_workspace_bytes() */
+  ATTN_ERR_WORKSPACE = -8, /* workspace given but smaller than the matching *_workspace_bytes() */
+  ATTN_ERR_KERNEL = -9     /* attn_decode_multi_ex: kernel not 0, 1 or 2, or kernel 2 asked for a
+                              shape that kernel does not serve */
 } attn_status;
 
 /*
@@ -179,22 +181,21 @@ int attn_decode(const void *q, const void *kcache, const void *vcache, const int
                 void *out, int B, int Hq, int Hkv, int Lmax, int D, float scale, void *stream);
 
 /*
- * attn_decode_ex -- attn_decode with three extra controls:
+ * attn_decode_ex -- attn_decode with two extra controls:
  *   lse        [B][Hq] fp32 output (natural log; -inf where n_b == 0), may be NULL;
  *   split_keys 0: one key range per resident wave of the device; otherwise a
  *              positive multiple of 128 (else ATTN_ERR_SPLIT): enough ranges
  *              that none would exceed split_keys keys if every sequence had
- *              Lmax keys (at most 4096 ranges);
- *   workspace  caller-owned device buffer of workspace_bytes for the partials;
- *              NULL takes it from the stream-ordered allocator as attn_decode
- *              does.  If non-NULL it must hold at least
- *              attn_decode_workspace_bytes(...) bytes (else ATTN_ERR_WORKSPACE)
- *              and must not be used by other work until this call's kernels
- *              have finished on `stream`.
+ *              Lmax keys (at most 4096 ranges).  Results agree for every
+ *              split up to fp32 rounding of the merge.
+ * The partials live in a workspace taken from HIP's stream-ordered allocator
+ * on `stream`, as for attn_decode (attn_decode_multi_ex takes a caller's).
+ * Validation as attn_decode, with the split_keys check after the size checks
+ * and before the empty-call return.
  */
 int attn_decode_ex(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens,
                    void *out, float *lse, int B, int Hq, int Hkv, int Lmax, int D, float scale,
-                   int split_keys, void *workspace, size_t workspace_bytes, void *stream);
+                   int split_keys, void *stream);
 
 /*
  * attn_decode_multi -- T new query rows per sequence over the ragged cache
@@ -219,16 +220,15 @@ int attn_decode_ex(const void *q, const void *kcache, const void *vcache, const 
  *
  * The G * T rows of one KV head (G = Hq / Hkv) share every K/V read, in
  * groups of up to 64 rows.  1 <= T <= Lmax (else ATTN_ERR_SHAPE).  Key ranges
- * are chosen as attn_decode does; workspace as attn_decode_ex (NULL: taken
- * from the stream-ordered allocator), sized by
- * attn_decode_multi_workspace_bytes.
+ * are chosen as attn_decode does.  workspace: NULL takes the partials from
+ * the stream-ordered allocator; otherwise a caller-owned device buffer of at
+ * least attn_decode_multi_workspace_bytes(...) bytes (else
+ * ATTN_ERR_WORKSPACE), not used by other work until this call's kernels have
+ * finished on `stream`.
  *
  * Groups of 33 to 64 rows over a large cache (at least 32768 32-key blocks
  * by the shapes, D 64 or 128, bf16 caches) take a second kernel with 32-row
- * matrix blocks and K/V staged through LDS; results agree to rounding.  The
- * environment variable ATTN_DECODE_WIDE, read at each call, overrides that
- * choice (here and in attn_decode): "0" never, "1" whenever the group size
- * and head dim allow it.
+ * matrix blocks and K/V staged through LDS; results agree to rounding.
  */
 int attn_decode_multi(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens,
                       void *out, float *lse, int B, int Hq, int Hkv, int T, int window, int Lmax, int D,
@@ -268,11 +268,25 @@ int attn_decode_q8(const void *q, const void *kq, const void *kscale, const void
 size_t attn_decode_multi_workspace_bytes(int B, int Hq, int Hkv, int T, int Lmax, int D);
 
 /*
- * attn_decode_workspace_bytes -- bytes of workspace attn_decode_ex needs for
- * these sizes (the same for every split_keys and device).  Returns 0 for an
- * empty call and for invalid arguments.
+ * attn_decode_multi_ex -- attn_decode_multi with the key-range size of
+ * attn_decode_ex (split_keys) and an explicit choice of main kernel, for tests
+ * and tuning:
+ *   kernel  0: chosen as attn_decode_multi does;
+ *           1: the kernel for row groups of up to 64 rows with K/V streamed
+ *              into registers (every shape);
+ *           2: the wide-group kernel (32-row matrix blocks, K/V staged through
+ *              LDS), whatever the cache size; only for groups of 33 to 64
+ *              rows (G * T > 32), D 64 or 128 (else ATTN_ERR_KERNEL);
+ *           anything else: ATTN_ERR_KERNEL.
+ * All three give the same results up to rounding order.  Everything else,
+ * including the workspace and its size, is as attn_decode_multi; validation
+ * order: as attn_decode_multi, then split_keys, then kernel, then the
+ * workspace size.
  */
-size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Lmax, int D, int split_keys);
+int attn_decode_multi_ex(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens,
+                         void *out, float *lse, int B, int Hq, int Hkv, int T, int window, int Lmax, int D,
+                         float scale, int split_keys, int kernel, void *workspace, size_t workspace_bytes,
+                         void *stream);
 
 /*
  * attn_decode_waves -- the number of key ranges (waves) attn_decode_ex uses

@@ -21,7 +21,10 @@ Pages cited (by title):
                  caches)
 
 Pinned by tests/test_oracle.py (page example, closed forms, invariants,
-brute force).  Every function here is pinned; none is "parity unpinned".
+brute force; the byte and FLOP counters of ``accounting`` against the cost
+guide's per-token KV size and FLOP count and the int8 layout's own arrays),
+tests/test_oracle_q8.py and tests/test_oracle_backward.py.  Every function
+here has such a pin; none is "parity unpinned".
 """
 from .reference import (visible_mask, kv_head_of, attention, attention_rows, decode, combine_partials,
                         attention_probs)

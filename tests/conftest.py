@@ -13,12 +13,6 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: large CPU oracle work (minutes)")
 
 
-def pytest_collection_modifyitems(config, items):
-    # GPU tests fail loudly (not skip) when a GPU run cannot find the library;
-    # on a machine without a GPU they are deselected by -m "not gpu".
-    pass
-
-
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")

@@ -5,8 +5,9 @@ Tolerance (stated for this method's bf16 inputs and outputs with fp32
 softmax statistics and accumulation, unit-normal inputs):
   * out: max |gpu - oracle| <= 1e-2 and mean |gpu - oracle| <= 1e-3;
     where |oracle| >= 4 the bf16 output grid itself is 2^-5 apart (half a
-    step is 0.0156 > 1e-2), so there the bound is one bf16 step of the
-    oracle's magnitude instead;
+    step is 0.0156 > 1e-2, so a correctly rounded output may miss 1e-2),
+    so there the bound is 1e-2 plus half a bf16 step of |oracle|; such
+    elements are counted and reported separately;
   * lse: max |gpu - oracle| <= 1e-3.
 """
 from __future__ import annotations
@@ -41,8 +42,12 @@ def check_out(gpu, ref, what=""):
     small_max = float(err[~big].max()) if np.any(~big) else 0.0
     assert small_max <= OUT_MAX_ABS, f"{what}: max|err| {small_max:.3e} > {OUT_MAX_ABS}"
     if np.any(big):
-        step = np.exp2(np.floor(np.log2(np.abs(ref[big]))) - 7)
-        assert np.all(err[big] <= step), f"{what}: error above one bf16 step where |out| >= 4"
+        half_step = np.exp2(np.floor(np.log2(np.abs(ref[big]))) - 8)
+        bound = OUT_MAX_ABS + half_step
+        worst = float(np.max(err[big] / bound))
+        print(f"[{what}] {int(big.sum())} elements with |oracle| >= 4: max|err| {float(err[big].max()):.3e}, "
+              f"{worst:.2f} of 1e-2 + half a bf16 step")
+        assert worst <= 1.0, f"{what}: error above 1e-2 + half a bf16 step where |out| >= 4"
     mean = float(err.mean())
     assert mean <= OUT_MEAN_ABS, f"{what}: mean|err| {mean:.3e} > {OUT_MEAN_ABS}"
     return small_max, mean

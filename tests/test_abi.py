@@ -27,13 +27,14 @@ def declared_functions():
 def test_library_exports_every_declared_symbol(attn):
     names = declared_functions()
     assert {"attn_prefill", "attn_decode", "attn_decode_ex", "attn_status_string"} <= set(names)
+    assert "attn_decode_workspace_bytes" not in names
     lib = ctypes.CDLL(attn.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_status_strings(attn):
-    for code in range(0, -9, -1):
+    for code in range(0, -10, -1):
         s = attn.lib.attn_status_string(code).decode()
         assert s and s != "unknown status"
     assert attn.lib.attn_status_string(-99).decode() == "unknown status"
@@ -68,9 +69,33 @@ def test_prefill_validation(attn):
     assert prefill(attn, B=0, D=96) == -3          # the other arguments are still checked
 
 
-def decode(attn, split=0, ws=N, ws_bytes=0, lens=P, B=2, Hq=8, Hkv=2, Lmax=4096, D=128, scale=0.1):
-    return attn.lib.attn_decode_ex(P, P, P, lens, P, N, B, Hq, Hkv, Lmax, D, ctypes.c_float(scale), split, ws,
-                                   ws_bytes, None)
+def decode(attn, split=0, lens=P, B=2, Hq=8, Hkv=2, Lmax=4096, D=128, scale=0.1):
+    # the attn_decode_ex signature of include/attn.h, argument by argument:
+    # (q, kcache, vcache, kv_lens, out, lse, B, Hq, Hkv, Lmax, D, scale, split_keys, stream)
+    return attn.lib.attn_decode_ex(P, P, P, lens, P, N, B, Hq, Hkv, Lmax, D, ctypes.c_float(scale), split, None)
+
+
+def multi_ex(attn, split=0, kernel=0, ws=N, ws_bytes=0, B=2, Hq=8, Hkv=2, T=1, window=0, Lmax=4096, D=128):
+    return attn.lib.attn_decode_multi_ex(P, P, P, P, P, N, B, Hq, Hkv, T, window, Lmax, D, ctypes.c_float(0.1),
+                                         split, kernel, ws, ws_bytes, None)
+
+
+def test_boundary_signatures():
+    """The four calls of the boundary take exactly the arguments of their
+    declarations (names and order), with no extra controls."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+
+    def params(name):
+        m = re.search(r"\b" + name + r"\s*\(([^)]*)\)\s*;", text)
+        assert m, name
+        return [re.split(r"[\s*]+", a.strip())[-1] for a in m.group(1).split(",")]
+    assert params("attn_prefill") == ["q", "k", "v", "out", "lse", "B", "Hq", "Hkv", "Lq", "Lk", "D", "causal",
+                                      "scale", "stream"]
+    assert params("attn_decode") == ["q", "kcache", "vcache", "kv_lens", "out", "B", "Hq", "Hkv", "Lmax", "D",
+                                     "scale", "stream"]
+    assert params("attn_decode_ex") == ["q", "kcache", "vcache", "kv_lens", "out", "lse", "B", "Hq", "Hkv", "Lmax",
+                                        "D", "scale", "split_keys", "stream"]
+    assert params("attn_status_string") == ["status"]
 
 
 def test_decode_validation(attn):
@@ -83,12 +108,24 @@ def test_decode_validation(attn):
     assert decode(attn, B=70000) == -2
     assert decode(attn, split=100) == -7
     assert decode(attn, split=-128) == -7
-    need = attn.decode_workspace_bytes(2, 8, 2, 4096, 128, 256)
-    assert need > 0
-    assert decode(attn, split=256, ws=P, ws_bytes=need - 1) == -8
     assert decode(attn, B=0) == 0
+    assert decode(attn, B=0, split=100) == -7      # checked before the empty-call return
     assert attn.lib.attn_decode(N, N, N, N, N, 0, 8, 2, 64, 128, ctypes.c_float(0.1), None) == 0
     assert attn.lib.attn_decode(P, P, P, N, P, 1, 8, 2, 64, 128, ctypes.c_float(0.1), None) == -1
+
+
+def test_decode_multi_ex_validation(attn):
+    need = attn.decode_multi_workspace_bytes(2, 8, 2, 1, 4096, 128)
+    assert need > 0
+    assert multi_ex(attn, split=100) == -7
+    assert multi_ex(attn, kernel=3) == -9
+    assert multi_ex(attn, kernel=-1) == -9
+    assert multi_ex(attn, kernel=2) == -9                       # 4 rows per KV head: not a wide group
+    assert multi_ex(attn, kernel=2, T=16, D=256) == -9          # wide kernel not built for D = 256
+    assert multi_ex(attn, kernel=2, T=16, ws=P, ws_bytes=1) == -8   # a wide group: the kernel is accepted
+    assert multi_ex(attn, kernel=1, ws=P, ws_bytes=need - 1) == -8
+    assert multi_ex(attn, B=0, kernel=1) == 0
+    assert multi_ex(attn, B=0, kernel=2, T=16) == 0
 
 
 def test_decode_workspace_sizes(attn):
@@ -98,14 +135,12 @@ def test_decode_workspace_sizes(attn):
     B, Hq, Hkv, D = 64, 32, 8, 128
     slots = 4096 + B * Hkv
     want = al((B + 1) * 8) + al(slots * 4 * 4) + al(slots * 4 * D * 4)
-    assert attn.decode_workspace_bytes(B, Hq, Hkv, 32768, D, 0) == want
-    assert attn.decode_workspace_bytes(B, Hq, Hkv, 32768, D, 1024) == want     # independent of the split
-    assert attn.decode_workspace_bytes(B, Hq, Hkv, 10, D, 0) == want           # and of Lmax
+    assert attn.decode_multi_workspace_bytes(B, Hq, Hkv, 1, 32768, D) == want
+    assert attn.decode_multi_workspace_bytes(B, Hq, Hkv, 1, 10, D) == want           # independent of Lmax
     # G = 80: two head groups of up to 64 heads per KV head
     slots = 4096 + 3 * 1 * 2
-    assert attn.decode_workspace_bytes(3, 80, 1, 100, 64, 0) == al(4 * 8) + al(slots * 64 * 4) + al(slots * 64 * 64 * 4)
-    assert attn.decode_workspace_bytes(1, 3, 2, 10, 128, 0) == 0          # invalid GQA -> 0
-    assert attn.decode_workspace_bytes(1, 4, 2, 10, 128, 100) == 0        # invalid split -> 0
+    assert attn.decode_multi_workspace_bytes(3, 80, 1, 1, 100, 64) == al(4 * 8) + al(slots * 64 * 4) + al(slots * 64 * 64 * 4)
+    assert attn.decode_multi_workspace_bytes(1, 3, 2, 1, 10, 128) == 0          # invalid GQA -> 0
     # explicit split: enough ranges that none exceeds split_keys at full length (no device needed)
     assert attn.decode_waves(4, 32, 8, 32768, 128, 1024) == 4 * 8 * 32
     assert attn.decode_waves(2, 8, 2, 1000, 128, 256) == 2 * 2 * 4          # ceil(1000/32)*32 = 1024 keys
@@ -179,7 +214,6 @@ def test_decode_multi_validation_and_sizes(attn):
     B, Hq, Hkv, T, D = 2, 8, 1, 16, 64       # G * T = 128 -> two groups of 64
     slots = 4096 + B * 1 * 2
     assert attn.decode_multi_workspace_bytes(B, Hq, Hkv, T, 64, D) == al((B + 1) * 8) + al(slots * 64 * 4) + al(slots * 64 * D * 4)
-    assert attn.decode_multi_workspace_bytes(2, 8, 2, 1, 64, 128) == attn.decode_workspace_bytes(2, 8, 2, 64, 128)
     assert attn.decode_multi_workspace_bytes(2, 8, 2, 0, 64, 128) == 0
     need = attn.decode_multi_workspace_bytes(2, 8, 2, 4, 64, 128)
     assert multi(ws=P, ws_bytes=need - 1) == -8

@@ -143,14 +143,15 @@ def test_decode_caller_workspace(attn):
     kc, vc = decode_cache_on_device(c, lens)
     q = to_dev(c.q_bits())
     ld = torch.from_numpy(lens).to(DEV)
-    need = attn.decode_workspace_bytes(c.B, c.Hq, c.Hkv, c.Lmax, c.D, 256)
+    need = attn.decode_multi_workspace_bytes(c.B, c.Hq, c.Hkv, 1, c.Lmax, c.D)
     ws = torch.empty(need, dtype=torch.uint8, device=DEV)
-    o1, l1 = attn.decode_ex(q, kc, vc, ld, scale=c.scale, split_keys=256, workspace=ws)
+    q4 = q[:, :, None, :].contiguous()
+    o1, l1 = attn.decode_multi_ex(q4, kc, vc, ld, scale=c.scale, split_keys=256, workspace=ws)
     o2, l2 = attn.decode_ex(q, kc, vc, ld, scale=c.scale, split_keys=256)
     torch.cuda.synchronize()
-    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o1[:, :, 0], o2) and torch.equal(l1[:, :, 0], l2)
     with pytest.raises(attn.AttnError):
-        attn.decode_ex(q, kc, vc, ld, scale=c.scale, split_keys=256, workspace=ws[:-1])
+        attn.decode_multi_ex(q4, kc, vc, ld, scale=c.scale, split_keys=256, workspace=ws[:-1])
 
 
 def test_decode_deterministic(attn):
@@ -217,41 +218,29 @@ def test_decode_multi_parity(attn, T, case, _):
     check_lse(to_np(lse), rl, case.name)
 
 
-@pytest.fixture
-def wide_env(monkeypatch):
-    """Set ATTN_DECODE_WIDE (read by the library at each call) for one test."""
-    def set_(v):
-        if v is None:
-            monkeypatch.delenv("ATTN_DECODE_WIDE", raising=False)
-        else:
-            monkeypatch.setenv("ATTN_DECODE_WIDE", v)
-    return set_
-
-
 # the MULTI cases whose row groups have more than 32 rows (the wide kernel's domain)
 WIDE = [m for m in MULTI if m[1].Hq // m[1].Hkv * m[0] > 32]
 
 
-@pytest.mark.parametrize("mode", ["1", "0"])
+@pytest.mark.parametrize("mode", ["wide", "main"])
 @pytest.mark.parametrize("T,case,_", WIDE, ids=lambda x: x.name if hasattr(x, "name") else str(x))
-def test_decode_multi_wide_kernel_parity(attn, wide_env, mode, T, case, _):
-    """Both kernels for wide row groups (forced on and off at small sizes)."""
-    wide_env(mode)
+def test_decode_multi_wide_kernel_parity(attn, mode, T, case, _):
+    """Both kernels for wide row groups (each chosen explicitly at small sizes)."""
     lens = case.kv_lens()
     qb = multi_q_bits(case, T)
     kc, vc = decode_cache_on_device(case, lens)
     ro, rl = multi_reference(case, T, qb, lens)
-    out, lse = attn.decode_multi(to_dev(qb), kc, vc, torch.from_numpy(lens).to(DEV), scale=case.scale)
+    out, lse = attn.decode_multi_ex(to_dev(qb), kc, vc, torch.from_numpy(lens).to(DEV), scale=case.scale,
+                                    kernel=mode)
     torch.cuda.synchronize()
     check_out(to_np(out), ro, f"{case.name} wide={mode}")
     check_lse(to_np(lse), rl, f"{case.name} wide={mode}")
 
 
 @pytest.mark.parametrize("T,window,idx", [(16, 100, 2), (16, 1, 1), (7, 30, 4)])
-def test_decode_multi_wide_kernel_window(attn, wide_env, T, window, idx):
+def test_decode_multi_wide_kernel_window(attn, T, window, idx):
     """The wide kernel with a window: keys before the earliest window start
     hold NaN and must not be read."""
-    wide_env("1")
     case = MULTI[idx][1]
     lens = case.kv_lens()
     qb = multi_q_bits(case, T)
@@ -262,14 +251,15 @@ def test_decode_multi_wide_kernel_window(attn, wide_env, T, window, idx):
             kc[b, :, :start] = float("nan")
             vc[b, :, :start] = float("nan")
     ro, rl = multi_reference(case, T, qb, lens, window=window)
-    out, lse = attn.decode_multi(to_dev(qb), kc, vc, torch.from_numpy(lens).to(DEV), scale=case.scale, window=window)
+    out, lse = attn.decode_multi_ex(to_dev(qb), kc, vc, torch.from_numpy(lens).to(DEV), scale=case.scale,
+                                    window=window, kernel="wide")
     torch.cuda.synchronize()
     check_out(to_np(out), ro, f"{case.name} window={window} wide")
     check_lse(to_np(lse), rl, f"{case.name} window={window} wide")
 
 
 @pytest.mark.timeout(600)
-def test_decode_multi_wide_auto_at_scale(attn, wide_env):
+def test_decode_multi_wide_auto_at_scale(attn):
     """T = 16 at Qwen3-8B heads over a 32768-key ragged cache: large enough
     that the library picks the wide kernel by itself (its bits equal the
     forced run's and differ from the other kernel's), and it matches the
@@ -281,12 +271,9 @@ def test_decode_multi_wide_auto_at_scale(attn, wide_env):
     qb = multi_q_bits(case, T)
     kc, vc = decode_cache_on_device(case, lens)
     q, ld = to_dev(qb), torch.from_numpy(lens).to(DEV)
-    wide_env(None)
     o_auto, l_auto = attn.decode_multi(q, kc, vc, ld, scale=case.scale)
-    wide_env("1")
-    o_on, l_on = attn.decode_multi(q, kc, vc, ld, scale=case.scale)
-    wide_env("0")
-    o_off, _ = attn.decode_multi(q, kc, vc, ld, scale=case.scale)
+    o_on, l_on = attn.decode_multi_ex(q, kc, vc, ld, scale=case.scale, kernel="wide")
+    o_off, _ = attn.decode_multi_ex(q, kc, vc, ld, scale=case.scale, kernel="main")
     torch.cuda.synchronize()
     assert torch.equal(o_auto, o_on) and torch.equal(l_auto, l_on)
     assert not torch.equal(o_on, o_off)

@@ -107,6 +107,54 @@ def test_visible_pairs_counts_the_mask():
     assert acc.prefill_flops(1, 32, 128, 512, 16384, True) == 4 * 32 * 128 * 8257792
 
 
+def test_decode_kv_bytes_is_the_pages_per_token_size(golden_dir):
+    """Decode KV bytes = the cost guide's KV bytes per token (use_cache
+    section: 144 KiB at 8 KV heads, 576 KiB at 32, over 36 layers) divided by
+    the layers, times the keys each sequence reads (lengths clamped to
+    [0, Lmax])."""
+    g = json.load(open(os.path.join(golden_dir, "cost_guide_kv_per_token.json")))
+    m = g["model"]
+    for row in g["rows"]:
+        per_key = row["KiB_per_token"] * acc.KiB // m["layers"]          # one layer: 4 KiB at Hkv = 8
+        assert acc.decode_kv_bytes([1], row["Hkv"], m["D"], 100) == per_key
+        assert acc.decode_kv_bytes([37], row["Hkv"], m["D"], 100) == 37 * per_key
+        # ragged batch by hand: 3 + 0 (empty) + 0 (negative) + 100 (clamped) + 99 keys
+        assert acc.decode_kv_bytes([3, 0, -2, 10 ** 6, 99], row["Hkv"], m["D"], 100) == 202 * per_key
+    assert acc.decode_kv_bytes([1], 8, 128, 10) == 4 * acc.KiB
+    # the ragged workload's seeded lengths: 1,102,942 keys x 4 KiB
+    lens = ai.RAGGED_DECODE.kv_lens()
+    assert int(lens.sum()) == 1102942
+    assert acc.decode_kv_bytes(lens, 8, 128, 32768) == 1102942 * 4096 == 4517650432
+
+
+def test_decode_q8_kv_bytes_counts_the_int8_layout():
+    """int8 caches: the bytes of the codes and binary16 scales the seeded
+    generator actually lays out for those keys (K and V), counted from the
+    arrays themselves; 272 B per key and KV head at D = 128 by hand
+    (2 x (128 codes + 4 scales x 2 B))."""
+    assert acc.decode_q8_kv_bytes([1], 1, 128, 10) == 2 * (128 + 4 * 2) == 272
+    for D, Hkv, lens, Lmax in [(32, 1, [5], 8), (64, 2, [7, 0, 3], 10), (128, 8, [1, 9], 9), (256, 3, [4, 12], 6)]:
+        case = ai.DecodeCase("q8_bytes", 90, B=len(lens), Hq=Hkv, Hkv=Hkv, Lmax=Lmax, D=D, lens_lo=0, lens_hi=0,
+                             fixed_lens=lens)
+        counted = 0
+        for b, n, kq, vq in case.iter_q8_seqs():
+            if n:
+                counted += sum(x.nbytes for x in (*kq, *vq))
+        assert acc.decode_q8_kv_bytes(lens, Hkv, D, Lmax) == counted, (D, Hkv, lens)
+
+
+def test_decode_flops_is_the_pages_per_token_count():
+    """A decode row over n keys costs the compute-share section's 4 Hq D t
+    FLOPs (t = n), and equals a one-row causal prefill over the same n keys
+    (bottom-right: the row sees them all)."""
+    for lens, Hq, D, Lmax in [([1], 32, 128, 10), ([5, 0, 300, -4, 70000], 32, 128, 32768), ([17, 2], 64, 256, 16)]:
+        n = np.minimum(np.maximum(np.asarray(lens), 0), Lmax)
+        want = sum(acc.attention_flops_at(Hq, D, int(t), 1) for t in n)
+        assert acc.decode_flops(lens, Hq, D, Lmax) == want
+        assert acc.decode_flops(lens, Hq, D, Lmax) == sum(
+            acc.prefill_flops(1, Hq, D, 1, int(t), True) for t in n if t > 0)
+
+
 # ---------------------------------------------------------------------------
 # 3. Closed form: zero scores.  lse_i = ln(#visible keys), out_i = mean of them.
 # ---------------------------------------------------------------------------
@@ -480,6 +528,35 @@ def test_planted_softmax_over_wrong_axis_is_caught(monkeypatch):
     monkeypatch.setattr(ref, "_softmax_rows", wrong_axis)
     with pytest.raises(AssertionError):
         test_softmax_rows_sum_to_one_and_respect_the_mask()
+
+
+def test_planted_accounting_slips_are_caught(golden_dir, monkeypatch):
+    """K/V factor of 2 dropped, a 4-byte element, the scales left out of the
+    int8 count, one head's FLOPs instead of all heads': each fails a pin."""
+    good_kv, good_q8, good_fl = acc.decode_kv_bytes, acc.decode_q8_kv_bytes, acc.decode_flops
+
+    def clamp(lens, Lmax):
+        return np.minimum(np.maximum(np.asarray(lens, dtype=np.int64), 0), Lmax)
+
+    slips = [
+        ("decode_kv_bytes", lambda l, Hkv, D, Lmax, e=2: int(clamp(l, Lmax).sum()) * Hkv * D * e,
+         lambda: test_decode_kv_bytes_is_the_pages_per_token_size(golden_dir)),
+        ("decode_kv_bytes", lambda l, Hkv, D, Lmax, e=2: int(clamp(l, Lmax).sum()) * Hkv * D * 2 * 4,
+         lambda: test_decode_kv_bytes_is_the_pages_per_token_size(golden_dir)),
+        ("decode_kv_bytes", lambda l, Hkv, D, Lmax, e=2: int(np.asarray(l).sum()) * Hkv * D * 2 * e,
+         lambda: test_decode_kv_bytes_is_the_pages_per_token_size(golden_dir)),
+        ("decode_q8_kv_bytes", lambda l, Hkv, D, Lmax: int(clamp(l, Lmax).sum()) * Hkv * 2 * D,
+         test_decode_q8_kv_bytes_counts_the_int8_layout),
+        ("decode_flops", lambda l, Hq, D, Lmax: 4 * D * int(clamp(l, Lmax).sum()),
+         test_decode_flops_is_the_pages_per_token_count),
+    ]
+    for name, bad, pin in slips:
+        monkeypatch.setattr(acc, name, bad)
+        with pytest.raises(AssertionError):
+            pin()
+        monkeypatch.setattr(acc, "decode_kv_bytes", good_kv)
+        monkeypatch.setattr(acc, "decode_q8_kv_bytes", good_q8)
+        monkeypatch.setattr(acc, "decode_flops", good_fl)
 
 
 def test_planted_log2_lse_is_caught(monkeypatch):
