@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libattn.so")
 ATTN_OK = 0
 STATUS_NAMES = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_HEADDIM",
                 -4: "ATTN_ERR_GQA", -5: "ATTN_ERR_SCALE", -6: "ATTN_ERR_HIP", -7: "ATTN_ERR_SPLIT",
-                -8: "ATTN_ERR_WORKSPACE", -9: "ATTN_ERR_KERNEL"}
+                -8: "ATTN_ERR_WORKSPACE", -9: "ATTN_ERR_KERNEL", -10: "ATTN_ERR_SCRATCH"}
 
 
 def _load(path: str = LIB_PATH):
@@ -40,6 +40,10 @@ def _load(path: str = LIB_PATH):
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
     lib.attn_decode.restype = i
     lib.attn_decode_ex.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    lib.attn_decode_noalloc.restype = i
+    lib.attn_decode_noalloc_max_bytes.argtypes = []
+    lib.attn_decode_noalloc_max_bytes.restype = sz
     lib.attn_decode_ex.restype = i
     lib.attn_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
     lib.attn_decode_multi.restype = i
@@ -163,6 +167,20 @@ def decode(q, kcache, vcache, kv_lens, scale: float | None = None, out=None):
     scale = default_scale(D) if scale is None else float(scale)
     _check(lib.attn_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(kv_lens), _ptr(out), B, Hq, Hkv, Lmax, D,
                            ctypes.c_float(scale), _stream(q.device)))
+    return out
+
+
+def decode_noalloc(q, kcache, vcache, kv_lens, scale: float | None = None, out=None):
+    """attn_decode_noalloc: attn_decode with its partials in the library's static device scratch (no allocation
+    by the library; `out` is allocated here only when not given)."""
+    B, Hq, Hkv, Lmax, D = _decode_shapes(q, kcache, vcache, kv_lens)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.bfloat16, 3)
+    scale = default_scale(D) if scale is None else float(scale)
+    _check(lib.attn_decode_noalloc(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(kv_lens), _ptr(out), B, Hq, Hkv, Lmax,
+                                   D, ctypes.c_float(scale), _stream(q.device)))
     return out
 
 
@@ -308,6 +326,7 @@ def _decode_shapes(q, kcache, vcache, kv_lens):
     return B, Hq, Hkv, Lmax, D
 
 
-__all__ = ["prefill", "prefill_ex", "prefill_splits", "prefill_workspace_bytes", "decode", "decode_ex",
+__all__ = ["prefill", "prefill_ex", "prefill_splits", "prefill_workspace_bytes", "decode", "decode_noalloc",
+           "decode_ex",
            "decode_multi", "decode_multi_ex", "decode_q8", "backward", "backward_workspace_bytes",
            "decode_multi_workspace_bytes", "decode_waves", "AttnError", "lib", "LIB_PATH", "default_scale"]

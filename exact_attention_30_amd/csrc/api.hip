@@ -53,13 +53,15 @@ struct DecodeShape {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout: pre [B + 1] int64 | part_lse [slots][GW] | part_o [slots][GW][D],
-// slots = kDecodeMaxWaves + B * Hkv * n_hg (independent of the device); a KV
-// head has G * T query rows, in groups of up to kDecodeGroup (GW = the group size).
-void decode_workspace(int B, int Hq, int Hkv, int T, int D, DecodeShape *ds) {
+// slots = wave_slots + B * Hkv * n_hg, with wave_slots = kDecodeMaxWaves for a
+// size independent of the device; a KV head has G * T query rows, in groups
+// of up to kDecodeGroup (GW = the group size).
+void decode_workspace(int B, int Hq, int Hkv, int T, int D, DecodeShape *ds,
+                      long long wave_slots = attn::kDecodeMaxWaves) {
   const long long GT = (long long)(Hq / Hkv) * T;
   const long long hh = (long long)Hkv * ((GT + attn::kDecodeGroup - 1) / attn::kDecodeGroup);
   const long long gw = GT < attn::kDecodeGroup ? GT : attn::kDecodeGroup;
-  const size_t slots = (size_t)attn::kDecodeMaxWaves + (size_t)B * hh;
+  const size_t slots = (size_t)wave_slots + (size_t)B * hh;
   ds->pre_bytes = align256((size_t)(B + 1) * sizeof(long long));
   ds->part_lse_bytes = align256(slots * gw * sizeof(float));
   ds->part_o_bytes = align256(slots * gw * D * sizeof(float));
@@ -132,14 +134,42 @@ int decode_check(const void *q, const void *kc, const void *vc, const int32_t *l
   return ATTN_OK;
 }
 
+// Static scratch of attn_decode_noalloc: the decode's partials for callers
+// that cannot allocate.  The array is a file-scope device variable, so every
+// device holds its own copy (at its own address) from the library's load on
+// that device until the process ends.  Host code never uses the array's name
+// as an address: the address is looked up per device (scratch_address).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void *g_scratch[64];
+
+// The device address of `scratch` on the current device (looked up once per
+// device, with that device current).
+int scratch_address(void **ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return ATTN_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return ATTN_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return ATTN_OK;
+}
+
 // kscale / vscale: per-block fp16 scales of int8 caches (both null for bf16
 // caches; q8 says which the caller meant, so a missing scale is an error).
 // kernel: 0 automatic, 1 decode_main_kernel, 2 decode_wide_kernel (must be
 // able to serve the shape, else ATTN_ERR_KERNEL).
+// use_scratch: the partials go to the static scratch, laid out for the actual
+// wave count; sizes that need more than kScratchBytes are ATTN_ERR_SCRATCH,
+// and nothing is allocated.
 int run_decode(const void *q, const void *kc, const void *vc, const int32_t *lens, void *out, float *lse, int B,
                int Hq, int Hkv, int T, int window, int Lmax, int D, float scale, int split_keys, void *ws,
                size_t ws_bytes, void *stream, bool q8 = false, const void *kscale = nullptr,
-               const void *vscale = nullptr, int kernel = 0) {
+               const void *vscale = nullptr, int kernel = 0, bool use_scratch = false) {
   int st = decode_check(q, kc, vc, lens, out, B, Hq, Hkv, T, Lmax, D, scale);
   if (st != ATTN_OK) return st;
   if (q8 && B > 0 && (kscale == nullptr || vscale == nullptr)) return ATTN_ERR_NULL;
@@ -156,6 +186,14 @@ int run_decode(const void *q, const void *kc, const void *vc, const int32_t *len
       decode_pick_wide(D, (Hq / Hkv) * T, q8, B, Hkv, T, window < Lmax ? window : 0, Lmax, kernel);
   st = decode_waves(B, Hq, Hkv, T, Lmax, D, split_keys, q8, wide, &ds.waves);
   if (st != ATTN_OK) return st;
+  if (use_scratch) {
+    const int waves = ds.waves;
+    decode_workspace(B, Hq, Hkv, T, D, &ds, waves);
+    ds.waves = waves;
+    if (ds.total > kScratchBytes) return ATTN_ERR_SCRATCH;
+    st = scratch_address(&ws);
+    if (st != ATTN_OK) return st;
+  }
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   void *mem = ws;
@@ -416,6 +454,14 @@ int attn_decode(const void *q, const void *kcache, const void *vcache, const int
                     stream);
 }
 
+int attn_decode_noalloc(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens, void *out,
+                        int B, int Hq, int Hkv, int Lmax, int D, float scale, void *stream) {
+  return run_decode(q, kcache, vcache, kv_lens, out, nullptr, B, Hq, Hkv, 1, 0, Lmax, D, scale, 0, nullptr, 0, stream,
+                    false, nullptr, nullptr, 0, true);
+}
+
+size_t attn_decode_noalloc_max_bytes(void) { return kScratchBytes; }
+
 int attn_decode_ex(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens, void *out,
                    float *lse, int B, int Hq, int Hkv, int Lmax, int D, float scale, int split_keys, void *stream) {
   return run_decode(q, kcache, vcache, kv_lens, out, lse, B, Hq, Hkv, 1, 0, Lmax, D, scale, split_keys, nullptr, 0,
@@ -470,6 +516,7 @@ const char *attn_status_string(int status) {
     case ATTN_ERR_SPLIT: return "split_keys must be 0 or a positive multiple of 128";
     case ATTN_ERR_WORKSPACE: return "workspace smaller than the matching *_workspace_bytes()";
     case ATTN_ERR_KERNEL: return "kernel choice not 0, 1 or 2, or the chosen kernel cannot serve this shape";
+    case ATTN_ERR_SCRATCH: return "sizes need more partials than the static scratch of attn_decode_noalloc holds";
     default: return "unknown status";
   }
 }

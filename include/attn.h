@@ -75,8 +75,10 @@ typedef enum {
   ATTN_ERR_SPLIT = -7,    /* decode split_keys not 0 and not a positive multiple of 128, or
                              prefill splits outside 0..64 */
   ATTN_ERR_WORKSPACE = -8, /* workspace given but smaller than the matching *_workspace_bytes() */
-  ATTN_ERR_KERNEL = -9     /* attn_decode_multi_ex: kernel not 0, 1 or 2, or kernel 2 asked for a
+  ATTN_ERR_KERNEL = -9,    /* attn_decode_multi_ex: kernel not 0, 1 or 2, or kernel 2 asked for a
                               shape that kernel does not serve */
+  ATTN_ERR_SCRATCH = -10   /* attn_decode_noalloc: the sizes need more partials than its static
+                              scratch holds (attn_decode_noalloc_max_bytes()) */
 } attn_status;
 
 /*
@@ -179,6 +181,32 @@ size_t attn_prefill_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int 
  */
 int attn_decode(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens,
                 void *out, int B, int Hq, int Hkv, int Lmax, int D, float scale, void *stream);
+
+/*
+ * attn_decode_noalloc -- attn_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, semantics and results (bit for bit) as
+ * attn_decode, but the partial outputs and log-sum-exps live in one static
+ * device array of the library (attn_decode_noalloc_max_bytes() = 64 MiB),
+ * which each GPU the library runs on holds from the library's load until the
+ * process ends.  The call allocates nothing and enqueues no memset; on the
+ * first call on a device it looks up that device's copy of the array.
+ *
+ * Limit: the partials of these sizes -- (W + B * Hkv * ceil(G / 64)) slots of
+ * min(G, 64) rows of D + 1 fp32 values, W the wave count attn_decode_ex
+ * reports with split_keys = 0 (2048 at G <= 16 and D = 128 on an MI355X),
+ * plus (B + 1) int64 -- must fit in it, else ATTN_ERR_SCRATCH before anything
+ * is enqueued (the ragged 64-sequence decode at Qwen3-8B heads needs 5 MB).
+ * Every call on one GPU uses that GPU's one array: calls that overlap on one
+ * GPU (on different streams, or from different threads) race and give wrong
+ * results; calls ordered on one stream are safe.  Nothing in the array needs
+ * to start at zero (each call writes every partial before it reads it).
+ */
+int attn_decode_noalloc(const void *q, const void *kcache, const void *vcache, const int32_t *kv_lens,
+                        void *out, int B, int Hq, int Hkv, int Lmax, int D, float scale, void *stream);
+
+/* attn_decode_noalloc_max_bytes -- the size of attn_decode_noalloc's static scratch. */
+size_t attn_decode_noalloc_max_bytes(void);
 
 /*
  * attn_decode_ex -- attn_decode with two extra controls:

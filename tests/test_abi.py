@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol(attn):
 
 
 def test_status_strings(attn):
-    for code in range(0, -10, -1):
+    for code in range(0, -11, -1):
         s = attn.lib.attn_status_string(code).decode()
         assert s and s != "unknown status"
     assert attn.lib.attn_status_string(-99).decode() == "unknown status"
