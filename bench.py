@@ -47,12 +47,25 @@ def parse():
                    help="time every prefill and decode configuration (one JSON line each) instead of the step")
     p.add_argument("--only", default="",
                    help="with --all-configs: comma-separated substrings; only configurations whose name contains one")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the per-configuration records the default run adds to its JSON line")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy three times (scale for HBM byte counters)")
     return p.parse_args()
 
 
 COPY_BYTES = 1 << 30
+
+# the configurations the default run also times (5 calls each) and reports
+# under "configs" in its JSON line: every prefill and decode workload shape,
+# the backward at 16K and the int8-cache decode
+SUB_CONFIGS = (
+    "tiny_causal_prefill_L256_D64", "qwen3_8b_prefill_L4096", "qwen3_8b_prefill_L32768",
+    "qwen3_8b_chunked_prefill_Lq512_Lk16384", "d256_prefill_L4096",
+    "gsweep_prefill_G1_L8192", "gsweep_prefill_G8_L8192", "gsweep_prefill_G64_L8192",
+    "gsweep_decode_G1_B32_L8192", "gsweep_decode_G8_B32_L8192", "gsweep_decode_G64_B32_L8192",
+    "qwen3_8b_backward_L16384", "q8_ragged_gqa_decode_B64_L1024_32768_T1",
+)
 
 
 def copy_calibration():
@@ -199,8 +212,13 @@ def cpu_decode_baseline(case: ai.DecodeCase, lens, seconds: float):
 
 def _time_ms(fn, iters: int, stream, between=None) -> float:
     """Mean duration of fn() from HIP events recorded on `stream`; `between`
-    runs outside the timed window before each call (the MALL flush)."""
+    runs outside the timed window before each call (the MALL flush).  The
+    device idles for a second first, so that every configuration starts from
+    the same clock state (the clock follows the power drawn by the work just
+    before, and the configurations run back to back)."""
     import torch
+    torch.cuda.synchronize()
+    time.sleep(1.0)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
     for i, (a, b) in enumerate(evs):
         if between is not None:
@@ -212,7 +230,7 @@ def _time_ms(fn, iters: int, stream, between=None) -> float:
     return float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
 
-def all_configs(iters: int, only=()):
+def all_configs(iters: int, only=(), exact=(), emit=None):
     """Every prefill and decode shape of the workload list, timed on the GPU
     (ONLY: name substrings selecting some of them).
 
@@ -228,7 +246,13 @@ def all_configs(iters: int, only=()):
     stream = torch.cuda.current_stream(dev)
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
 
+    if emit is None:
+        def emit(rec):
+            print(json.dumps(rec), flush=True)
+
     def want(name):
+        if exact:
+            return name in exact
         return not only or any(o in name for o in only)
 
     prefills = [ai.TINY, ai.QWEN_4K, ai.QWEN_16K, ai.QWEN_32K, ai.QWEN_CHUNK, ai.D256, ai.D256_8K, ai.D64_8K]
@@ -245,9 +269,9 @@ def all_configs(iters: int, only=()):
         ms = _time_ms(fn, iters, stream)
         fl = acc.prefill_flops(pc.B, pc.Hq, pc.D, pc.Lq, pc.Lk, True)
         tf = fl / (ms * 1e-3) / 1e12
-        print(json.dumps({"config": pc.name, "kind": "prefill", "B": pc.B, "Hq": pc.Hq, "Hkv": pc.Hkv, "Lq": pc.Lq,
+        emit({"config": pc.name, "kind": "prefill", "B": pc.B, "Hq": pc.Hq, "Hkv": pc.Hkv, "Lq": pc.Lq,
                           "Lk": pc.Lk, "D": pc.D, "ms": round(ms, 4), "flops": fl, "TFLOP/s": round(tf, 1),
-                          "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}), flush=True)
+                          "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
         del q, k, v, out, lse
 
     # backward (dq, dk, dv from the forward's out and lse) at the Qwen3-8B
@@ -269,10 +293,10 @@ def all_configs(iters: int, only=()):
         ms = _time_ms(fn, iters, stream)
         fl = 5 * acc.prefill_flops(pc.B, pc.Hq, pc.D, pc.Lq, pc.Lk, True) // 2
         tf = fl / (ms * 1e-3) / 1e12
-        print(json.dumps({"config": pc.name.replace("prefill", "backward"), "kind": "backward", "B": pc.B,
+        emit({"config": pc.name.replace("prefill", "backward"), "kind": "backward", "B": pc.B,
                           "Hq": pc.Hq, "Hkv": pc.Hkv, "Lq": pc.Lq, "Lk": pc.Lk, "D": pc.D, "causal": True,
                           "ms": round(ms, 4), "flops": fl, "TFLOP/s": round(tf, 1),
-                          "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}), flush=True)
+                          "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
         del q, k, v, g, out, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
 
@@ -291,10 +315,10 @@ def all_configs(iters: int, only=()):
             fn()
         ms = _time_ms(fn, iters, stream, between=lambda i: flush.fill_(i & 0xFF))
         gbps = nb / (ms * 1e-3) / 1e9
-        print(json.dumps({"config": f"multi_query_decode_T{T}_ragged_B64", "kind": "decode_multi", "T": T, "B": dc.B,
+        emit({"config": f"multi_query_decode_T{T}_ragged_B64", "kind": "decode_multi", "T": T, "B": dc.B,
                           "Hq": dc.Hq, "Hkv": dc.Hkv, "Lmax": dc.Lmax, "D": dc.D, "ms": round(ms, 4), "kv_bytes": nb,
                           "GB/s": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
-                          "flops": 4 * dc.D * dc.Hq * T * int(lens.sum())}), flush=True)
+                          "flops": 4 * dc.D * dc.Hq * T * int(lens.sum())})
     del kc, vc
     torch.cuda.empty_cache()
 
@@ -311,9 +335,9 @@ def all_configs(iters: int, only=()):
         i = np.arange(pc.Lq, dtype=np.int64)
         vis = int(np.minimum(W, i + (pc.Lk - pc.Lq) + 1).sum())
         fl = 4 * pc.B * pc.Hq * pc.D * vis
-        print(json.dumps({"config": f"qwen3_8b_prefill_L16384_window{W}", "kind": "prefill", "window": W, "ms": round(ms, 4),
+        emit({"config": f"qwen3_8b_prefill_L16384_window{W}", "kind": "prefill", "window": W, "ms": round(ms, 4),
                           "flops": fl, "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
-                          "frac_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}), flush=True)
+                          "frac_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
         del q, k, v, out
     if want(f"ragged_gqa_decode_B64_window{W}"):
         dc = ai.RAGGED_DECODE
@@ -327,9 +351,9 @@ def all_configs(iters: int, only=()):
             fn()
         ms = _time_ms(fn, iters, stream, between=lambda i: flush.fill_(i & 0xFF))
         nb = int(np.minimum(lens, W).sum()) * dc.Hkv * dc.D * 2 * 2
-        print(json.dumps({"config": f"ragged_gqa_decode_B64_window{W}", "kind": "decode", "window": W, "ms": round(ms, 4),
+        emit({"config": f"ragged_gqa_decode_B64_window{W}", "kind": "decode", "window": W, "ms": round(ms, 4),
                           "kv_bytes": nb, "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
-                          "frac_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}), flush=True)
+                          "frac_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)})
         del kc, vc
     torch.cuda.empty_cache()
 
@@ -356,10 +380,10 @@ def all_configs(iters: int, only=()):
         ms = _time_ms(fn, iters, stream, between=lambda i: flush.fill_(i & 0xFF))
         nb = acc.decode_kv_bytes(lens, dc.Hkv, dc.D, dc.Lmax)
         gbps = nb / (ms * 1e-3) / 1e9
-        print(json.dumps({"config": dc.name, "kind": "decode", "B": dc.B, "Hq": dc.Hq, "Hkv": dc.Hkv,
+        emit({"config": dc.name, "kind": "decode", "B": dc.B, "Hq": dc.Hq, "Hkv": dc.Hkv,
                           "Lmax": dc.Lmax, "D": dc.D, "sum_lens": int(lens.sum()), "ms": round(ms, 4),
                           "kv_bytes": nb, "GB/s": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
-                          "waves": attn.decode_waves(dc.B, dc.Hq, dc.Hkv, dc.Lmax, dc.D)}), flush=True)
+                          "waves": attn.decode_waves(dc.B, dc.Hq, dc.Hkv, dc.Lmax, dc.D)})
         if dc is ai.RAGGED_DECODE:
             bf16_ms = ms
         del kc, vc
@@ -398,7 +422,7 @@ def all_configs(iters: int, only=()):
         if T == 1 and bf16_ms is not None:
             rec["bf16_cache_ms"] = round(bf16_ms, 4)
             rec["speedup_vs_bf16_cache"] = round(bf16_ms / ms, 3)
-        print(json.dumps(rec), flush=True)
+        emit(rec)
     del kq, vq, ks, vs
     torch.cuda.empty_cache()
 
@@ -505,6 +529,19 @@ def main():
                                 "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": dtraffic}},
         "kernel_source_hash": src,
     }
+    if not args.no_configs:
+        # the other workloads, timed the same way (fewer calls each), so that
+        # one bench line carries every configuration's figure
+        del q, k, v, out, lse, kc, vc, dq, dlens, dout, flush
+        torch.cuda.empty_cache()
+        subs = {}
+
+        def keep(r):
+            name = r.pop("config")
+            subs[name] = {kk: r[kk] for kk in ("kind", "ms", "TFLOP/s", "frac_bf16_peak", "GB/s", "frac_hbm_peak",
+                                               "flops", "kv_bytes") if kk in r}
+        all_configs(5, exact=SUB_CONFIGS, emit=keep)
+        rec["configs"] = subs
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_prefill_baseline(pc, qb, kb, vb, args.cpu_seconds)
         rec["decode"]["cpu_baseline"] = cpu_decode_baseline(dc, lens, args.cpu_seconds * 0.5)

@@ -55,12 +55,13 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Workspace layout: pre [B + 1] int64 | part_lse [slots][GW] | part_o [slots][GW][D],
 // slots = wave_slots + B * Hkv * n_hg, with wave_slots = kDecodeMaxWaves for a
 // size independent of the device; a KV head has G * T query rows, in groups
-// of up to kDecodeGroup (GW = the group size).
+// of up to decode_group(D) (GW = the group size).
 void decode_workspace(int B, int Hq, int Hkv, int T, int D, DecodeShape *ds,
                       long long wave_slots = attn::kDecodeMaxWaves) {
   const long long GT = (long long)(Hq / Hkv) * T;
-  const long long hh = (long long)Hkv * ((GT + attn::kDecodeGroup - 1) / attn::kDecodeGroup);
-  const long long gw = GT < attn::kDecodeGroup ? GT : attn::kDecodeGroup;
+  const int grp = attn::decode_group(D);
+  const long long hh = (long long)Hkv * ((GT + grp - 1) / grp);
+  const long long gw = GT < grp ? GT : grp;
   const size_t slots = (size_t)wave_slots + (size_t)B * hh;
   ds->pre_bytes = align256((size_t)(B + 1) * sizeof(long long));
   ds->part_lse_bytes = align256(slots * gw * sizeof(float));
@@ -76,8 +77,8 @@ int g_occ_cache[64][3][3][2][2];
 
 // 32-key blocks of a decode, bounded from the shapes: every sequence at Lmax
 // keys (with a window, the keys its rows can see)
-long long decode_block_bound(int B, int Hkv, int GT, int T, int window, int Lmax) {
-  const long long n_hg = (GT + attn::kDecodeGroup - 1) / attn::kDecodeGroup;
+long long decode_block_bound(int B, int Hkv, int GT, int T, int window, int Lmax, int D) {
+  const long long n_hg = (GT + attn::decode_group(D) - 1) / attn::decode_group(D);
   long long keys = Lmax;
   if (window > 0 && (long long)window + T + 31 < keys) keys = (long long)window + T + 31;
   return (long long)B * Hkv * n_hg * ((keys + 31) / 32);
@@ -89,14 +90,14 @@ long long decode_block_bound(int B, int Hkv, int GT, int T, int window, int Lmax
 bool decode_pick_wide(int D, int GT, bool q8, int B, int Hkv, int T, int window, int Lmax, int kernel = 0) {
   if (kernel == 1) return false;
   if (kernel == 2) return true;
-  return attn::decode_use_wide(D, GT, q8, decode_block_bound(B, Hkv, GT, T, window, Lmax));
+  return attn::decode_use_wide(D, GT, q8, decode_block_bound(B, Hkv, GT, T, window, Lmax, D));
 }
 
 int device_waves(int D, int GT, bool q8, bool wide, int *waves) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return ATTN_ERR_HIP;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return ATTN_ERR_HIP;
-  const int gw = GT < attn::kDecodeGroup ? GT : attn::kDecodeGroup;
+  const int gw = GT < attn::decode_group(D) ? GT : attn::decode_group(D);
   const int ci = (gw + 15) / 16 >= 3 ? 2 : (gw + 15) / 16 - 1;
   const int di = D == 64 ? 0 : (D == 128 ? 1 : 2);
   std::lock_guard<std::mutex> lk(g_occ_mu);
@@ -110,7 +111,7 @@ int device_waves(int D, int GT, bool q8, bool wide, int *waves) {
 int decode_waves(int B, int Hq, int Hkv, int T, int Lmax, int D, int split_keys, bool q8, bool wide, int *waves) {
   const int GT = (Hq / Hkv) * T;
   if (split_keys == 0) return device_waves(D, GT, q8, wide, waves);
-  const double keys = (double)B * Hkv * ((GT + attn::kDecodeGroup - 1) / attn::kDecodeGroup) *
+  const double keys = (double)B * Hkv * ((GT + attn::decode_group(D) - 1) / attn::decode_group(D)) *
                       (double)((Lmax + 31) / 32) * 32.0;
   double w = keys / split_keys;
   if (w < 1) w = 1;
@@ -131,6 +132,9 @@ int decode_check(const void *q, const void *kc, const void *vc, const int32_t *l
   if ((long long)B * Hq * T > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   // element counts must fit comfortably in 64-bit offsets
   if ((double)B * Hkv * (double)Lmax * D > 9.0e18) return ATTN_ERR_SHAPE;
+  // one sequence's cache rows of one KV head are read through a buffer
+  // resource with 32-bit offsets: at most 2^31 - 1 bytes (2 GiB)
+  if ((long long)Lmax * D * 2 >= (1LL << 31)) return ATTN_ERR_SHAPE;
   return ATTN_OK;
 }
 
@@ -224,7 +228,7 @@ int run_decode(const void *q, const void *kc, const void *vc, const int32_t *len
   a.G = Hq / Hkv;
   a.T = T;
   a.window = window < Lmax ? window : 0;   // a window of Lmax or more keys hides nothing
-  a.n_hg = (a.G * T + attn::kDecodeGroup - 1) / attn::kDecodeGroup;
+  a.n_hg = (a.G * T + attn::decode_group(D) - 1) / attn::decode_group(D);
   a.c = scale * kLog2e;
   a.wide = wide ? 1 : 0;
   hipError_t e = attn::launch_decode(a, D, ds.waves, s);

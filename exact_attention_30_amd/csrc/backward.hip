@@ -13,7 +13,11 @@
 // gfx950 design
 //  * No score table: every tile of p is recomputed from q, k and the saved
 //    lse (one exp2 per element), as the forward never stored it.
-//  * dk/dv kernel: a wave owns 32 keys of one KV head and keeps their k and v
+//  * dk/dv kernel for D = 64 and 128 (bwd_dkdv2_kernel): pairs of waves on one
+//    SIMD own 32 keys; one wave of a pair forms S, P (handed to its partner
+//    through LDS) and dV, the other dP, dS and dK, so each holds one operand
+//    and one accumulator set and two waves fit per SIMD.
+//  * dk/dv kernel for D = 256 (bwd_dkdv_kernel): a wave owns 32 keys of one KV head and keeps their k and v
 //    rows as MFMA operands in registers; the workgroup (4 waves, 128 keys)
 //    walks 64-row stages of all G query heads that read the KV head, moving
 //    q, dout, lse and delta straight from global memory into LDS (direct
@@ -101,6 +105,10 @@ ATTN_DEV void sched_interleave() {
 
 }  // namespace
 
+//  ATTN_BWD_PAIRS      dk/dv for D = 64 and 128 on bwd_dkdv2_kernel (paired waves)
+#ifndef ATTN_BWD_PAIRS
+#define ATTN_BWD_PAIRS 1
+#endif
 //  ATTN_BWD_PIPE       dk/dv: both halves of an unmasked stage software-pipelined
 //  ATTN_BWD_VALU_PER   VALU instructions scheduled after each MFMA there
 #ifndef ATTN_BWD_PIPE
@@ -444,6 +452,269 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
 }
 
 // ---------------------------------------------------------------------------
+// dk / dv with paired waves (D = 64, 128)
+// ---------------------------------------------------------------------------
+// Eight waves, two per SIMD: wave w (w < 4) and wave w + 4 share a SIMD and
+// own the same 32 keys.  Wave w keeps the keys' k rows, forms S = Q K^T and
+// P = exp2(S c - lse2), hands P to its partner through LDS and accumulates
+// dV^T += dO^T P; wave w + 4 keeps the v rows, forms dP = dO V^T, then
+// dS = P (dP - delta) with the partner's P, and accumulates dK^T += Q^T dS.
+// Each wave thus holds one operand set and one accumulator set (about half
+// the registers of a wave doing all four products), so two fit per SIMD and
+// the exponentials of one run beside the MFMAs of the other.  Per 64-row
+// stage: [P-waves: S, P -> LDS | partner: dP], barrier, [P-waves: dV |
+// partner: dS, dK]; the same products as bwd_dkdv_kernel, in the same order
+// per accumulator (bit-identical results).
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv2_kernel(BackwardArgs a) {
+  constexpr int NW = 8;
+  constexpr int ROWS = 64;                    // query rows per stage: two halves of 32
+  constexpr int TILE = ROWS * D;
+  constexpr int CPR = D / 8;
+  constexpr int RPB = 512 / D;
+  constexpr int BPW = TILE * 2 / 1024 / NW;   // 1 KiB blocks per wave per tensor and stage
+  static_assert(BPW * NW * 1024 == TILE * 2, "stage must split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) uint16_t qa[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t qb[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t qc[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t da[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t db_[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t dc[TILE];
+  __shared__ __attribute__((aligned(256))) float sa[2 * ROWS];
+  __shared__ __attribute__((aligned(256))) float sb[2 * ROWS];
+  __shared__ __attribute__((aligned(256))) float sc_[2 * ROWS];
+  // P of each pair and half: element rr of lane l at [(rr / 4) * 64 + l][rr % 4]
+  __shared__ __attribute__((aligned(1024))) float pbuf[4][2][16 * 64];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int pair = wu & 3;
+  const bool pwave = wu < 4;                   // forms P and dV (else dP, dS and dK)
+  const int ql = lane & 31, hh = lane >> 5, g16 = lane >> 4, j16 = lane & 15;
+
+  const int nbh = a.B * a.Hkv;
+  const int t = blockIdx.x;
+  const int kbk = t / nbh;
+  const int bh = t - kbk * nbh;
+  const int b = bh / a.Hkv, hkv = bh - b * a.Hkv;
+  const int j0 = kbk * kBwdKeys;
+  const int kw0 = j0 + 32 * pair;              // the pair's first key
+  const int key = kw0 + ql;                    // this lane's key (column)
+  const int off = a.Lk - a.Lq;
+  const int win = a.window;
+
+  // k rows (P-waves) or v rows (partners) of the pair's keys as B operands
+  const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)a.Lk * D;
+  bf16x8 kvf[D / 16];
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const bool in = key < a.Lk;
+    const uint16_t *src = (pwave ? a.k : a.v) + kvbase + (size_t)(in ? key : 0) * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) kvf[ks] = as_bf16x8(in ? ld16(src + 16 * ks) : z);
+  }
+
+  int qlo = 0, qhi = a.Lq;
+  if (a.causal) {
+    qlo = max(0, j0 - off);
+    if (win) qhi = min(a.Lq, j0 + kBwdKeys - 1 - off + win);
+  }
+  qlo = qlo / 32 * 32;
+  const int ntile_h = qhi > qlo ? (qhi - qlo + ROWS - 1) / ROWS : 0;
+  const int ntile = ntile_h * a.G;
+
+  int roff[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) roff[ks] = toff<D>(ql, 2 * ks + hh);
+  int tlo[D / 32], thi[D / 32];
+  {
+    const int r = 4 * hh + (j16 >> 2);
+    const int c = 2 * (g16 & 1) + ((j16 & 3) >> 1);
+#pragma unroll
+    for (int dd = 0; dd < D / 32; ++dd) {
+      tlo[dd] = toff<D>(r, 4 * dd + c) + 4 * (j16 & 1);
+      thi[dd] = toff<D>(r + 8, 4 * dd + c) + 4 * (j16 & 1);
+    }
+  }
+
+  f32x16 acc[D / 32];   // dV^T (P-waves) or dK^T (partners)
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+
+  // stage tile tt into LDS (as bwd_dkdv_kernel, the work spread over 8 waves)
+  auto issue = [&](int tt, uint16_t *qd, uint16_t *dd, float *sd) __attribute__((always_inline)) {
+    const int hq = hkv * a.G + tt / ntile_h;
+    const int i0 = qlo + (tt % ntile_h) * ROWS;
+    const size_t rowbase = ((size_t)b * a.Hq + hq) * a.Lq;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int blk = wu * BPW + i;
+      const int row = blk * RPB + lane / CPR;
+      const int c = (lane % CPR) ^ tswz<D>(row);
+      const size_t grow = rowbase + min(i0 + row, a.Lq - 1);
+      dma_to_lds<16>(a.q + grow * D + 8 * c, qd + blk * 512);
+      dma_to_lds<16>(a.dout + grow * D + 8 * c, dd + blk * 512);
+    }
+    if (wu < 2) {
+      const float *src = wu == 0 ? a.lse2 : a.delta;
+      const size_t grow = rowbase + min(i0 + lane, a.Lq - 1);
+      dma_to_lds<4>(src + grow, sd + ROWS * wu);
+    }
+  };
+  auto wait_tile = [&](bool younger) __attribute__((always_inline)) {
+    if (younger) {
+      if (wu < 2) ATTN_BWD_WAIT_VM(2 * BPW + 1);
+      else ATTN_BWD_WAIT_VM(2 * BPW);
+    } else {
+      ATTN_BWD_WAIT_VM(0);
+    }
+  };
+
+  const float c = a.c;
+  auto skip_half = [&](int i0h) __attribute__((always_inline)) {
+    if (i0h >= a.Lq) return true;
+    return a.causal && (i0h + 31 + off < kw0 || (win && i0h + off - win + 1 > kw0 + 31));
+  };
+  auto cross_half = [&](int i0h) __attribute__((always_inline)) {
+    return i0h + 31 >= a.Lq || (a.causal && (i0h + off < kw0 + 31 || (win && i0h + 31 + off - win + 1 > kw0)));
+  };
+  // 8 MFMAs: acc16 = (rows of the half) x (the pair's keys), A from LDS rows
+  auto rowprod = [&](const uint16_t *xt, f32x16 &r) __attribute__((always_inline)) {
+    r = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(xt + roff[ks])), kvf[ks], r, 0, 0, 0);
+  };
+  // acc^T += X^T Y (k = the half's 32 rows), X^T read transposed from LDS
+  auto colprod = [&](const uint16_t *xt, const bf16x8(&y)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int dd = 0; dd < D / 32; ++dd)
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh)
+        acc[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            tr_operand(xt + 16 * qh * D + tlo[dd], xt + 16 * qh * D + thi[dd]), y[qh], acc[dd], 0, 0, 0);
+  };
+  auto pack16 = [&](const float(&v)[16], bf16x8(&o)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh)
+      o[qh] = pack8(v[8 * qh], v[8 * qh + 1], v[8 * qh + 2], v[8 * qh + 3], v[8 * qh + 4], v[8 * qh + 5], v[8 * qh + 6],
+                    v[8 * qh + 7]);
+  };
+
+  // One stage, for one role (the two roles run separate copies of the loop,
+  // so that each keeps only its own values live; both pass the same
+  // barriers, in the same number and order).
+  auto step = [&](int tt, const uint16_t *qt, const uint16_t *dt, const float *st, uint16_t *qn, uint16_t *dn,
+                  float *sn, auto role) __attribute__((always_inline)) {
+    constexpr bool PW = decltype(role)::value;
+    wait_tile(tt + 1 < ntile);
+    __syncthreads();
+    if (tt + 2 < ntile) issue(tt + 2, qn, dn, sn);
+    const int i0 = qlo + (tt % ntile_h) * ROWS;
+    bool live[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) live[h] = !skip_half(i0 + 32 * h);
+    if constexpr (PW) {
+      bf16x8 pk[2][2];      // P of each half, kept for dV
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (!live[h]) continue;
+        f32x16 s;
+        rowprod(qt + 32 * h * D, s);
+        sched_reads_ahead<D / 16, 1, kQkAhead<D>>();
+        const bool crosses = cross_half(i0 + 32 * h);
+        float pv[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int r = 8 * (rr >> 2) + 4 * hh + (rr & 3);
+          float pe = fast_exp2(__builtin_fmaf(s[rr], c, -st[32 * h + r]));
+          if (crosses) {
+            const int i = i0 + 32 * h + r;
+            const int lim = i + off;
+            const bool vis = i < a.Lq && (!a.causal || (key <= lim && (!win || key > lim - win)));
+            pe = vis ? pe : 0.f;
+          }
+          pv[rr] = pe;
+        }
+        float *pw = &pbuf[pair][h][0];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<f32x4 *>(pw + 4 * (g * 64 + lane)) = f32x4{pv[4 * g], pv[4 * g + 1], pv[4 * g + 2], pv[4 * g + 3]};
+        pack16(pv, pk[h]);
+      }
+      __syncthreads();   // P of every pair is in LDS
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (!live[h]) continue;
+        colprod(dt + 32 * h * D, pk[h]);
+        sched_reads_ahead<2 * (D / 32), 2, kTrAhead<D>>();
+      }
+    } else {
+      f32x16 dp[2];         // dP of each half
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (!live[h]) continue;
+        rowprod(dt + 32 * h * D, dp[h]);
+        sched_reads_ahead<D / 16, 1, kQkAhead<D>>();
+      }
+      __syncthreads();   // the partner's P is in LDS
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (!live[h]) continue;
+        const float *pr = &pbuf[pair][h][0];
+        float dsv[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 p4 = *reinterpret_cast<const f32x4 *>(pr + 4 * (g * 64 + lane));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int rr = 4 * g + i;
+            const int r = 8 * g + 4 * hh + i;
+            dsv[rr] = p4[i] * (dp[h][rr] - st[ROWS + 32 * h + r]);
+          }
+        }
+        bf16x8 sk[2];
+        pack16(dsv, sk);
+        colprod(qt + 32 * h * D, sk);
+        sched_reads_ahead<2 * (D / 32), 2, kTrAhead<D>>();
+      }
+    }
+  };
+  auto run = [&](auto role) __attribute__((always_inline)) {
+    issue(0, qa, da, sa);
+    if (ntile > 1) issue(1, qb, db_, sb);
+    for (int tt = 0; tt < ntile; tt += 3) {
+      step(tt, qa, da, sa, qc, dc, sc_, role);
+      if (tt + 1 >= ntile) break;
+      step(tt + 1, qb, db_, sb, qa, da, sa, role);
+      if (tt + 2 >= ntile) break;
+      step(tt + 2, qc, dc, sc_, qb, db_, sb, role);
+    }
+  };
+
+  ATTN_BWD_WAIT_VM(0);
+  if (ntile > 0) {
+    if (pwave) run(std::true_type{});
+    else run(std::false_type{});
+  }
+
+  // dk = scale dK (partners), dv = dV (P-waves); lane: key column, dims 32 dd + 8 j + 4 hh + (0..3)
+  if (key < a.Lk) {
+    uint16_t *op = (pwave ? a.dv : a.dk) + kvbase + (size_t)key * D;
+    const float scl = pwave ? 1.f : a.scale;
+#pragma unroll
+    for (int dd = 0; dd < D / 32; ++dd)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x4 o4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o4[i] = (__bf16)(acc[dd][4 * j + i] * scl);
+        *reinterpret_cast<bf16x4 *>(op + 32 * dd + 8 * j + 4 * hh) = o4;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dq
 // ---------------------------------------------------------------------------
 // keys per tile of the dq loop: 32 keeps a wave within 256 registers and a
@@ -660,7 +931,10 @@ static hipError_t launch_bwd_t(const BackwardArgs &a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long nkb = (a.Lk + kBwdKeys - 1) / kBwdKeys;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)(nkb * a.B * a.Hkv)), dim3(256), 0, s, a);
+  if (ATTN_BWD_PAIRS && D <= 128)
+    hipLaunchKernelGGL((bwd_dkdv2_kernel<D <= 128 ? D : 128>), dim3((unsigned)(nkb * a.B * a.Hkv)), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)(nkb * a.B * a.Hkv)), dim3(256), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rows_wg = 32 * (kBwdWaves / a.dq_hpw);

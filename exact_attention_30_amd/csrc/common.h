@@ -84,6 +84,28 @@ ATTN_DEV bf16x4 lds_tr16(const uint16_t *p) {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
+// Raw buffer resource over `bytes` bytes from `base` (no stride, the
+// descriptor word of the gfx9 family): loads at offsets at or past `bytes`
+// return zeros instead of reading memory.  The resource type exists only in
+// the device compilation pass; kernel code that uses it is compiled under
+// ATTN_DEVICE_PASS (the host pass only needs the kernels' signatures).
+#if defined(__HIP_DEVICE_COMPILE__)
+#define ATTN_DEVICE_PASS 1
+ATTN_DEV __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+// The same for a base and size that are uniform across the wave but that the
+// compiler may not prove so (they are moved to scalar registers, so the loads
+// take them as an operand directly).
+ATTN_DEV __amdgpu_buffer_rsrc_t buf_rsrc_uniform(const void *base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p), hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  return buf_rsrc(reinterpret_cast<const void *>(((uint64_t)hi << 32) | lo), __builtin_amdgcn_readfirstlane(bytes));
+}
+#else
+#define ATTN_DEVICE_PASS 0
+#endif
+
 // LDS row swizzles.  A tile row is stored unpadded; its 16-byte chunk c sits
 // at chunk c ^ swz(row).  K: the b128 operand reads (16 rows, one chunk) then
 // hit 16 distinct bank groups.  V: the swizzle moves whole 64-byte groups, so

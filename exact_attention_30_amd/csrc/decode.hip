@@ -30,6 +30,10 @@
 //    block, two blocks per 32-key step), up to 16 query heads on the N side per
 //    column block.  K rows are loaded straight from HBM into the A-operand
 //    registers (64 contiguous bytes per lane), no LDS.
+//  * K and V (or their int8 codes) are read with raw buffer loads over the
+//    readable rows of a segment: keys outside them read as zeros, so a load
+//    needs no select, and its offset is one per-lane register per block plus
+//    the instruction's immediate (no 64-bit address arithmetic per load).
 //  * V rows go to a per-wave LDS tile as loaded (16-byte writes, rows padded
 //    by 32 bytes against bank conflicts); the V^T operand of O^T += V^T P^T
 //    comes back with ds_read_b64_tr_b16 in the key order of P^T, which is
@@ -55,18 +59,13 @@
 
 // Load choices (compile-time):
 //  ATTN_DEC_KNT / ATTN_DEC_VNT   nontemporal (streaming) loads for K / V
-//  ATTN_DEC_KNAT                 K operand layout: lane group g, step ks holds
-//                                dims 32 ks + 8 g (each load instruction reads
-//                                64 contiguous bytes per key row) instead of
-//                                dims (D / 4) g + 8 ks
+//  (K operand layout: lane group g, step ks holds dims 32 ks + 8 g, so that
+//  each load instruction reads 64 contiguous bytes per key row)
 #ifndef ATTN_DEC_KNT
 #define ATTN_DEC_KNT 1
 #endif
 #ifndef ATTN_DEC_VNT
 #define ATTN_DEC_VNT 1
-#endif
-#ifndef ATTN_DEC_KNAT
-#define ATTN_DEC_KNAT 1
 #endif
 
 namespace attn {
@@ -212,13 +211,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
   const bool cpos = cexp >= 0.f;
   const float maskval = cpos ? -__builtin_inff() : __builtin_inff();
   const int GT = a.G * a.T;               // query rows of one KV head
-  const int GW = min(GT, kDecodeGroup);
+  const int GW = min(GT, decode_group(D));
 
   while (r < r1) {
     const long long take = min(nb - blk, r1 - r);
     const int hkv = hh / a.n_hg, hg = hh - hkv * a.n_hg;
-    const int gq0 = hg * kDecodeGroup;
-    const int gcnt = min(kDecodeGroup, GT - gq0);
+    const int gq0 = hg * decode_group(D);
+    const int gcnt = min(decode_group(D), GT - gq0);
     const int n = max(0, min(a.lens[b], a.Lmax));
     const int kseg = seg_begin(a, n);
     const int kmin = a.window ? max(0, n - a.T - a.window + 1) : 0;   // keys below are never read
@@ -246,9 +245,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
       const uint16_t *qp = a.q + (((size_t)b * a.Hq + hkv * a.G) * a.T + gq0 + min(qi, gcnt - 1)) * D;
 #pragma unroll
       for (int ks = 0; ks < KST; ++ks)
-        qf[cb][ks] = as_bf16x8(qi < gcnt ? ld16(qp + (Q8              ? 64 * (ks >> 1) + 16 * g + 8 * (ks & 1)
-                                                      : ATTN_DEC_KNAT ? 32 * ks + 8 * g
-                                                                      : (D / 4) * g + 8 * ks))
+        qf[cb][ks] = as_bf16x8(qi < gcnt ? ld16(qp + (Q8 ? 64 * (ks >> 1) + 16 * g + 8 * (ks & 1) : 32 * ks + 8 * g))
                                          : zero4);
     }
     const size_t base = ((size_t)b * a.Hkv + hkv) * (size_t)a.Lmax * D;
@@ -271,20 +268,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
     const uint16_t *ksg = Q8 ? a.kscale + base / 32 : nullptr;
     const uint16_t *vsg = Q8 ? a.vscale + base / 32 : nullptr;
     const uint32_t zero2 = 0u;
+#if ATTN_DEVICE_PASS
+    // Buffer resources over this segment's readable rows [kmin, k1): a key
+    // outside them gets an offset at or past the resource's end (keys below
+    // kmin wrap to offsets near 2^32), and such loads return zeros without
+    // touching memory.  Offsets: a per-lane constant plus (kb - kmin) rows
+    // per block; the step within a block is the instruction's immediate.
+    constexpr int EB = Q8 ? 1 : 2;   // bytes per cached element
+    const auto rk = buf_rsrc(reinterpret_cast<const char *>(Q8 ? (const void *)kq8 : (const void *)kg) +
+                                 (size_t)kmin * D * EB,
+                             (uint32_t)(k1 - kmin) * (D * EB));
+    const auto rv = buf_rsrc(reinterpret_cast<const char *>(Q8 ? (const void *)vq8 : (const void *)vg) +
+                                 (size_t)kmin * D * EB,
+                             (uint32_t)(k1 - kmin) * (D * EB));
     auto load = [&](Raw &raw, int kb) {
+      const int rowb = (kb - kmin) * (D * EB);   // byte offset of the block's first key
       if constexpr (Q8) {
-        // K: 16 codes of dims 64 i + 16 g ... per piece (each instruction reads
-        // 64 contiguous bytes of a row)
-  #pragma unroll
+#pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-          const int key = kb + 16 * rb + ql;
-          const bool in = key < k1 && key >= kmin;
-          const int8_t *p = kq8 + (size_t)key * D + 16 * g;
-  #pragma unroll
-          for (int i = 0; i < Raw::KQ; ++i) raw.kq[rb][i] = in ? ld16_stream(p + 64 * i) : zero4;
+          const int vo = rowb + (16 * rb + ql) * D + 16 * g;
+#pragma unroll
+          for (int i = 0; i < Raw::KQ; ++i) raw.kq[rb][i] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo + 64 * i, 0, 2);
         }
-        // scales: one row per lane (K rows on lanes 0..31, V rows on 32..63),
-        // one load instead of a small load per element group
         {
           const int key = kb + (lane & 31);
           const bool in = key < k1 && key >= kmin;
@@ -298,11 +303,56 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
             raw.sc[1] = v2[1];
           } else {
             const u32x4 v4 = in ? ld16_stream(ps) : zero4;
-  #pragma unroll
+#pragma unroll
             for (int j = 0; j < 4; ++j) raw.sc[j] = v4[j];
           }
         }
-        // V: 8 codes (one 8-dim chunk) of 8 keys per unit
+#pragma unroll
+        for (int iu = 0; iu < VU; ++iu) {
+          const int u = lane + 64 * iu;
+          if (VUN % 64 == 0 || u < VUN) {
+            const int c = u % (D / 8), gg = u / (D / 8);
+            const int v0 = rowb + 4 * gg * D + 8 * c, v1 = v0 + 16 * D;
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk)
+              raw.vq[iu][kk] = __builtin_amdgcn_raw_buffer_load_b64(rv, (kk < 4 ? v0 : v1) + (kk & 3) * D, 0, 2);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const int vo = rowb + (16 * rb + ql) * (D * 2) + 16 * g;
+#pragma unroll
+          for (int ks = 0; ks < KST; ++ks)
+            raw.kr[rb * KST + ks] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo + 64 * ks, 0, ATTN_DEC_KNT ? 2 : 0);
+        }
+#pragma unroll
+        for (int iu = 0; iu < VU; ++iu) {
+          const int u = lane + 64 * iu;
+          if (VUN % 64 == 0 || u < VUN) {
+            const int c = u % (D / 8), gg = u / (D / 8);
+            const int v0 = rowb + 4 * gg * (D * 2) + 16 * c, v1 = v0 + 16 * (D * 2);
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk)
+              raw.vr[iu][kk] =
+                  __builtin_amdgcn_raw_buffer_load_b128(rv, (kk < 4 ? v0 : v1) + (kk & 3) * (D * 2), 0, ATTN_DEC_VNT ? 2 : 0);
+          }
+        }
+      }
+    };
+#else
+    auto load = [&](Raw &, int) {};   // (host pass: the kernel body is not built)
+#endif
+    auto compute = [&](const Raw &raw, int kb) {
+      u32x4 kr[NKR];
+      if constexpr (Q8) {
+        // the scale rows through LDS; each lane then reads the scales it needs
+  #pragma unroll
+        for (int j = 0; j < Raw::SW; ++j)
+          *reinterpret_cast<uint32_t *>(sct + lane * (D / 32) + 2 * j) = raw.sc[j];
+        __syncthreads();
+        // V: each 8-code unit dequantized straight into the block's LDS tile
+        // (rows as loaded), so that no register copy of the whole block is live
   #pragma unroll
         for (int iu = 0; iu < VU; ++iu) {
           const int u = lane + 64 * iu;
@@ -310,52 +360,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
             const int c = u % (D / 8), gg = u / (D / 8);
   #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
-              const int key = kb + (kk < 4 ? 4 * gg + kk : 16 + 4 * gg + kk - 4);
-              const bool in = key < k1 && key >= kmin;
-              const u32x2 *pv = reinterpret_cast<const u32x2 *>(vq8 + (size_t)key * D + 8 * c);
-              raw.vq[iu][kk] = in ? __builtin_nontemporal_load(pv) : u32x2{zero2, zero2};
+              const int row = kk < 4 ? 4 * gg + kk : 16 + 4 * gg + kk - 4;
+              const uint16_t sv = sct[(32 + row) * (D / 32) + c / 4];
+              st16(vt + row * VRS + 8 * c, dequant8(raw.vq[iu][kk][0], raw.vq[iu][kk][1], half_bits_to_float(sv)));
             }
           }
         }
-        return;
-      } else {
-      u32x4(&kr)[NKR] = raw.kr;
-      u32x4(&vr)[VU][8] = raw.vr;
-  #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const int key = kb + 16 * rb + ql;
-        const uint16_t *p = kg + (size_t)key * D;
-  #pragma unroll
-        for (int ks = 0; ks < KST; ++ks) {
-          const uint16_t *pk = p + (ATTN_DEC_KNAT ? 32 * ks + 8 * g : (D / 4) * g + 8 * ks);
-          kr[rb * KST + ks] = (key < k1 && key >= kmin) ? (ATTN_DEC_KNT ? ld16_stream(pk) : ld16(pk)) : zero4;
-        }
-      }
-  #pragma unroll
-      for (int iu = 0; iu < VU; ++iu) {
-        const int u = lane + 64 * iu;
-        if (VUN % 64 == 0 || u < VUN) {
-          const int c = u % (D / 8), gg = u / (D / 8);
-  #pragma unroll
-          for (int kk = 0; kk < 8; ++kk) {
-            const int key = kb + (kk < 4 ? 4 * gg + kk : 16 + 4 * gg + kk - 4);
-            const uint16_t *pv = vg + (size_t)key * D + 8 * c;
-            vr[iu][kk] = (key < k1 && key >= kmin) ? (ATTN_DEC_VNT ? ld16_stream(pv) : ld16(pv)) : zero4;
-          }
-        }
-      }
-      }
-    };
-
-    auto compute = [&](const Raw &raw, int kb) {
-      u32x4 kr[NKR];
-      u32x4 vr[VU][8];
-      if constexpr (Q8) {
-        // the scale rows through LDS; each lane then reads the scales it needs
-  #pragma unroll
-        for (int j = 0; j < Raw::SW; ++j)
-          *reinterpret_cast<uint32_t *>(sct + lane * (D / 32) + 2 * j) = raw.sc[j];
-        __syncthreads();
   #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
   #pragma unroll
@@ -366,35 +376,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NCB == 1 ? 2
             const uint16_t sk = sct[(16 * rb + ql) * (D / 32) + 2 * i + (g >> 1)];
             kr[rb * KST + ks] = dequant8(raw.kq[rb][i][2 * h], raw.kq[rb][i][2 * h + 1], half_bits_to_float(sk));
           }
-  #pragma unroll
-        for (int iu = 0; iu < VU; ++iu) {
-          const int u = lane + 64 * iu;
-          const int c = u % (D / 8), gg = u / (D / 8);
-  #pragma unroll
-          for (int kk = 0; kk < 8; ++kk) {
-            const int row = kk < 4 ? 4 * gg + kk : 16 + 4 * gg + kk - 4;
-            const uint16_t sv = sct[(32 + row) * (D / 32) + c / 4];
-            vr[iu][kk] = dequant8(raw.vq[iu][kk][0], raw.vq[iu][kk][1], half_bits_to_float(sv));
-          }
-        }
       } else {
   #pragma unroll
         for (int i = 0; i < NKR; ++i) kr[i] = raw.kr[i];
+        // V block -> LDS, rows as loaded
   #pragma unroll
-        for (int iu = 0; iu < VU; ++iu)
+        for (int iu = 0; iu < VU; ++iu) {
+          const int u = lane + 64 * iu;
+          if (VUN % 64 == 0 || u < VUN) {
+            const int c = u % (D / 8), gg = u / (D / 8);
   #pragma unroll
-          for (int kk = 0; kk < 8; ++kk) vr[iu][kk] = raw.vr[iu][kk];
-      }
-      // V block -> LDS, rows as loaded
-  #pragma unroll
-      for (int iu = 0; iu < VU; ++iu) {
-        const int u = lane + 64 * iu;
-        if (VUN % 64 == 0 || u < VUN) {
-          const int c = u % (D / 8), gg = u / (D / 8);
-  #pragma unroll
-          for (int kk = 0; kk < 8; ++kk) {
-            const int row = kk < 4 ? 4 * gg + kk : 16 + 4 * gg + kk - 4;
-            st16(vt + row * VRS + 8 * c, vr[iu][kk]);
+            for (int kk = 0; kk < 8; ++kk) {
+              const int row = kk < 4 ? 4 * gg + kk : 16 + 4 * gg + kk - 4;
+              st16(vt + row * VRS + 8 * c, raw.vr[iu][kk]);
+            }
           }
         }
       }
@@ -616,7 +611,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NC == 1 ? 2 
   const bool cpos = cexp >= 0.f;
   const float maskval = cpos ? -__builtin_inff() : __builtin_inff();
   const int GT = a.G * a.T;
-  const int GW = min(GT, kDecodeGroup);
+  const int GW = min(GT, decode_group(D));
 
   // per-lane LDS offsets (elements) of the operands, as in the prefill
   // kernel: K row ql, chunk 2 ks + hf; V^T rows 4 hf + (j16 >> 2) of each
@@ -641,8 +636,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NC == 1 ? 2 
   while (r < r1) {
     const long long take = min(nb - blk, r1 - r);
     const int hkv = hseg / a.n_hg, hg = hseg - hkv * a.n_hg;
-    const int gq0 = hg * kDecodeGroup;
-    const int gcnt = min(kDecodeGroup, GT - gq0);
+    const int gq0 = hg * decode_group(D);
+    const int gcnt = min(decode_group(D), GT - gq0);
     const int n = max(0, min(a.lens[b], a.Lmax));
     const int kseg = seg_begin(a, n);
     const int kmin = a.window ? max(0, n - a.T - a.window + 1) : 0;
@@ -884,7 +879,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a, int W)
   const int b = row / HT, ht = row - b * HT;
   const int lane = threadIdx.x;
   const int hkv = ht / GT, gfull = ht - hkv * GT;   // row within the KV head's G * T rows
-  const int hg = gfull / kDecodeGroup, qi = gfull - hg * kDecodeGroup;
+  const int hg = gfull / decode_group(D), qi = gfull - hg * decode_group(D);
   const long long HH = (long long)a.Hkv * a.n_hg;
   const long long hh = (long long)hkv * a.n_hg + hg;
   const long long nb = a.pre[b + 1] - a.pre[b];
@@ -898,7 +893,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a, int W)
   const long long s0 = HH * a.pre[b] + hh * nb;       // first flat block of the segment
   const long long w0 = wave_of(s0, total, W), w1 = wave_of(s0 + nb - 1, total, W);
   if (w0 == w1) return;  // one wave covered it and wrote the result
-  const int GW = min(GT, kDecodeGroup);
+  const int GW = min(GT, decode_group(D));
   const long long seg = (long long)b * HH + hh;
   const int np = (int)(w1 - w0 + 1);
   auto prow = [&](int c) { return ((size_t)(seg + w0 + c) * GW + qi); };
@@ -991,14 +986,14 @@ constexpr bool kDecodeWide = D <= 128 && (ATTN_DEC_WIDE & (D == 64 ? 1 : 2)) != 
 template <int D>
 static hipError_t launch_d(const DecodeArgs &a, int W, hipStream_t s) {
   const int gt = a.G * a.T;
-  const int gw = gt < kDecodeGroup ? gt : kDecodeGroup;
+  const int gw = gt < decode_group(D) ? gt : decode_group(D);
   const int ncb = (gw + 15) / 16;
   if constexpr (D <= 128) {
     if (a.wide) return launch_w<D, 2>(a, W, s);
   }
   if (ncb == 1) return launch_t<D, 1>(a, W, s);
-  if (ncb == 2) return launch_t<D, 2>(a, W, s);
-  return launch_t<D, 4>(a, W, s);
+  if (ncb == 2 || D == 256) return launch_t<D, 2>(a, W, s);   // (D = 256: groups of at most 32 rows)
+  return launch_t<D, D == 256 ? 2 : 4>(a, W, s);
 }
 
 hipError_t launch_decode(const DecodeArgs &a, int D, int W, hipStream_t s) {
@@ -1013,13 +1008,13 @@ hipError_t launch_decode(const DecodeArgs &a, int D, int W, hipStream_t s) {
 // Resident 64-thread workgroups of the main kernel per CU for GW query rows
 // per wave group (q8: the int8-cache kernel).
 bool decode_use_wide(int D, int GW, bool q8, long long blocks) {
-  const int gw = GW < kDecodeGroup ? GW : kDecodeGroup;
+  const int gw = GW < decode_group(D) ? GW : decode_group(D);
   const bool built = D == 64 ? kDecodeWide<64> : D == 128 ? kDecodeWide<128> : kDecodeWide<256>;
   return built && !q8 && gw > 32 && blocks >= kDecodeWideMinBlocks;
 }
 
 hipError_t decode_waves_per_cu(int D, int GW, bool q8, bool wide, int *out) {
-  const int gw = GW < kDecodeGroup ? GW : kDecodeGroup;
+  const int gw = GW < decode_group(D) ? GW : decode_group(D);
   const int ncb = (gw + 15) / 16;
   const void *f = nullptr;
   if (wide) {
@@ -1033,7 +1028,7 @@ hipError_t decode_waves_per_cu(int D, int GW, bool q8, bool wide, int *out) {
          : reinterpret_cast<const void *>(&decode_main_kernel<DD, NN, false>)
   if (D == 64) { if (ncb == 1) ATTN_PICK(64, 1); else if (ncb == 2) ATTN_PICK(64, 2); else ATTN_PICK(64, 4); }
   else if (D == 128) { if (ncb == 1) ATTN_PICK(128, 1); else if (ncb == 2) ATTN_PICK(128, 2); else ATTN_PICK(128, 4); }
-  else { if (ncb == 1) ATTN_PICK(256, 1); else if (ncb == 2) ATTN_PICK(256, 2); else ATTN_PICK(256, 4); }
+  else { if (ncb == 1) ATTN_PICK(256, 1); else ATTN_PICK(256, 2); }
 #undef ATTN_PICK
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, f, 64, 0);
 }

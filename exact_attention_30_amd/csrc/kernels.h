@@ -47,8 +47,8 @@ struct DecodeArgs {
   int G;            // Hq / Hkv
   int T;            // query rows per sequence and head (1: plain decode)
   int window;       // sliding window: row t sees its `window` most recent keys (0: all)
-  int n_hg;         // groups of up to kDecodeGroup query rows per KV head
-                    // (a KV head's G * T rows; GW = min(G * T, kDecodeGroup))
+  int n_hg;         // groups of up to decode_group(D) query rows per KV head
+                    // (a KV head's G * T rows; GW = min(G * T, decode_group(D)))
   float c;          // scale * log2(e)
   int wide;         // 1: decode_wide_kernel (see decode_use_wide)
 };
@@ -83,6 +83,10 @@ constexpr int kDecodeMaxWaves = 4096;
 #define ATTN_DEC_GROUP 64
 #endif
 constexpr int kDecodeGroup = ATTN_DEC_GROUP;
+// Query rows of one KV head served by one wave at head dim D: kDecodeGroup up
+// to D = 128; 32 at D = 256, where the accumulators of more rows do not fit
+// beside a block of K and V in a wave's registers.
+constexpr int decode_group(int D) { return D == 256 && kDecodeGroup > 32 ? 32 : kDecodeGroup; }
 
 // Fill in the query-row packing (hpw, wph, Bq, n_qblk, n_hg, total) for the
 // kernel that serves head dim D, for a.nsplit key ranges per query block;

@@ -22,15 +22,20 @@
 //    those registers.  V stays row-major in LDS; its V^T operand is read with
 //    ds_read_b64_tr_b16 (a 4 x 16 transpose per 16-lane group), two reads per
 //    MFMA, in the key order the P^T registers hold.
-//  * Tiles move HBM -> LDS with global_load_lds_dwordx4 (no registers, no
-//    ds_write).  Rows are unpadded; a row's 16-byte chunks are XOR-swizzled so
-//    that the b128 K reads and the transposing V reads are free of bank
-//    conflicts.  K and V are double-buffered in four separate LDS arrays.
-//  * Softmax in the log2 domain: p = exp2(s*c - m) with c = scale*log2(e);
-//    the running maximum is raised lazily (ATTN_RESCALE_SLACK), so the O
-//    rescale is skipped on almost every tile.  The row sum adds the fp32
-//    exponentials (before their rounding to bf16), so that the log-sum-exp
-//    is that of the true normaliser.
+//  * Tiles move HBM -> LDS with buffer_load_dwordx4 ... lds (no registers, no
+//    ds_write): a buffer resource per tile (scalar base and size, so rows
+//    past the keys read as zeros) and a fixed offset per lane, so a load
+//    costs no vector instruction.  Rows are unpadded; a row's 16-byte chunks
+//    are XOR-swizzled so that the b128 K reads and the transposing V reads
+//    are free of bank conflicts.  K and V are double-buffered in four
+//    separate LDS arrays.
+//  * Softmax in the log2 domain: p = exp2(s*c - m) with c = scale*log2(e).
+//    The running maximum only has to keep the exponentials from overflowing
+//    the fp32 sums: prefill_kernel exponentiates a tile against it first and
+//    takes the tile's maximum (and rescales O and l) only when some sum
+//    exceeds 2^32; prefill_iw_kernel raises it only past a slack of 2^8.
+//    The row sum adds the fp32 exponentials (before their rounding to
+//    bf16), so that the log-sum-exp is that of the true normaliser.
 //  * Two schedules.  prefill_kernel pairs the waves of a SIMD in two groups
 //    that alternate matrix work and softmax (one group's exponentials run
 //    beside the other group's MFMAs).  prefill_iw_kernel runs one schedule in
@@ -76,6 +81,11 @@
 #ifndef ATTN_PF_IW_V2
 #define ATTN_PF_IW_V2 2
 #endif
+//  ATTN_PF_LAZYMAX      prefill_kernel takes a tile's maximum only when its
+//                       exponentials against the running max would exceed 2^32
+#ifndef ATTN_PF_LAZYMAX
+#define ATTN_PF_LAZYMAX 1
+#endif
 //  ATTN_PF_BK128        key-tile size for D = 128
 #ifndef ATTN_PF_BK128
 #define ATTN_PF_BK128 64
@@ -96,6 +106,7 @@ namespace attn {
 
 template <int D>
 constexpr int kPfThreads = (D == 256 ? ATTN_PF_NW256 : 8) * 64;
+
 
 template <int D, int BK>
 struct PrefillCfg {
@@ -184,15 +195,20 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
   // so their K only meets -inf scores and their V only zero weights.
   auto dma = [&](const uint16_t *g, uint16_t *dst, int j, auto is_v) __attribute__((always_inline)) {
     constexpr bool V = decltype(is_v)::value;
+#if ATTN_DEVICE_PASS
+    // a buffer resource over the tile's rows that exist: the rows past the
+    // end of the keys read as zeros (they are masked); the tile base is
+    // scalar and a lane's offset fixed, so a load takes no vector work
+    const auto rs = buf_rsrc_uniform(g + (size_t)j * BK * D, (uint32_t)min(BK, a.Lk - j * BK) * (D * 2));
 #pragma unroll
     for (int i = 0; i < 2 * C::DPW; ++i) {
       const int blk = (wu % (C::NW / 2)) * 2 * C::DPW + i;
       const int row = blk * C::RPD + lane / C::CPR;
       const int c = (lane % C::CPR) ^ (V ? vswz<D>(row) : kswz<D>(row));
-      const int grow = min(j * BK + row, a.Lk - 1);
-      __builtin_amdgcn_global_load_lds((glb_void_t *)(g + (size_t)grow * D + 8 * c),
-                                       (lds_void_t *)(dst + blk * 512), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(dst + blk * 512), 16,
+                                               (lane / C::CPR) * (D * 2) + 16 * c, blk * 1024, 0, 0);
     }
+#endif
   };
 
   f32x16 o[D / 32];
@@ -254,11 +270,19 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
   };
 
   // Online-softmax update for one tile of S^T (this lane: one query, BK/2
-  // keys): raise the running max if needed, P = exp2(s*c - m) into pb,
-  // row sum into l_run.  MASKED: the tile crosses the diagonal or the end of
+  // keys): P = exp2(s*c - m) into pb, row sum into l_run, the running max
+  // raised when needed.  MASKED: the tile crosses the diagonal or the end of
   // the keys and hidden scores hold maskval.
-  auto softmax = [&](f32x16(&s)[BK / 32], auto masked) {
-    constexpr bool MASKED = decltype(masked)::value;
+  //
+  // The tile maximum is only needed when the exponentials would grow too
+  // large for the fp32 sums (the running max only has to bound them), so the
+  // tile is first exponentiated against the current running max; only if
+  // some lane's tile sum exceeds 2^32 (or is not finite: the first tile,
+  // where the running max is -inf) is the tile maximum taken, the running
+  // max raised, O and l rescaled, and the tile exponentiated again.  The
+  // running max therefore stays an actual maximum of scores seen (never above
+  // the true one), and every exponential stays below 2^32.
+  auto raise_max = [&](const f32x16(&s)[BK / 32]) __attribute__((always_inline)) {
     float red;
     if (cpos) {
       float mx[BK / 32][4];
@@ -299,7 +323,13 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
       for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
       m_run = mnew;
     }
+  };
+  // P = exp2(s*c - m_run) packed to bf16 into pb; returns this lane's sum
+  // of the fp32 exponentials (the lse needs the unrounded normaliser)
+  auto expsum = [&](const f32x16(&s)[BK / 32], auto masked) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
     const float nm = -m_run;
+    float tsum = 0.f;
 #pragma unroll
     for (int rb = 0; rb < BK / 32; ++rb) {
       float p[16];
@@ -311,11 +341,25 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
       }
       pb[2 * rb] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
       pb[2 * rb + 1] = pack8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
-      // row sum of the fp32 exponentials (the lse needs the unrounded normaliser)
       float t8[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) t8[i] = p[i] + p[i + 8];
-      l_run += ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
+      const float rs = ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
+      tsum = rb == 0 ? rs : tsum + rs;
+    }
+    return tsum;
+  };
+  auto softmax = [&](f32x16(&s)[BK / 32], auto masked) {
+    if (ATTN_PF_LAZYMAX) {
+      float tsum = expsum(s, masked);
+      if (wave_any(!(tsum <= 4294967296.f))) {   // also true for inf and NaN
+        raise_max(s);
+        tsum = expsum(s, masked);
+      }
+      l_run += tsum;
+    } else {
+      raise_max(s);
+      l_run += expsum(s, masked);
     }
   };
 
@@ -331,10 +375,50 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
   // the end of phase 2j+1 (double-buffered: K(j) and V(j-1) are read during
   // phases 2j and 2j+1).
   const bool grpA = w < C::NW / 2;
-  f32x16 s[BK / 32];
   auto active = [&](int jj) __attribute__((always_inline)) {
     return jj >= 0 && jj < nt && (j0 + jj) * BK < kend_w && (j0 + jj + 1) * BK > kbeg_w;
   };
+  // hidden scores of tile jj set to maskval (tiles that cross the diagonal,
+  // the end of the keys or a window's lower edge); true if it did
+  auto mask_tile = [&](f32x16(&s)[BK / 32], int jj) __attribute__((always_inline)) {
+    const int k0 = (j0 + jj) * BK;
+    if (!(k0 + BK > kmask_from || k0 < klo_until)) return false;
+    const int lim = a.causal ? min(a.Lk - 1, qrow + off) : a.Lk - 1;
+#pragma unroll
+    for (int rb = 0; rb < BK / 32; ++rb)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int key = k0 + 32 * rb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+        s[rb][rr] = (key <= lim && key >= qlo) ? s[rb][rr] : maskval;
+      }
+    return true;
+  };
+  // S^T of tile jj: the QK MFMAs (their K operand reads ATTN_PF_QK_AHEAD
+  // ahead), with the NLD direct loads of LOADS among them
+  auto qk = [&](f32x16(&s)[BK / 32], const uint16_t *ks_, auto loads, auto nld) __attribute__((always_inline)) {
+    constexpr int NLD = decltype(nld)::value;
+#pragma unroll
+    for (int rb = 0; rb < BK / 32; ++rb) s[rb] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < (BK / 32) * (D / 16); ++i) {
+      const int rb = i / (D / 16), ks = i % (D / 16);
+      s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(ks_ + 32 * rb * D + koff(ks))), qf[ks], s[rb],
+                                                      0, 0, 0);
+    }
+    loads();
+    constexpr int N = (BK / 32) * (D / 16);
+    constexpr int A = ATTN_PF_QK_AHEAD;
+    constexpr int SP = NLD > 0 && N / NLD > 0 ? N / NLD : 1;
+    __builtin_amdgcn_sched_group_barrier(0x100, A, 0);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (NLD > 0 && i % SP == 0 && i / SP < NLD) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+      if (i < N - A) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+
+  f32x16 s[BK / 32];
   // LOADS (NLD direct loads, NLD > 0) go among the QK MFMAs, which then run
   // whether or not this wave sees tile jj (every wave must move its share of
   // the tiles; the scores of a tile it does not see are not used)
@@ -342,46 +426,13 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
       __attribute__((always_inline)) {
     constexpr int NLD = decltype(nld)::value;
     if (active(jj - 1)) pv(vs_);
-    if (NLD > 0 || active(jj)) {
-#pragma unroll
-      for (int rb = 0; rb < BK / 32; ++rb) s[rb] = f32x16{};
-#pragma unroll
-      for (int i = 0; i < (BK / 32) * (D / 16); ++i) {
-        const int rb = i / (D / 16), ks = i % (D / 16);
-        s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(ks_ + 32 * rb * D + koff(ks))), qf[ks], s[rb],
-                                                        0, 0, 0);
-      }
-      loads();
-      // K operand reads ATTN_PF_QK_AHEAD MFMAs ahead of their use, a direct
-      // load after every SP-th MFMA
-      constexpr int N = (BK / 32) * (D / 16);
-      constexpr int A = ATTN_PF_QK_AHEAD;
-      constexpr int SP = NLD > 0 && N / NLD > 0 ? N / NLD : 1;
-      __builtin_amdgcn_sched_group_barrier(0x100, A, 0);
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (NLD > 0 && i % SP == 0 && i / SP < NLD) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-        if (i < N - A) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    }
+    if (NLD > 0 || active(jj))
+      qk(s, ks_, loads, nld);
   };
   auto soft = [&](int jj) __attribute__((always_inline)) {
     if (!active(jj)) return;
-    const int k0 = (j0 + jj) * BK;
-    if (k0 + BK > kmask_from || k0 < klo_until) {
-      const int lim = a.causal ? min(a.Lk - 1, qrow + off) : a.Lk - 1;
-#pragma unroll
-      for (int rb = 0; rb < BK / 32; ++rb)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int key = k0 + 32 * rb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-          s[rb][rr] = (key <= lim && key >= qlo) ? s[rb][rr] : maskval;
-        }
-      softmax(s, std::true_type{});
-    } else {
-      softmax(s, std::false_type{});
-    }
+    if (mask_tile(s, jj)) softmax(s, std::true_type{});
+    else softmax(s, std::false_type{});
   };
 
   // One tile step j (P = j % 2): K(j) is in kb[P], V(j-1) in vb[1-P].
@@ -535,15 +586,17 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_iw_kernel(PrefillArgs a
   // tile j of K or V into LDS: every wave moves DPW blocks of 1 KiB
   auto dma = [&](const uint16_t *g, uint16_t *dst, int j, auto is_v) __attribute__((always_inline)) {
     constexpr bool V = decltype(is_v)::value;
+#if ATTN_DEVICE_PASS
+    const auto rs = buf_rsrc_uniform(g + (size_t)j * BK * D, (uint32_t)min(BK, a.Lk - j * BK) * (D * 2));
 #pragma unroll
     for (int i = 0; i < C::DPW; ++i) {
       const int blk = wu * C::DPW + i;
       const int row = blk * C::RPD + lane / C::CPR;
       const int c = (lane % C::CPR) ^ (V ? vswz<D>(row) : kswz<D>(row));
-      const int grow = min(j * BK + row, a.Lk - 1);
-      __builtin_amdgcn_global_load_lds((glb_void_t *)(g + (size_t)grow * D + 8 * c),
-                                       (lds_void_t *)(dst + blk * 512), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(dst + blk * 512), 16,
+                                               (lane / C::CPR) * (D * 2) + 16 * c, blk * 1024, 0, 0);
     }
+#endif
   };
 
   f32x16 o[D / 32];

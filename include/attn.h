@@ -66,8 +66,9 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = -1,     /* a required pointer is NULL */
   ATTN_ERR_SHAPE = -2,    /* a negative size, Lk = 0 with Lq > 0, causal with Lq > Lk,
-                             Lmax < 1, T outside 1..Lmax, or a size whose element count
-                             overflows */
+                             Lmax < 1, T outside 1..Lmax, Lmax * D >= 2^30 (decode: one
+                             sequence's rows of one KV head must stay below 2 GiB), or a
+                             size whose element count overflows */
   ATTN_ERR_HEADDIM = -3,  /* D not in {64, 128, 256} */
   ATTN_ERR_GQA = -4,      /* Hq < 1, Hkv < 1 or Hq % Hkv != 0 */
   ATTN_ERR_SCALE = -5,    /* scale is NaN or infinite */

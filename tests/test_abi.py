@@ -106,6 +106,8 @@ def test_decode_validation(attn):
     assert decode(attn, Lmax=0) == -2
     assert decode(attn, B=-3) == -2
     assert decode(attn, B=70000) == -2
+    assert decode(attn, Lmax=1 << 23, D=128) == -2       # 2 GiB of rows per sequence and KV head
+    assert decode(attn, Lmax=(1 << 23) - 1, D=128, split=100) == -7   # just below: the sizes pass
     assert decode(attn, split=100) == -7
     assert decode(attn, split=-128) == -7
     assert decode(attn, B=0) == 0

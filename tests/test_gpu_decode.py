@@ -282,6 +282,25 @@ def test_decode_multi_wide_auto_at_scale(attn):
     check_lse(to_np(l_auto), rl, case.name)
 
 
+@pytest.mark.timeout(600)
+def test_decode_multi_d256_wide_group_long_cache(attn):
+    """D = 256 with 64 query rows per KV head (G = 4, T = 16) over a cache of
+    32,768 keys: served as two groups of 32 rows (the largest group whose
+    accumulators fit beside a block of K and V at this head dim), each
+    reading the cache; every sequence against the oracle."""
+    T = 16
+    case = ai.DecodeCase("multi_T16_G4_D256_L32768", 39, B=2, Hq=16, Hkv=4, Lmax=32768, D=256, lens_lo=0,
+                         lens_hi=0, fixed_lens=[32768, 20001])
+    lens = case.kv_lens()
+    qb = multi_q_bits(case, T)
+    kc, vc = decode_cache_on_device(case, lens)
+    out, lse = attn.decode_multi(to_dev(qb), kc, vc, torch.from_numpy(lens).to(DEV), scale=case.scale)
+    torch.cuda.synchronize()
+    ro, rl = multi_reference(case, T, qb, lens)
+    check_out(to_np(out), ro, case.name)
+    check_lse(to_np(lse), rl, case.name)
+
+
 def test_decode_multi_one_row_is_decode(attn):
     """T = 1 is attn_decode (same kernel path, identical bits)."""
     case = ai.DecodeCase("multi_T1", 37, B=5, Hq=8, Hkv=2, Lmax=700, D=128, lens_lo=0, lens_hi=0,
