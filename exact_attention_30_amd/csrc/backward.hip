@@ -400,7 +400,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   auto step = [&](int tt, const uint16_t *qt, const uint16_t *dt, const float *st, uint16_t *qn, uint16_t *dn,
                   float *sn) __attribute__((always_inline)) {
     wait_tile(tt + 1 < ntile);
-    __syncthreads();
+    barrier_keep_loads();
     if (tt + 2 < ntile) issue(tt + 2, qn, dn, sn);
     const int i0 = qlo + (tt % ntile_h) * ROWS;
     if constexpr (ROWS == 32) {
@@ -608,7 +608,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
                   float *sn, auto role) __attribute__((always_inline)) {
     constexpr bool PW = decltype(role)::value;
     wait_tile(tt + 1 < ntile);
-    __syncthreads();
+    barrier_keep_loads();
     if (tt + 2 < ntile) issue(tt + 2, qn, dn, sn);
     const int i0 = qlo + (tt % ntile_h) * ROWS;
     bool live[2];
@@ -622,27 +622,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
         f32x16 s;
         rowprod(qt + 32 * h * D, s);
         sched_reads_ahead<D / 16, 1, kQkAhead<D>>();
-        const bool crosses = cross_half(i0 + 32 * h);
         float pv[16];
+        auto expo = [&](auto masked) __attribute__((always_inline)) {
+          constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int r = 8 * (rr >> 2) + 4 * hh + (rr & 3);
-          float pe = fast_exp2(__builtin_fmaf(s[rr], c, -st[32 * h + r]));
-          if (crosses) {
-            const int i = i0 + 32 * h + r;
-            const int lim = i + off;
-            const bool vis = i < a.Lq && (!a.causal || (key <= lim && (!win || key > lim - win)));
-            pe = vis ? pe : 0.f;
+          for (int rr = 0; rr < 16; ++rr) {
+            const int r = 8 * (rr >> 2) + 4 * hh + (rr & 3);
+            float pe = fast_exp2(__builtin_fmaf(s[rr], c, -st[32 * h + r]));
+            if (MASKED) {
+              const int i = i0 + 32 * h + r;
+              const int lim = i + off;
+              const bool vis = i < a.Lq && (!a.causal || (key <= lim && (!win || key > lim - win)));
+              pe = vis ? pe : 0.f;
+            }
+            pv[rr] = pe;
           }
-          pv[rr] = pe;
-        }
+        };
+        // only halves that cross a mask boundary or the end of the rows evaluate the mask
+        if (cross_half(i0 + 32 * h)) expo(std::true_type{});
+        else expo(std::false_type{});
         float *pw = &pbuf[pair][h][0];
 #pragma unroll
         for (int g = 0; g < 4; ++g)
           *reinterpret_cast<f32x4 *>(pw + 4 * (g * 64 + lane)) = f32x4{pv[4 * g], pv[4 * g + 1], pv[4 * g + 2], pv[4 * g + 3]};
         pack16(pv, pk[h]);
       }
-      __syncthreads();   // P of every pair is in LDS
+      barrier_keep_loads();   // P of every pair is in LDS
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         if (!live[h]) continue;
@@ -657,7 +662,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
         rowprod(dt + 32 * h * D, dp[h]);
         sched_reads_ahead<D / 16, 1, kQkAhead<D>>();
       }
-      __syncthreads();   // the partner's P is in LDS
+      barrier_keep_loads();   // the partner's P is in LDS
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         if (!live[h]) continue;
@@ -841,7 +846,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdQWaves<
   const float c = a.c;
   auto compute = [&](int jj, const uint16_t *kt, const uint16_t *vt) __attribute__((always_inline)) {
     const int k0 = (jbeg + jj) * BK;
-    if (k0 >= kend_w || k0 + BK <= kbeg_w) return;
+    if (uniform(k0 >= kend_w || k0 + BK <= kbeg_w)) return;
     f32x16 s[BK / 32], dp[BK / 32];
 #pragma unroll
     for (int rb = 0; rb < BK / 32; ++rb) {
@@ -857,25 +862,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdQWaves<
     }
     sched_reads_ahead<2 * (BK / 32) * (D / 16), 1, kQkAhead<D>>();
     // this lane: query row qrow, keys k0 + 32 rb + 8 (rr >> 2) + 4 hh + (rr & 3)
-    const bool crosses = k0 + BK > kfull || k0 < klo_until;
     const int lim = a.causal ? qrow + off : a.Lk - 1;
     bf16x8 sb[BK / 16];
+    auto ds_tile = [&](auto masked) __attribute__((always_inline)) {
+      constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-    for (int rb = 0; rb < BK / 32; ++rb) {
-      float dsv[16];
+      for (int rb = 0; rb < BK / 32; ++rb) {
+        float dsv[16];
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int kk = k0 + 32 * rb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-        float pe = fast_exp2(__builtin_fmaf(s[rb][rr], c, -lse2));
-        if (crosses) {
-          const bool vis = kk < a.Lk && kk <= lim && (!(a.causal && win) || kk > lim - win);
-          pe = vis ? pe : 0.f;
+        for (int rr = 0; rr < 16; ++rr) {
+          const int kk = k0 + 32 * rb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+          float pe = fast_exp2(__builtin_fmaf(s[rb][rr], c, -lse2));
+          if (MASKED) {
+            const bool vis = kk < a.Lk && kk <= lim && (!(a.causal && win) || kk > lim - win);
+            pe = vis ? pe : 0.f;
+          }
+          dsv[rr] = pe * (dp[rb][rr] - del);
         }
-        dsv[rr] = pe * (dp[rb][rr] - del);
+        sb[2 * rb] = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+        sb[2 * rb + 1] = pack8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
       }
-      sb[2 * rb] = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
-      sb[2 * rb + 1] = pack8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
-    }
+    };
+    // only tiles that cross the diagonal, a window edge or the end of the
+    // keys evaluate the mask
+    if (uniform(k0 + BK > kfull || k0 < klo_until)) ds_tile(std::true_type{});
+    else ds_tile(std::false_type{});
     // dQ^T += K^T dS^T  (k = the tile's keys)
 #pragma unroll
     for (int dd = 0; dd < D / 32; ++dd)
@@ -889,7 +900,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdQWaves<
       __attribute__((always_inline)) {
     if (jj + 1 < nt) ATTN_BWD_WAIT_VM(2 * BPW);
     else ATTN_BWD_WAIT_VM(0);
-    __syncthreads();
+    barrier_keep_loads();
     if (jj + 2 < nt) issue(jj + 2, kn, vn);
     compute(jj, kt, vt);
   };

@@ -32,6 +32,23 @@ ATTN_DEV float xor32(float x) { return __shfl_xor(x, 32); }
 ATTN_DEV float xor16(float x) { return __shfl_xor(x, 16); }
 
 ATTN_DEV bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+// Workgroup barrier that leaves direct global->LDS loads in flight.  A fenced
+// barrier (__syncthreads) waits for every outstanding load of the wave,
+// including those of tiles staged further ahead; here the caller first waits
+// (s_waitcnt vmcnt(n)) for the loads whose data other waves read after the
+// barrier.  This wave's own LDS reads and writes complete before it
+// (lgkmcnt(0)), and the "memory" clobber keeps the compiler from moving any
+// memory access across it.
+ATTN_DEV void barrier_keep_loads() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), other counters left alone
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// A condition that is the same in every lane of the wave (computed from
+// per-wave values the compiler cannot prove uniform), as a scalar value: a
+// branch on it is a scalar branch, and the code it guards is skipped, not
+// executed under an exec mask.
+ATTN_DEV bool uniform(bool p) { return __builtin_amdgcn_readfirstlane(p ? 1 : 0) != 0; }
 
 // 16-byte global load / store helpers.
 ATTN_DEV u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
