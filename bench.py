@@ -51,6 +51,9 @@ def parse():
                    help="skip the per-configuration records the default run adds to its JSON line")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy three times (scale for HBM byte counters)")
+    p.add_argument("--gemm-ceiling", action="store_true",
+                   help="only time torch.matmul (the vendor bf16 GEMM) on square unit-normal and all-zero operands: "
+                        "the matrix rate this GPU sustains under its power limit, next to the attention kernels")
     return p.parse_args()
 
 
@@ -66,6 +69,41 @@ SUB_CONFIGS = (
     "gsweep_decode_G1_B32_L8192", "gsweep_decode_G8_B32_L8192", "gsweep_decode_G64_B32_L8192",
     "qwen3_8b_backward_L16384", "q8_ragged_gqa_decode_B64_L1024_32768_T1",
 )
+
+
+def gemm_ceiling():
+    """bf16 GEMM C = A B (torch.matmul, the vendor library) at n = 8192 and
+    16384: operands unit-normal (the attention inputs' distribution) and all
+    zero (little switching activity, so little power).  One JSON line each:
+    median of 10 timed calls after 3 untimed."""
+    import torch
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    for n in (8192, 16384):
+        a = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+        b = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+        for data in ("unit_normal", "zeros"):
+            if data == "zeros":
+                a.zero_()
+                b.zero_()
+            for _ in range(3):
+                torch.matmul(a, b)
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(10):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                torch.matmul(a, b)
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            ms = sorted(ts)[len(ts) // 2]
+            tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+            print(json.dumps({"gemm_ceiling": {"n": n, "dtype": "bf16", "data": data, "ms": round(ms, 4),
+                                               "TFLOP/s": round(tf, 1), "frac_bf16_peak": round(tf / 2500.0, 4)}}),
+                  flush=True)
+        del a, b
 
 
 def copy_calibration():
@@ -211,14 +249,18 @@ def cpu_decode_baseline(case: ai.DecodeCase, lens, seconds: float):
 
 
 def _time_ms(fn, iters: int, stream, between=None) -> float:
-    """Mean duration of fn() from HIP events recorded on `stream`; `between`
+    """Median duration of fn() from HIP events recorded on `stream`; `between`
     runs outside the timed window before each call (the MALL flush).  The
     device idles for a second first, so that every configuration starts from
     the same clock state (the clock follows the power drawn by the work just
-    before, and the configurations run back to back)."""
+    before, and the configurations run back to back), then one untimed call
+    brings the clock back up."""
     import torch
     torch.cuda.synchronize()
     time.sleep(1.0)
+    if between is not None:
+        between(iters)
+    fn()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
     for i, (a, b) in enumerate(evs):
         if between is not None:
@@ -227,7 +269,7 @@ def _time_ms(fn, iters: int, stream, between=None) -> float:
         fn()
         b.record(stream)
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return float(np.median([a.elapsed_time(b) for a, b in evs]))
 
 
 def all_configs(iters: int, only=(), exact=(), emit=None):
@@ -429,6 +471,9 @@ def all_configs(iters: int, only=(), exact=(), emit=None):
 
 def main():
     args = parse()
+    if args.gemm_ceiling:
+        gemm_ceiling()
+        return
     if args.copy_calibration:
         copy_calibration()
         return
