@@ -40,7 +40,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU seconds per oracle sample")
     p.add_argument("--all-configs", action="store_true",
@@ -250,17 +250,19 @@ def cpu_decode_baseline(case: ai.DecodeCase, lens, seconds: float):
 
 def _time_ms(fn, iters: int, stream, between=None) -> float:
     """Median duration of fn() from HIP events recorded on `stream`; `between`
-    runs outside the timed window before each call (the MALL flush).  The
-    device idles for a second first, so that every configuration starts from
-    the same clock state (the clock follows the power drawn by the work just
-    before, and the configurations run back to back), then one untimed call
-    brings the clock back up."""
+    runs outside the timed window before each call (the MALL flush).  Untimed
+    calls first run for at least 100 ms (and at least 3 calls), so that every
+    configuration is timed at the clock its own work settles to rather than
+    the one the previous configuration or an idle device left behind."""
     import torch
     torch.cuda.synchronize()
-    time.sleep(1.0)
-    if between is not None:
-        between(iters)
-    fn()
+    t0, n = time.perf_counter(), 0
+    while n < 3 or time.perf_counter() - t0 < 0.1:
+        if between is not None:
+            between(n)
+        fn()
+        torch.cuda.synchronize()
+        n += 1
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
     for i, (a, b) in enumerate(evs):
         if between is not None:
