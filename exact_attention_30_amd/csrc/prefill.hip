@@ -683,7 +683,7 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_iw_kernel(PrefillArgs a
   // end of the keys or the window's lower edge)
   auto mask_tile = [&](f32x16(&s)[BK / 32], int jj) __attribute__((always_inline)) {
     const int k0 = (j0 + jj) * BK;
-    if (!(k0 + BK > kmask_from || k0 < klo_until)) return;
+    if (!uniform(k0 + BK > kmask_from || k0 < klo_until)) return;
     const int lim = a.causal ? min(a.Lk - 1, qrow + off) : a.Lk - 1;
 #pragma unroll
     for (int rb = 0; rb < BK / 32; ++rb)
