@@ -83,6 +83,12 @@
 #endif
 //  ATTN_PF_LAZYMAX      prefill_kernel takes a tile's maximum only when its
 //                       exponentials against the running max would exceed 2^32
+//  ATTN_PF_IW_LAZY      prefill_iw_kernel likewise for D < 256 (its row sums then
+//                       move into bracket 1, ahead of the P.V products that need
+//                       the check)
+#ifndef ATTN_PF_IW_LAZY
+#define ATTN_PF_IW_LAZY 1
+#endif
 #ifndef ATTN_PF_LAZYMAX
 #define ATTN_PF_LAZYMAX 1
 #endif
@@ -670,6 +676,26 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_iw_kernel(PrefillArgs a
       pb[2 * rb + 1] = pack8(s[rb][8], s[rb][9], s[rb][10], s[rb][11], s[rb][12], s[rb][13], s[rb][14], s[rb][15]);
     }
   };
+  // P = exp2(s c - m) packed to bf16 in pb, the scores kept; returns this
+  // lane's sum of the fp32 exponentials
+  auto expo_sum = [&](const f32x16(&s)[BK / 32]) __attribute__((always_inline)) {
+    const float nm = -m_run;
+    float tsum = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < BK / 32; ++rb) {
+      float p[16];
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) p[rr] = fast_exp2(__builtin_fmaf(s[rb][rr], cexp, nm));
+      pb[2 * rb] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+      pb[2 * rb + 1] = pack8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
+      float t8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t8[i] = p[i] + p[i + 8];
+      const float rs = ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
+      tsum = rb == 0 ? rs : tsum + rs;
+    }
+    return tsum;
+  };
   auto rsum = [&](const f32x16(&s)[BK / 32]) __attribute__((always_inline)) {
 #pragma unroll
     for (int rb = 0; rb < BK / 32; ++rb) {
@@ -772,6 +798,29 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_iw_kernel(PrefillArgs a
       if (j + 1 < nt) dma(vg, vfill, j0 + j + 1, std::true_type{});
     }
     mask_tile(cur, j);
+    if (ATTN_PF_IW_LAZY && D < 256) {   // (D = 256: the 32 exponential registers would spill)
+      // bracket 1: exponentials of tile j against the running max, and their
+      // row sums, beside the products of tile j+1 and the direct loads; the
+      // tile maximum is taken (and the tile exponentiated again) only when
+      // some sum exceeds 2^32 or is not finite, as in prefill_kernel
+      float tsum = expo_sum(cur);
+      qk_ops(nxt, kread);
+      if (SPREAD) {
+        dma(kg, kfill, j0 + min(j + 2, nt - 1), std::false_type{});
+        dma(vg, vfill, j0 + min(j + 1, nt - 1), std::true_type{});
+      }
+      sched_b1();
+      __builtin_amdgcn_sched_barrier(0);
+      if (wave_any(!(tsum <= 4294967296.f))) {
+        raise(cur);
+        tsum = expo_sum(cur);
+      }
+      l_run += tsum;
+      // bracket 2: P.V of tile j
+      pv_ops(vread);
+      sched_b2();
+      return;
+    }
     raise(cur);
     // bracket 1: exponentials of tile j beside the products of tile j+1 (past
     // the last tile those products are not used) and the direct loads of
