@@ -117,6 +117,11 @@ ATTN_DEV void sched_interleave() {
 #ifndef ATTN_BWD_VALU_PER
 #define ATTN_BWD_VALU_PER 6
 #endif
+//  ATTN_BWD_PAIR_LOADS paired dk/dv: only the dP/dS waves stage the query tiles (the
+//                      S/P waves, which hold each stage's critical path, issue none)
+#ifndef ATTN_BWD_PAIR_LOADS
+#define ATTN_BWD_PAIR_LOADS 1
+#endif
 //  ATTN_BWD_QK_AHEAD   operand reads of the S / dP products issued this many MFMAs ahead
 //  ATTN_BWD_TR_AHEAD   transposed operand reads of the dV / dK / dQ products, likewise
 #ifndef ATTN_BWD_QK_AHEAD
@@ -474,6 +479,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   constexpr int RPB = 512 / D;
   constexpr int BPW = TILE * 2 / 1024 / NW;   // 1 KiB blocks per wave per tensor and stage
   static_assert(BPW * NW * 1024 == TILE * 2, "stage must split evenly over the waves");
+  constexpr int NL = ATTN_BWD_PAIR_LOADS ? NW / 2 : NW;   // waves that stage the query tiles
+  constexpr int BPL = TILE * 2 / 1024 / NL;              // their 1 KiB blocks per tensor and stage
   __shared__ __attribute__((aligned(1024))) uint16_t qa[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t qb[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t qc[TILE];
@@ -490,6 +497,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int pair = wu & 3;
   const bool pwave = wu < 4;                   // forms P and dV (else dP, dS and dK)
+  const int lw = wu - (NW - NL);               // index among the staging waves (< 0: none)
   const int ql = lane & 31, hh = lane >> 5, g16 = lane >> 4, j16 = lane & 15;
 
   const int nbh = a.B * a.Hkv;
@@ -546,25 +554,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
     const int hq = hkv * a.G + tt / ntile_h;
     const int i0 = qlo + (tt % ntile_h) * ROWS;
     const size_t rowbase = ((size_t)b * a.Hq + hq) * a.Lq;
+    if (lw < 0) return;
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-      const int blk = wu * BPW + i;
+    for (int i = 0; i < BPL; ++i) {
+      const int blk = lw * BPL + i;
       const int row = blk * RPB + lane / CPR;
       const int c = (lane % CPR) ^ tswz<D>(row);
       const size_t grow = rowbase + min(i0 + row, a.Lq - 1);
       dma_to_lds<16>(a.q + grow * D + 8 * c, qd + blk * 512);
       dma_to_lds<16>(a.dout + grow * D + 8 * c, dd + blk * 512);
     }
-    if (wu < 2) {
-      const float *src = wu == 0 ? a.lse2 : a.delta;
+    if (lw < 2) {
+      const float *src = lw == 0 ? a.lse2 : a.delta;
       const size_t grow = rowbase + min(i0 + lane, a.Lq - 1);
-      dma_to_lds<4>(src + grow, sd + ROWS * wu);
+      dma_to_lds<4>(src + grow, sd + ROWS * lw);
     }
   };
   auto wait_tile = [&](bool younger) __attribute__((always_inline)) {
     if (younger) {
-      if (wu < 2) ATTN_BWD_WAIT_VM(2 * BPW + 1);
-      else ATTN_BWD_WAIT_VM(2 * BPW);
+      if (lw >= 0 && lw < 2) ATTN_BWD_WAIT_VM(2 * BPL + 1);
+      else ATTN_BWD_WAIT_VM(2 * BPL);
     } else {
       ATTN_BWD_WAIT_VM(0);
     }
