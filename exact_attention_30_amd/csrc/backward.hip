@@ -654,12 +654,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
         for (int g = 0; g < 4; ++g)
           *reinterpret_cast<f32x4 *>(pw + 4 * (g * 64 + lane)) = f32x4{pv[4 * g], pv[4 * g + 1], pv[4 * g + 2], pv[4 * g + 3]};
-        pack16(pv, pk[h]);
       }
       barrier_keep_loads();   // P of every pair is in LDS
+      // the bf16 packing of P for dV happens here, in the phase where this
+      // wave has slack, from the copy it handed to its partner
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         if (!live[h]) continue;
+        {
+          const float *pr = &pbuf[pair][h][0];
+          float pv[16];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 p4 = *reinterpret_cast<const f32x4 *>(pr + 4 * (g * 64 + lane));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pv[4 * g + i] = p4[i];
+          }
+          pack16(pv, pk[h]);
+        }
         colprod(dt + 32 * h * D, pk[h]);
         sched_reads_ahead<2 * (D / 32), 2, kTrAhead<D>>();
       }
@@ -670,6 +682,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
         if (!live[h]) continue;
         rowprod(dt + 32 * h * D, dp[h]);
         sched_reads_ahead<D / 16, 1, kQkAhead<D>>();
+        // dP - delta here, where this wave has slack (the phase after the
+        // barrier holds the stage's critical path)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) dp[h][rr] -= st[ROWS + 32 * h + 8 * (rr >> 2) + 4 * hh + (rr & 3)];
       }
       barrier_keep_loads();   // the partner's P is in LDS
 #pragma unroll
@@ -681,11 +697,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
         for (int g = 0; g < 4; ++g) {
           const f32x4 p4 = *reinterpret_cast<const f32x4 *>(pr + 4 * (g * 64 + lane));
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int rr = 4 * g + i;
-            const int r = 8 * g + 4 * hh + i;
-            dsv[rr] = p4[i] * (dp[h][rr] - st[ROWS + 32 * h + r]);
-          }
+          for (int i = 0; i < 4; ++i) dsv[4 * g + i] = p4[i] * dp[h][4 * g + i];
         }
         bf16x8 sk[2];
         pack16(dsv, sk);
