@@ -28,10 +28,12 @@
 //    and dO^T, Q^T are read with ds_read_b64_tr_b16.  The two halves of an
 //    unmasked stage are software-pipelined.  dk and dv of a KV head are
 //    complete in one workgroup: no atomics.
-//  * dq kernel: a wave owns 32 query rows (q and dout rows as operands in
-//    registers) and walks the key tiles (64 keys, three in flight) in reach
-//    of its rows: S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T with K^T
-//    read transposed from the same LDS tile.
+//  * dq kernels: a wave owns 32 query rows (q and dout rows as operands in
+//    registers) and walks the 32-key tiles in reach of its rows: S^T = K Q^T,
+//    dP^T = V dO^T, then dQ^T += K^T dS^T with K^T read transposed from the
+//    same LDS tile.  For D = 64 and 128 (bwd_dq2_kernel) eight waves form two
+//    groups whose matrix and vector work alternate on each SIMD; for D = 256
+//    (bwd_dq_kernel) four waves, one per SIMD.
 //  * LDS operand reads are issued several MFMAs ahead of their use.
 //  * A tile that is read both row-wise (b128) and transposed (tr16) is stored
 //    with a 16-byte-chunk XOR swizzle that keeps both access patterns free of
@@ -121,6 +123,10 @@ ATTN_DEV void sched_interleave() {
 //                      S/P waves, which hold each stage's critical path, issue none)
 #ifndef ATTN_BWD_PAIR_LOADS
 #define ATTN_BWD_PAIR_LOADS 1
+#endif
+//  ATTN_BWD_DQ_PAIRS   dq for D = 64 and 128 on bwd_dq2_kernel (two groups of waves)
+#ifndef ATTN_BWD_DQ_PAIRS
+#define ATTN_BWD_DQ_PAIRS 1
 #endif
 //  ATTN_BWD_QK_AHEAD   operand reads of the S / dP products issued this many MFMAs ahead
 //  ATTN_BWD_TR_AHEAD   transposed operand reads of the dV / dK / dQ products, likewise
@@ -956,6 +962,280 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdQWaves<
   }
 }
 
+// dq with two groups of waves (D = 64, 128): eight waves, wave w and wave
+// w + 4 on one SIMD, each owning 32 query rows as in bwd_dq_kernel.  Per
+// 32-key tile j the matrix work G(j) = [dQ += K(j-1)^T dS(j-1)^T,
+// S^T(j) = K(j) Q^T, dP^T(j) = V(j) dO^T] and the vector work
+// dS(j) = P(j) (dP(j) - delta) alternate between the groups inside one step:
+// group A (waves 0-3) runs G(j) and then dS(j), group B runs dS(j-1) and then
+// G(j), so the exponentials of one wave execute beside the MFMAs of its SIMD
+// neighbour (as in the forward's ping-pong).  K and V tiles sit in a ring of
+// four LDS stages (tile j-1 is still read by dQ in step j); the loads of tile
+// j+2 are issued at the start of step j.  Same products in the same order per
+// accumulator as bwd_dq_kernel (bit-identical).
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq2_kernel(BackwardArgs a) {
+  constexpr int NW = 8;
+  constexpr int CPR = D / 8;
+  constexpr int BK = 32;
+  constexpr int TILE = BK * D;
+  constexpr int RPB = 512 / D;                       // rows per 1 KiB direct load
+  constexpr int NB = TILE * 2 / 1024;                // 1 KiB blocks per tensor and tile
+  constexpr int NL = NB < NW / 2 ? NB : NW / 2;      // waves that load (group A's first NL)
+  constexpr int BPL = NB / NL;                       // their blocks per tensor and tile
+  static_assert(BPL * NL == NB, "tile must split evenly over the loading waves");
+  __shared__ __attribute__((aligned(1024))) uint16_t kst[4][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t vst[4][TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const bool grpA = wu < NW / 2;
+  const int lw = wu < NL ? wu : -1;                  // index among the loading waves (< 0: none)
+  const int ql = lane & 31, hh = lane >> 5, g16 = lane >> 4, j16 = lane & 15;
+
+  // workgroup -> (row block, head group, b, hkv); waves are hpw heads x wph
+  // row sub-blocks of 32 rows; row blocks in descending order
+  const int hpw = a.dq_hpw, wph = NW / hpw;
+  const int rows_wg = 32 * wph;
+  const int nrb = (a.Lq + rows_wg - 1) / rows_wg;
+  const int ngrp = a.G / hpw;
+  const int nu = ngrp * a.Hkv * a.B;
+  const int t = blockIdx.x;
+  const int rbk = nrb - 1 - t / nu;
+  int u = t % nu;
+  const int grp = u % ngrp;
+  u /= ngrp;
+  const int hkv = u % a.Hkv;
+  const int b = u / a.Hkv;
+  const int hq = hkv * a.G + grp * hpw + wu / wph;
+  const int r0w = rbk * rows_wg + 32 * (wu % wph);
+  const int qrow = r0w + ql;
+  const int off = a.Lk - a.Lq;
+  const int win = a.window;
+
+  const size_t rowi = ((size_t)b * a.Hq + hq) * a.Lq + (qrow < a.Lq ? qrow : 0);
+  bf16x8 qf[D / 16], of[D / 16];
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const bool in = qrow < a.Lq;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      qf[ks] = as_bf16x8(in ? ld16(a.q + rowi * D + 16 * ks + 8 * hh) : z);
+      of[ks] = as_bf16x8(in ? ld16(a.dout + rowi * D + 16 * ks + 8 * hh) : z);
+    }
+  }
+  const float lse2 = qrow < a.Lq ? a.lse2[rowi] : __builtin_inff();
+  const float del = qrow < a.Lq ? a.delta[rowi] : 0.f;
+
+  // key range of the workgroup's rows (every wave walks it: one barrier per tile)
+  const int rlo = rbk * rows_wg, rhi = min(a.Lq, rlo + rows_wg) - 1;
+  int kbeg = 0, kend = a.Lk;
+  if (a.causal) {
+    kend = min(a.Lk, rhi + off + 1);
+    if (win) kbeg = max(0, rlo + off - win + 1);
+  }
+  const int jbeg = kbeg / BK;
+  const int nt = kend > kbeg ? (kend + BK - 1) / BK - jbeg : 0;
+  // this wave's key range (tiles outside it are skipped by the wave)
+  const int wlo = r0w, whi = min(a.Lq, r0w + 32) - 1;
+  const int kend_w = a.causal ? min(a.Lk, whi + off + 1) : a.Lk;
+  const int kbeg_w = (a.causal && win) ? max(0, wlo + off - win + 1) : 0;
+  const int kfull = a.causal ? min(a.Lk, wlo + off + 1) : a.Lk;
+  const int klo_until = (a.causal && win) ? whi + off - win + 1 : 0;
+
+  int roff[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) roff[ks] = toff<D>(ql, 2 * ks + hh);
+  int tlo[D / 32], thi[D / 32];
+  {
+    const int r = 4 * hh + (j16 >> 2);
+    const int c = 2 * (g16 & 1) + ((j16 & 3) >> 1);
+#pragma unroll
+    for (int dd = 0; dd < D / 32; ++dd) {
+      tlo[dd] = toff<D>(r, 4 * dd + c) + 4 * (j16 & 1);
+      thi[dd] = toff<D>(r + 8, 4 * dd + c) + 4 * (j16 & 1);
+    }
+  }
+
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) dq[i] = f32x16{};
+
+  const size_t kvrow = ((size_t)b * a.Hkv + hkv) * (size_t)a.Lk;
+  auto issue = [&](int jj, uint16_t *kd, uint16_t *vd) __attribute__((always_inline)) {
+    if (lw < 0) return;
+    const int k0 = (jbeg + jj) * BK;
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) {
+      const int blk = lw * BPL + i;
+      const int row = blk * RPB + lane / CPR;
+      const int c = (lane % CPR) ^ tswz<D>(row);
+      const size_t grow = kvrow + min(k0 + row, a.Lk - 1);
+      dma_to_lds<16>(a.k + grow * D + 8 * c, kd + blk * 512);
+      dma_to_lds<16>(a.v + grow * D + 8 * c, vd + blk * 512);
+    }
+  };
+  auto active = [&](int jj) __attribute__((always_inline)) {
+    const int k0 = (jbeg + jj) * BK;
+    return jj >= 0 && jj < nt && !uniform(k0 >= kend_w || k0 + BK <= kbeg_w);
+  };
+
+  const float c = a.c;
+  // dS^T = P (dP - delta) of tile jj from its S^T and dP^T, packed for dQ
+  auto ds_tile = [&](int jj, const f32x16 &s, const f32x16 &dp, bf16x8(&sb)[2]) __attribute__((always_inline)) {
+    const int k0 = (jbeg + jj) * BK;
+    const int lim = a.causal ? qrow + off : a.Lk - 1;
+    auto body = [&](auto masked) __attribute__((always_inline)) {
+      constexpr bool MASKED = decltype(masked)::value;
+      float dsv[16];
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int kk = k0 + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+        float pe = fast_exp2(__builtin_fmaf(s[rr], c, -lse2));
+        if (MASKED) {
+          const bool vis = kk < a.Lk && kk <= lim && (!(a.causal && win) || kk > lim - win);
+          pe = vis ? pe : 0.f;
+        }
+        dsv[rr] = pe * (dp[rr] - del);
+      }
+      sb[0] = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+      sb[1] = pack8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
+    };
+    if (uniform(k0 + BK > kfull || k0 < klo_until)) body(std::true_type{});
+    else body(std::false_type{});
+  };
+  // dQ^T += K^T dS^T of the tile in stage kp (K^T read transposed)
+  auto dq_part = [&](const uint16_t *kp, const bf16x8(&sb)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int dd = 0; dd < D / 32; ++dd)
+#pragma unroll
+      for (int kc2 = 0; kc2 < BK / 16; ++kc2)
+        dq[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            tr_operand(kp + 16 * kc2 * D + tlo[dd], kp + 16 * kc2 * D + thi[dd]), sb[kc2], dq[dd], 0, 0, 0);
+    sched_reads_ahead<(D / 32) * (BK / 16), 2, kTrAhead<D>>();
+  };
+  // S^T = K Q^T and dP^T = V dO^T of the tile in stages kt, vt; NLD > 0: the
+  // direct loads `loads` (NLD of them) go among the MFMAs, one every SP
+  auto sdp_part = [&](const uint16_t *kt, const uint16_t *vt, f32x16 &s, f32x16 &dp, auto loads, auto nld)
+      __attribute__((always_inline)) {
+    constexpr int NLD = decltype(nld)::value;
+    s = f32x16{};
+    dp = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(kt + roff[ks])), qf[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(vt + roff[ks])), of[ks], dp, 0, 0, 0);
+    }
+    loads();
+    constexpr int N = 2 * (D / 16);
+    constexpr int AH = kQkAhead<D>;
+    constexpr int SP = NLD > 0 && N / NLD > 0 ? N / NLD : 1;
+    __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (NLD > 0 && i % SP == 0 && i / SP < NLD) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+      if (i < N - AH) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  auto none = []() __attribute__((always_inline)) {};
+  // Values carried from one step to the next: group A the packed dS^T of its
+  // last tile, group B the S^T and dP^T of its last tile.  Every path through
+  // a step writes them (zeros for a tile the wave skips), so that they are
+  // not held live through the parts of the step that do not need them.
+  bf16x8 sbc[2];
+  f32x16 sc, dpc;
+  // step jj, tile jj in stage P = jj % 4: tile jj's loads are complete (the
+  // loads issued in step jj-1 may be in flight); the barrier publishes them
+  // and frees stage (P + 2) % 4 (tile jj-2), into which group A's waves load
+  // tile jj+2 among their S / dP MFMAs (past the last tile: a repeat of it,
+  // never read), so every step issues the same loads and waits for the same
+  // count
+  auto step = [&](int jj, auto stage, auto role) __attribute__((always_inline)) {
+    constexpr int P = decltype(stage)::value;
+    constexpr bool A = decltype(role)::value;
+    if (lw >= 0) ATTN_BWD_WAIT_VM(2 * BPL);
+    barrier_keep_loads();
+    const bool ap = active(jj - 1), ac = active(jj);
+    const uint16_t *kp = kst[(P + 3) & 3];
+    if constexpr (A) {
+      // G(jj), then dS(jj); the S / dP products run on every step for the
+      // loads among them (a tile this wave does not see gives dS = 0)
+      __builtin_amdgcn_s_setprio(1);
+      if (ap) dq_part(kp, sbc);
+      f32x16 s, dp;
+      if (lw >= 0) {
+        sdp_part(kst[P], vst[P], s, dp, [&]() __attribute__((always_inline)) {
+          issue(min(jj + 2, nt - 1), kst[(P + 2) & 3], vst[(P + 2) & 3]);
+        }, std::integral_constant<int, 2 * BPL>{});
+      } else if (ac) {
+        sdp_part(kst[P], vst[P], s, dp, none, std::integral_constant<int, 0>{});
+      }
+      __builtin_amdgcn_s_setprio(0);
+      if (ac) {
+        ds_tile(jj, s, dp, sbc);
+      } else {
+        sbc[0] = bf16x8{};
+        sbc[1] = bf16x8{};
+      }
+    } else {
+      // dS(jj-1), then G(jj)
+      if (ap) {
+        bf16x8 sb[2];
+        ds_tile(jj - 1, sc, dpc, sb);
+        __builtin_amdgcn_s_setprio(1);
+        dq_part(kp, sb);
+      } else {
+        __builtin_amdgcn_s_setprio(1);
+      }
+      if (ac) {
+        sdp_part(kst[P], vst[P], sc, dpc, none, std::integral_constant<int, 0>{});
+      } else {
+        sc = f32x16{};
+        dpc = f32x16{};
+      }
+      __builtin_amdgcn_s_setprio(0);
+    }
+  };
+  // the two groups run separate copies of the loop (each keeps only its own
+  // values live); both pass the same barriers in the same number
+  auto run = [&](auto role) __attribute__((always_inline)) {
+    issue(0, kst[0], vst[0]);
+    issue(min(1, nt - 1), kst[1], vst[1]);
+    for (int jj = 0; jj <= nt; jj += 4) {
+      step(jj, std::integral_constant<int, 0>{}, role);
+      if (jj + 1 > nt) break;
+      step(jj + 1, std::integral_constant<int, 1>{}, role);
+      if (jj + 2 > nt) break;
+      step(jj + 2, std::integral_constant<int, 2>{}, role);
+      if (jj + 3 > nt) break;
+      step(jj + 3, std::integral_constant<int, 3>{}, role);
+    }
+  };
+
+  // the q/dout operand loads complete before any staged load is issued
+  ATTN_BWD_WAIT_VM(0);
+  if (nt > 0) {
+    if (grpA) run(std::true_type{});
+    else run(std::false_type{});
+    ATTN_BWD_WAIT_VM(0);   // the repeats of the last tile have landed
+  }
+
+  if (qrow < a.Lq) {
+    uint16_t *qp = a.dq + rowi * D;
+    const float scl = a.scale;
+#pragma unroll
+    for (int dd = 0; dd < D / 32; ++dd)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x4 v4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v4[i] = (__bf16)(dq[dd][4 * j + i] * scl);
+        *reinterpret_cast<bf16x4 *>(qp + 32 * dd + 8 * j + 4 * hh) = v4;
+      }
+  }
+}
+
 template <int D>
 static hipError_t launch_bwd_t(const BackwardArgs &a, hipStream_t s) {
   const long long rows = (long long)a.B * a.Hq * a.Lq;
@@ -969,6 +1249,15 @@ static hipError_t launch_bwd_t(const BackwardArgs &a, hipStream_t s) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)(nkb * a.B * a.Hkv)), dim3(256), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (ATTN_BWD_DQ_PAIRS && D <= 128) {
+    BackwardArgs a2 = a;
+    a2.dq_hpw = a.G % 8 == 0 ? 8 : a.dq_hpw;   // query heads per workgroup: divides G and 8
+    const int rows_wg = 32 * (8 / a2.dq_hpw);
+    const long long nrb = (a.Lq + rows_wg - 1) / rows_wg;
+    hipLaunchKernelGGL((bwd_dq2_kernel<D <= 128 ? D : 128>), dim3((unsigned)(nrb * (a.G / a2.dq_hpw) * a.Hkv * a.B)),
+                       dim3(512), 0, s, a2);
+    return hipGetLastError();
+  }
   const int rows_wg = 32 * (kBwdWaves / a.dq_hpw);
   const long long nrb = (a.Lq + rows_wg - 1) / rows_wg;
   hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(nrb * (a.G / a.dq_hpw) * a.Hkv * a.B)), dim3(256), 0, s, a);
