@@ -119,10 +119,13 @@ ATTN_DEV void sched_interleave() {
 #ifndef ATTN_BWD_VALU_PER
 #define ATTN_BWD_VALU_PER 6
 #endif
-//  ATTN_BWD_PAIR_LOADS paired dk/dv: only the dP/dS waves stage the query tiles (the
-//                      S/P waves, which hold each stage's critical path, issue none)
+//  ATTN_BWD_PAIR_LOADS paired dk/dv, which waves stage the query tiles: 0 every wave at
+//                      the start of a stage; 1 the dP/dS waves there (the S/P waves
+//                      hold the first phase's critical path); 2 the S/P waves in their
+//                      second phase, between the dV products of the two halves (where
+//                      they wait for their partners anyway)
 #ifndef ATTN_BWD_PAIR_LOADS
-#define ATTN_BWD_PAIR_LOADS 1
+#define ATTN_BWD_PAIR_LOADS 2
 #endif
 //  ATTN_BWD_DQ_PAIRS   dq for D = 64 and 128 on bwd_dq2_kernel (two groups of waves)
 #ifndef ATTN_BWD_DQ_PAIRS
@@ -503,7 +506,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int pair = wu & 3;
   const bool pwave = wu < 4;                   // forms P and dV (else dP, dS and dK)
-  const int lw = wu - (NW - NL);               // index among the staging waves (< 0: none)
+  // index among the staging waves (< 0: none)
+  const int lw = ATTN_BWD_PAIR_LOADS == 2 ? (pwave ? wu : -1) : wu - (NW - NL);
   const int ql = lane & 31, hh = lane >> 5, g16 = lane >> 4, j16 = lane & 15;
 
   const int nbh = a.B * a.Hkv;
@@ -624,7 +628,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
     constexpr bool PW = decltype(role)::value;
     wait_tile(tt + 1 < ntile);
     barrier_keep_loads();
-    if (tt + 2 < ntile) issue(tt + 2, qn, dn, sn);
+    if (ATTN_BWD_PAIR_LOADS != 2 && tt + 2 < ntile) issue(tt + 2, qn, dn, sn);
     const int i0 = qlo + (tt % ntile_h) * ROWS;
     bool live[2];
 #pragma unroll
@@ -663,23 +667,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
       }
       barrier_keep_loads();   // P of every pair is in LDS
       // the bf16 packing of P for dV happens here, in the phase where this
-      // wave has slack, from the copy it handed to its partner
+      // wave has slack, from the copy it handed to its partner; so does the
+      // staging of stage tt + 2 (into the buffers of stage tt - 1, free since
+      // the stage's first barrier)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        if (!live[h]) continue;
-        {
-          const float *pr = &pbuf[pair][h][0];
-          float pv[16];
+        if (live[h]) {
+          {
+            const float *pr = &pbuf[pair][h][0];
+            float pv[16];
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 p4 = *reinterpret_cast<const f32x4 *>(pr + 4 * (g * 64 + lane));
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 p4 = *reinterpret_cast<const f32x4 *>(pr + 4 * (g * 64 + lane));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) pv[4 * g + i] = p4[i];
+              for (int i = 0; i < 4; ++i) pv[4 * g + i] = p4[i];
+            }
+            pack16(pv, pk[h]);
           }
-          pack16(pv, pk[h]);
+          colprod(dt + 32 * h * D, pk[h]);
+          sched_reads_ahead<2 * (D / 32), 2, kTrAhead<D>>();
         }
-        colprod(dt + 32 * h * D, pk[h]);
-        sched_reads_ahead<2 * (D / 32), 2, kTrAhead<D>>();
+        if (ATTN_BWD_PAIR_LOADS == 2 && h == 0 && tt + 2 < ntile) issue(tt + 2, qn, dn, sn);
       }
     } else {
       f32x16 dp[2];         // dP of each half
