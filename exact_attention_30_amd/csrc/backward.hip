@@ -476,7 +476,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
 // Each wave thus holds one operand set and one accumulator set (about half
 // the registers of a wave doing all four products), so two fit per SIMD and
 // the exponentials of one run beside the MFMAs of the other.  Per 64-row
-// stage: [P-waves: S, P -> LDS | partner: dP], barrier, [P-waves: dV |
+// stage: [P-waves: S, P -> LDS | partner: dP], barrier, [P-waves: dV, with
+// the direct loads of the stage after next between its two halves |
 // partner: dS, dK]; the same products as bwd_dkdv_kernel, in the same order
 // per accumulator (bit-identical results).
 template <int D>
