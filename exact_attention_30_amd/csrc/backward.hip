@@ -131,6 +131,16 @@ ATTN_DEV void sched_interleave() {
 #ifndef ATTN_BWD_DQ_PAIRS
 #define ATTN_BWD_DQ_PAIRS 1
 #endif
+//  ATTN_BWD_P_PIPE64 / ATTN_BWD_P_PIPE128   paired dk/dv at D = 64 / 128: the S/P wave
+//                      exponentiates the first half beside the second half's S products
+//                      (unmasked stages), this many vector instructions after each MFMA
+//                      (0: halves one after the other)
+#ifndef ATTN_BWD_P_PIPE64
+#define ATTN_BWD_P_PIPE64 2
+#endif
+#ifndef ATTN_BWD_P_PIPE128
+#define ATTN_BWD_P_PIPE128 6
+#endif
 //  ATTN_BWD_QK_AHEAD   operand reads of the S / dP products issued this many MFMAs ahead
 //  ATTN_BWD_TR_AHEAD   transposed operand reads of the dV / dK / dQ products, likewise
 #ifndef ATTN_BWD_QK_AHEAD
@@ -636,35 +646,49 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
     for (int h = 0; h < 2; ++h) live[h] = !skip_half(i0 + 32 * h);
     if constexpr (PW) {
       bf16x8 pk[2][2];      // P of each half, kept for dV
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (!live[h]) continue;
-        f32x16 s;
-        rowprod(qt + 32 * h * D, s);
-        sched_reads_ahead<D / 16, 1, kQkAhead<D>>();
+      // P of half h = exp2(S c - lse2), written to LDS for the partner
+      auto pexp = [&](int h, const f32x16 &s, auto masked) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked)::value;
         float pv[16];
-        auto expo = [&](auto masked) __attribute__((always_inline)) {
-          constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int r = 8 * (rr >> 2) + 4 * hh + (rr & 3);
-            float pe = fast_exp2(__builtin_fmaf(s[rr], c, -st[32 * h + r]));
-            if (MASKED) {
-              const int i = i0 + 32 * h + r;
-              const int lim = i + off;
-              const bool vis = i < a.Lq && (!a.causal || (key <= lim && (!win || key > lim - win)));
-              pe = vis ? pe : 0.f;
-            }
-            pv[rr] = pe;
+        for (int rr = 0; rr < 16; ++rr) {
+          const int r = 8 * (rr >> 2) + 4 * hh + (rr & 3);
+          float pe = fast_exp2(__builtin_fmaf(s[rr], c, -st[32 * h + r]));
+          if (MASKED) {
+            const int i = i0 + 32 * h + r;
+            const int lim = i + off;
+            const bool vis = i < a.Lq && (!a.causal || (key <= lim && (!win || key > lim - win)));
+            pe = vis ? pe : 0.f;
           }
-        };
-        // only halves that cross a mask boundary or the end of the rows evaluate the mask
-        if (cross_half(i0 + 32 * h)) expo(std::true_type{});
-        else expo(std::false_type{});
+          pv[rr] = pe;
+        }
         float *pw = &pbuf[pair][h][0];
 #pragma unroll
         for (int g = 0; g < 4; ++g)
           *reinterpret_cast<f32x4 *>(pw + 4 * (g * 64 + lane)) = f32x4{pv[4 * g], pv[4 * g + 1], pv[4 * g + 2], pv[4 * g + 3]};
+      };
+      constexpr int PPIPE = D == 64 ? ATTN_BWD_P_PIPE64 : ATTN_BWD_P_PIPE128;
+      if (PPIPE > 0 && live[0] && live[1] && !cross_half(i0) && !cross_half(i0 + 32)) {
+        // both halves unmasked: the first half's exponentials beside the
+        // second half's S products
+        f32x16 s0, s1;
+        rowprod(qt, s0);
+        sched_reads_ahead<D / 16, 1, kQkAhead<D>>();
+        rowprod(qt + 32 * D, s1);
+        pexp(0, s0, std::false_type{});
+        sched_interleave<D / 16, 1, kQkAhead<D>, (PPIPE > 0 ? PPIPE : 1)>();
+        pexp(1, s1, std::false_type{});
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (!live[h]) continue;
+          f32x16 s;
+          rowprod(qt + 32 * h * D, s);
+          sched_reads_ahead<D / 16, 1, kQkAhead<D>>();
+          // only halves that cross a mask boundary or the end of the rows evaluate the mask
+          if (cross_half(i0 + 32 * h)) pexp(h, s, std::true_type{});
+          else pexp(h, s, std::false_type{});
+        }
       }
       barrier_keep_loads();   // P of every pair is in LDS
       // the bf16 packing of P for dV happens here, in the phase where this
