@@ -750,7 +750,16 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_iw_kernel(PrefillArgs a
       const float alpha = need ? fast_exp2(m_run - mnew) : 1.f;
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+      for (int db = 0; db < D / 32; ++db) {
+        // D = 256: O lives in AGPRs (accumulation registers), which vector
+        // arithmetic cannot address; the empty asm statements, which take O
+        // in AGPRs, keep its copies to and from vector registers inside this
+        // rarely taken branch (without them the compiler placed 128 such
+        // copies per tile on the common path)
+        if constexpr (D == 256) asm volatile("" : "+a"(o[db]));
+        o[db] *= alpha;
+        if constexpr (D == 256) asm volatile("" : "+a"(o[db]));
+      }
       m_run = mnew;
     }
   };
