@@ -70,6 +70,18 @@
 #ifndef ATTN_PF_IW
 #define ATTN_PF_IW 5
 #endif
+//  ATTN_PF_IW_QKA256 / ATTN_PF_IW_PVA256 / ATTN_PF_IW_V1_256   the read-ahead distances
+//                       and bracket-1 vector instructions per MFMA of prefill_iw_kernel at D = 256
+//                       (its registers leave room for reads further ahead)
+#ifndef ATTN_PF_IW_QKA256
+#define ATTN_PF_IW_QKA256 8
+#endif
+#ifndef ATTN_PF_IW_PVA256
+#define ATTN_PF_IW_PVA256 5
+#endif
+#ifndef ATTN_PF_IW_V1_256
+#define ATTN_PF_IW_V1_256 3
+#endif
 //  ATTN_PF_IW_SPREAD    head dims (bit mask as above) for which prefill_iw_kernel
 //                       spreads its direct loads over the MFMAs
 #ifndef ATTN_PF_IW_SPREAD
@@ -772,18 +784,19 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_iw_kernel(PrefillArgs a
   constexpr int NLD = SPREAD ? 2 * C::DPW : 0;
   constexpr int SP = NLD ? (NQK / NLD > 0 ? NQK / NLD : 1) : 1;
   auto sched_b1 = [&]() __attribute__((always_inline)) {
-    constexpr int A = ATTN_PF_QK_AHEAD;
+    constexpr int A = D == 256 ? ATTN_PF_IW_QKA256 : ATTN_PF_QK_AHEAD;
+    constexpr int V1 = D == 256 ? ATTN_PF_IW_V1_256 : ATTN_PF_IW_V1;
     __builtin_amdgcn_sched_group_barrier(0x100, A, 0);
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, ATTN_PF_IW_V1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, V1, 0);
       if (NLD && i % SP == 0 && i / SP < NLD) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
       if (i < NQK - A) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
   auto sched_b2 = [&]() __attribute__((always_inline)) {
-    constexpr int A = ATTN_PF_PV_AHEAD;
+    constexpr int A = D == 256 ? ATTN_PF_IW_PVA256 : ATTN_PF_PV_AHEAD;
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * A, 0);
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
