@@ -149,6 +149,9 @@ CASES = [
     ai.PrefillCase("bwd_full_G2_D128_Lq300_Lk50", 70, B=1, Hq=4, Hkv=2, Lq=300, Lk=50, D=128, causal=False),
     ai.PrefillCase("bwd_G2_D256_Lq150_Lk260", 71, B=1, Hq=4, Hkv=2, Lq=150, Lk=260, D=256),
     ai.PrefillCase("bwd_full_G1_D256_L70", 72, B=2, Hq=2, Hkv=2, Lq=70, Lk=70, D=256, causal=False),
+    # eight heads per dq workgroup (G a multiple of 8), at D = 64 and with Lq < Lk
+    ai.PrefillCase("bwd_G16_D64_L333", 73, B=1, Hq=16, Hkv=1, Lq=333, Lk=333, D=64),
+    ai.PrefillCase("bwd_G8_D128_Lq200_Lk520", 74, B=2, Hq=16, Hkv=2, Lq=200, Lk=520, D=128),
 ]
 
 
