@@ -41,6 +41,7 @@
 //  * Causal (bottom-right) and window masks: query or key tiles that no row
 //    or key of a wave can see are skipped; the mask is applied per element
 //    only on tiles that cross a boundary.
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -1269,19 +1270,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   }
 }
 
+// The dq kernel does not depend on the dk/dv kernel (both read only q, k, v,
+// dout and the pre-pass's row statistics), so with ATTN_BWD_SIDE it runs on a
+// second stream of the library, forked from and joined back into the caller's
+// stream with events: its workgroups fill the CUs that the dk/dv kernel's
+// last, uneven round leaves idle.  One side stream and event pair per device,
+// created on first use; the fork and join are enqueued under a lock, so
+// concurrent calls on one device share the side stream in order.
+#ifndef ATTN_BWD_SIDE
+#define ATTN_BWD_SIDE 1
+#endif
+namespace {
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+SideStream g_side[64];
+std::mutex g_side_mu;
+}  // namespace
+
 template <int D>
-static hipError_t launch_bwd_t(const BackwardArgs &a, hipStream_t s) {
-  const long long rows = (long long)a.B * a.Hq * a.Lq;
-  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const long long nkb = (a.Lk + kBwdKeys - 1) / kBwdKeys;
-  if (ATTN_BWD_PAIRS && D <= 128)
-    hipLaunchKernelGGL((bwd_dkdv2_kernel<D <= 128 ? D : 128>), dim3((unsigned)(nkb * a.B * a.Hkv)), dim3(512), 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)(nkb * a.B * a.Hkv)), dim3(256), 0, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+static hipError_t launch_dq(const BackwardArgs &a, hipStream_t s) {
   if (ATTN_BWD_DQ_PAIRS && D <= 128) {
     BackwardArgs a2 = a;
     a2.dq_hpw = a.G % 8 == 0 ? 8 : a.dq_hpw;   // query heads per workgroup: divides G and 8
@@ -1295,6 +1304,50 @@ static hipError_t launch_bwd_t(const BackwardArgs &a, hipStream_t s) {
   const long long nrb = (a.Lq + rows_wg - 1) / rows_wg;
   hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(nrb * (a.G / a.dq_hpw) * a.Hkv * a.B)), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_dkdv(const BackwardArgs &a, hipStream_t s) {
+  const long long nkb = (a.Lk + kBwdKeys - 1) / kBwdKeys;
+  if (ATTN_BWD_PAIRS && D <= 128)
+    hipLaunchKernelGGL((bwd_dkdv2_kernel<D <= 128 ? D : 128>), dim3((unsigned)(nkb * a.B * a.Hkv)), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)(nkb * a.B * a.Hkv)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_bwd_t(const BackwardArgs &a, hipStream_t s) {
+  const long long rows = (long long)a.B * a.Hq * a.Lq;
+  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int dev = -1;
+  if (!ATTN_BWD_SIDE || hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    if ((e = launch_dkdv<D>(a, s)) != hipSuccess) return e;
+    return launch_dq<D>(a, s);
+  }
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  SideStream &ss = g_side[dev];
+  if (ss.s == nullptr) {
+    SideStream n;
+    if ((e = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking)) == hipSuccess &&
+        (e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming)) == hipSuccess &&
+        (e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming)) == hipSuccess) {
+      ss = n;
+    } else {
+      if (n.fork) (void)hipEventDestroy(n.fork);
+      if (n.s) (void)hipStreamDestroy(n.s);
+      return e;
+    }
+  }
+  // fork after the pre-pass, whose row statistics the dq kernel reads
+  if ((e = hipEventRecord(ss.fork, s)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(ss.s, ss.fork, 0)) != hipSuccess) return e;
+  if ((e = launch_dq<D>(a, ss.s)) != hipSuccess) return e;
+  if ((e = hipEventRecord(ss.join, ss.s)) != hipSuccess) return e;
+  if ((e = launch_dkdv<D>(a, s)) != hipSuccess) return e;
+  return hipStreamWaitEvent(s, ss.join, 0);
 }
 
 int backward_dq_heads(int G) {

@@ -353,8 +353,13 @@ int attn_decode_waves(int B, int Hq, int Hkv, int Lmax, int D, int split_keys);
  * workspace: NULL (taken from HIP's stream-ordered allocator on `stream` and
  * released there) or at least attn_backward_workspace_bytes(B, Hq, Lq) bytes
  * of device memory (else ATTN_ERR_WORKSPACE), 256-byte aligned, not used by
- * other work until the call's kernels have finished.  Three kernels are
- * enqueued on `stream`; the call does not synchronise.
+ * other work until the call's kernels have finished.  The call does not
+ * synchronise: a pre-pass and the dk/dv kernel are enqueued on `stream`, and
+ * the dq kernel, which needs only the pre-pass, on a stream of the library's
+ * own (one per device, created on the first call) that waits for the
+ * pre-pass through an event; `stream` then waits for the dq kernel through a
+ * second event, so all of the call's work is ordered before whatever is
+ * enqueued on `stream` afterwards.
  */
 int attn_backward(const void *q, const void *k, const void *v, const void *out, const void *dout,
                   const float *lse, void *dq, void *dk, void *dv, int B, int Hq, int Hkv, int Lq, int Lk,
