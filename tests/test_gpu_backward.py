@@ -187,6 +187,29 @@ def test_backward_caller_workspace_and_determinism(attn):
 QWEN_BWD_4K = ai.PrefillCase("bwd_qwen3_8b_L4096", 69, B=1, Hq=32, Hkv=8, Lq=4096, Lk=4096, D=128)
 
 
+def test_backward_stream_order_and_two_streams(attn):
+    """The dq kernel runs on a stream of the library's own, forked from and joined back into the
+    caller's stream: work enqueued on the caller's stream right after the call (no host
+    synchronisation in between) sees the finished gradients, and calls on two streams at once give
+    the results of a call on its own."""
+    case = QWEN_BWD_4K
+    q, k, v, g = to_dev(case.q_bits()), to_dev(case.k_bits()), to_dev(case.v_bits()), to_dev(case.dout_bits())
+    out, lse = attn.prefill(q, k, v, causal=True, scale=case.scale)
+    ref = attn.backward(q, k, v, out, g, lse, causal=True, scale=case.scale)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(s1):
+        a = attn.backward(q, k, v, out, g, lse, causal=True, scale=case.scale)
+        ca = [x.clone() for x in a]
+    with torch.cuda.stream(s2):
+        b = attn.backward(q, k, v, out, g, lse, causal=True, scale=case.scale)
+        cb = [x.clone() for x in b]
+    torch.cuda.synchronize()
+    for name, x, y, z in zip(("dq", "dk", "dv"), ca, cb, ref):
+        assert torch.equal(x, z), name + " (first stream)"
+        assert torch.equal(y, z), name + " (second stream)"
+
+
 def test_backward_qwen_4k_sampled(attn):
     """Qwen3-8B heads at L = 4096, in the launch configuration the bench
     times, after the GPU forward: 24 query rows and 24 keys (first, last and
