@@ -39,8 +39,8 @@ FLUSH_BYTES = 512 << 20        # > the 256 MB Infinity Cache
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=10)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU seconds per oracle sample")
     p.add_argument("--all-configs", action="store_true",
