@@ -1004,9 +1004,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdQWaves<
 // group A (waves 0-3) runs G(j) and then dS(j), group B runs dS(j-1) and then
 // G(j), so the exponentials of one wave execute beside the MFMAs of its SIMD
 // neighbour (as in the forward's ping-pong).  K and V tiles sit in a ring of
-// four LDS stages (tile j-1 is still read by dQ in step j); the loads of tile
-// j+2 are issued at the start of step j.  Same products in the same order per
-// accumulator as bwd_dq_kernel (bit-identical).
+// four LDS stages (tile j-1 is still read by dQ in step j); group A's waves
+// load tile j+2 in step j, among their S / dP MFMAs.  Same products in the
+// same order per accumulator as bwd_dq_kernel (bit-identical).
 template <int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq2_kernel(BackwardArgs a) {
   constexpr int NW = 8;
