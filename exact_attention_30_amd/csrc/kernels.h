@@ -27,6 +27,7 @@ struct PrefillArgs {
   int nsplit;       // key ranges per query block (1: the kernel writes out and lse itself)
   float *part_o;    // nsplit > 1: [rows][nsplit][D] normalised partial outputs, rows = B * Hq * Lq
   float *part_lse;  // nsplit > 1: [rows][nsplit] partial log-sum-exps (-inf for an empty range)
+  int persist;      // > 0: the grid is this many resident workgroups, each taking several work items
 };
 
 struct DecodeArgs {
@@ -96,6 +97,9 @@ bool prefill_plan(PrefillArgs &a, int D);
 int prefill_tile_keys(int D);
 // Resident workgroups per CU of the prefill kernel for head dim D.
 hipError_t prefill_wgs_per_cu(int D, int *out);
+// whether the prefill kernel used for head dim D takes several work items per
+// workgroup (PrefillArgs::persist)
+bool prefill_can_persist(int D);
 // Largest key-split count the combine step supports.
 constexpr int kPrefillMaxSplits = 64;
 hipError_t launch_prefill(const PrefillArgs &a, int D, hipStream_t s);

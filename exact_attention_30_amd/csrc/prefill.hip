@@ -104,6 +104,17 @@
 #ifndef ATTN_PF_LAZYMAX
 #define ATTN_PF_LAZYMAX 1
 #endif
+//  ATTN_PF_PERSIST      prefill_kernel runs as one resident workgroup per slot,
+//                       each taking several work items, when the grid would
+//                       fill two or more rounds of the device
+#ifndef ATTN_PF_PERSIST
+#define ATTN_PF_PERSIST 1
+#endif
+//  ATTN_PF_PIPE         prefill_kernel issues its MFMA operand reads ahead in
+//                       explicit program order held by scheduling fences
+#ifndef ATTN_PF_PIPE
+#define ATTN_PF_PIPE 1
+#endif
 //  ATTN_PF_BK128        key-tile size for D = 128
 #ifndef ATTN_PF_BK128
 #define ATTN_PF_BK128 64
@@ -153,10 +164,35 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t vb1[C::TILE];
 
   // ---- which tile: XCD-grouped, heaviest q-block first -------------------
-  const int bid = blockIdx.x;
-  int t = bid;
+  // One work item per workgroup, or (a.persist > 0) a.persist resident
+  // workgroups that each take several: workgroup p runs on XCD p % 8 and
+  // takes that XCD's items (the same XCD-grouped, heaviest-first order) in
+  // rounds of a.persist / 8, alternately in increasing and decreasing order,
+  // so that the sizes of its items add up to about the same total in every
+  // workgroup.  The items left over by the grouping go one each to the first
+  // workgroups.
   const int tf = a.total & ~7;
-  if (bid < tf) t = (bid & 7) * (tf >> 3) + (bid >> 3);
+  const int per_x = tf >> 3, q8 = a.persist >> 3;
+  const int px = blockIdx.x & 7, pi = blockIdx.x >> 3;
+  bool tail_done = false;
+  for (int it = 0;; ++it) {
+  int t;
+  if (a.persist == 0) {
+    if (it > 0) break;
+    const int bid = blockIdx.x;
+    t = bid;
+    if (bid < tf) t = (bid & 7) * per_x + (bid >> 3);
+  } else {
+    const int kx = it * q8 + ((it & 1) ? q8 - 1 - pi : pi);
+    if (kx < per_x) {
+      t = px * per_x + kx;
+    } else if (!tail_done && (int)blockIdx.x < a.total - tf) {
+      t = tf + blockIdx.x;
+      tail_done = true;
+    } else {
+      break;
+    }
+  }
   const int sp = t % a.nsplit;  // key range of this workgroup
   t /= a.nsplit;
   int unit = t / a.n_qblk;
@@ -211,21 +247,28 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
   // the swizzle puts there.  Rows past the end of the keys are read from the
   // last row instead (the loads stay unconditional): such keys are masked,
   // so their K only meets -inf scores and their V only zero weights.
-  auto dma = [&](const uint16_t *g, uint16_t *dst, int j, auto is_v) __attribute__((always_inline)) {
-    constexpr bool V = decltype(is_v)::value;
 #if ATTN_DEVICE_PASS
-    // a buffer resource over the tile's rows that exist: the rows past the
-    // end of the keys read as zeros (they are masked); the tile base is
-    // scalar and a lane's offset fixed, so a load takes no vector work
-    const auto rs = buf_rsrc_uniform(g + (size_t)j * BK * D, (uint32_t)min(BK, a.Lk - j * BK) * (D * 2));
+  // a buffer resource over the rows of tile j that exist: the rows past the
+  // end of the keys read as zeros (they are masked); the tile base is scalar
+  // and a lane's offset fixed, so a load takes no vector work
+  auto tile_rs = [&](const uint16_t *g, int j) __attribute__((always_inline)) {
+    return buf_rsrc_uniform(g + (size_t)j * BK * D, (uint32_t)min(BK, a.Lk - j * BK) * (D * 2));
+  };
+  // the i-th of this wave's 2 DPW block loads of a tile
+  auto dma_one = [&](auto rs, uint16_t *dst, int i, auto is_v) __attribute__((always_inline)) {
+    constexpr bool V = decltype(is_v)::value;
+    const int blk = (wu % (C::NW / 2)) * 2 * C::DPW + i;
+    const int row = blk * C::RPD + lane / C::CPR;
+    const int c = (lane % C::CPR) ^ (V ? vswz<D>(row) : kswz<D>(row));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(dst + blk * 512), 16,
+                                             (lane / C::CPR) * (D * 2) + 16 * c, blk * 1024, 0, 0);
+  };
+#endif
+  auto dma = [&](const uint16_t *g, uint16_t *dst, int j, auto is_v) __attribute__((always_inline)) {
+#if ATTN_DEVICE_PASS
+    const auto rs = tile_rs(g, j);
 #pragma unroll
-    for (int i = 0; i < 2 * C::DPW; ++i) {
-      const int blk = (wu % (C::NW / 2)) * 2 * C::DPW + i;
-      const int row = blk * C::RPD + lane / C::CPR;
-      const int c = (lane % C::CPR) ^ (V ? vswz<D>(row) : kswz<D>(row));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(dst + blk * 512), 16,
-                                               (lane / C::CPR) * (D * 2) + 16 * c, blk * 1024, 0, 0);
-    }
+    for (int i = 0; i < 2 * C::DPW; ++i) dma_one(rs, dst, i, is_v);
 #endif
   };
 
@@ -266,18 +309,38 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
   // O^T += V^T P^T for one tile; the V^T operand comes from row-major V by
   // transposing reads
   auto pv = [&](const uint16_t *vs_) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < (D / 32) * (BK / 16); ++i) {
+    constexpr int N = (D / 32) * (BK / 16);
+    constexpr int A = ATTN_PF_PV_AHEAD;
+    auto vread = [&](int i) __attribute__((always_inline)) {
       const int db = i / (BK / 16), kb = i % (BK / 16);
       const uint16_t *vp = vs_ + 16 * kb * D + voff(db);
       const bf16x4 lo = lds_tr16(vp);
       const bf16x4 hi = lds_tr16(vp + 8 * D);
-      const bf16x8 vop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[kb], o[db], 0, 0, 0);
+      return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    if (ATTN_PF_PIPE) {
+      // operand reads A MFMAs ahead, in a ring of A + 1 register sets; the
+      // scheduling fences keep this order (left to itself the scheduler
+      // moved every read next to its MFMA, which then waited for it)
+      bf16x8 vr[A + 1];
+#pragma unroll
+      for (int i = 0; i < A && i < N; ++i) vr[i] = vread(i);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        if (i + A < N) vr[(i + A) % (A + 1)] = vread(i + A);
+        __builtin_amdgcn_sched_barrier(0);
+        const int db = i / (BK / 16), kb = i % (BK / 16);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[i % (A + 1)], pb[kb], o[db], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int db = i / (BK / 16), kb = i % (BK / 16);
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(i), pb[kb], o[db], 0, 0, 0);
     }
     // keep the transposing reads ATTN_PF_PV_AHEAD MFMAs ahead of their use
-    constexpr int N = (D / 32) * (BK / 16);
-    constexpr int A = ATTN_PF_PV_AHEAD;
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * A, 0);
 #pragma unroll
     for (int i = 0; i < N - A; ++i) {
@@ -415,18 +478,42 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
   // ahead), with the NLD direct loads of LOADS among them
   auto qk = [&](f32x16(&s)[BK / 32], const uint16_t *ks_, auto loads, auto nld) __attribute__((always_inline)) {
     constexpr int NLD = decltype(nld)::value;
-#pragma unroll
-    for (int rb = 0; rb < BK / 32; ++rb) s[rb] = f32x16{};
-#pragma unroll
-    for (int i = 0; i < (BK / 32) * (D / 16); ++i) {
-      const int rb = i / (D / 16), ks = i % (D / 16);
-      s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(ks_ + 32 * rb * D + koff(ks))), qf[ks], s[rb],
-                                                      0, 0, 0);
-    }
-    loads();
     constexpr int N = (BK / 32) * (D / 16);
     constexpr int A = ATTN_PF_QK_AHEAD;
     constexpr int SP = NLD > 0 && N / NLD > 0 ? N / NLD : 1;
+    auto kread = [&](int i) __attribute__((always_inline)) {
+      const int rb = i / (D / 16), ks = i % (D / 16);
+      return ld16(ks_ + 32 * rb * D + koff(ks));
+    };
+#pragma unroll
+    for (int rb = 0; rb < BK / 32; ++rb) s[rb] = f32x16{};
+    if (ATTN_PF_PIPE) {
+      // as in pv: reads A MFMAs ahead in a ring, the order held by fences;
+      // load i of LOADS follows MFMA i * SP
+      u32x4 kr[A + 1];
+#pragma unroll
+      for (int i = 0; i < A && i < N; ++i) kr[i] = kread(i);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        if (i + A < N) kr[(i + A) % (A + 1)] = kread(i + A);
+        __builtin_amdgcn_sched_barrier(0);
+        const int rb = i / (D / 16), ks = i % (D / 16);
+        s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[i % (A + 1)]), qf[ks], s[rb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (NLD > 0 && i % SP == 0 && i / SP < NLD) {
+          loads(i / SP);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int rb = i / (D / 16), ks = i % (D / 16);
+      s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kread(i)), qf[ks], s[rb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) loads(i);
     __builtin_amdgcn_sched_group_barrier(0x100, A, 0);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
@@ -468,16 +555,22 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
     uint16_t *knext = P ? kb0 : kb1;
     uint16_t *vprev = P ? vb0 : vb1;
     uint16_t *vcur = P ? vb1 : vb0;
-    auto none = []() __attribute__((always_inline)) {};
+    auto none = [](int) __attribute__((always_inline)) {};
     constexpr auto n0 = std::integral_constant<int, 0>{};
     if (grpA) {
       __builtin_amdgcn_s_setprio(1);
       // K(j+1) and V(j) among the QK MFMAs (past the last tile: a repeat of
       // it, never read)
-      gemm(j, kcur, vprev, [&]() __attribute__((always_inline)) {
-        dma(kg, knext, j0 + max(0, min(j + 1, nt - 1)), std::false_type{});
-        dma(vg, vcur, j0 + max(0, min(j, nt - 1)), std::true_type{});
+#if ATTN_DEVICE_PASS
+      const auto rk = tile_rs(kg, j0 + max(0, min(j + 1, nt - 1)));
+      const auto rv = tile_rs(vg, j0 + max(0, min(j, nt - 1)));
+      gemm(j, kcur, vprev, [&](int i) __attribute__((always_inline)) {
+        if (i < 2 * C::DPW) dma_one(rk, knext, i, std::false_type{});
+        else dma_one(rv, vcur, i - 2 * C::DPW, std::true_type{});
       }, std::integral_constant<int, 4 * C::DPW>{});
+#else
+      gemm(j, kcur, vprev, none, std::integral_constant<int, 4 * C::DPW>{});
+#endif
       __builtin_amdgcn_s_setprio(0);
       soft(j);
     } else {
@@ -535,6 +628,7 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
     }
     if (hh == 0) a.part_lse[row * a.nsplit + sp] = lt > 0.f ? m_run * ATTN_LN2 + __logf(lt) : -__builtin_inff();
   }
+  }  // work items
 }
 
 // In-wave pipelined variant.  Every wave runs the same schedule; per tile j
@@ -974,12 +1068,17 @@ static hipError_t launch_t(const PrefillArgs &a, hipStream_t s) {
   if (ATTN_PF_IW & (D == 64 ? 1 : D == 128 ? 2 : 4))
     hipLaunchKernelGGL((prefill_iw_kernel<D, BK>), dim3(a.total), dim3(PrefillCfg<D, BK>::NT), 0, s, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, BK>), dim3(a.total), dim3(PrefillCfg<D, BK>::NT), 0, s, a);
+    hipLaunchKernelGGL((prefill_kernel<D, BK>), dim3(a.persist > 0 ? a.persist : a.total),
+                       dim3(PrefillCfg<D, BK>::NT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   const long long rows = (long long)a.B * a.Hq * a.Lq;
   hipLaunchKernelGGL((prefill_combine_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a, rows);
   return hipGetLastError();
+}
+
+bool prefill_can_persist(int D) {
+  return ATTN_PF_PERSIST && !(ATTN_PF_IW & (D == 64 ? 1 : D == 128 ? 2 : 4));
 }
 
 int prefill_tile_keys(int D) { return D == 256 ? ATTN_PF_BK256 : (D == 128 ? ATTN_PF_BK128 : 64); }
