@@ -307,14 +307,6 @@ int prefill_setup(PrefillArgs *pa, int B, int Hq, int Hkv, int Lq, int Lk, int D
   }
   a.nsplit = ns;
   if (!attn::prefill_plan(a, D)) return ATTN_ERR_SHAPE;
-  if (ns == 1 && attn::prefill_can_persist(D)) {
-    // large grids: one resident workgroup per slot, several work items each
-    int cus = 0, occ = 0;
-    if (device_cus(&cus) != ATTN_OK) return ATTN_ERR_HIP;
-    if (attn::prefill_wgs_per_cu(D, &occ) != hipSuccess) return ATTN_ERR_HIP;
-    const long long slots = (long long)cus * (occ > 0 ? occ : 1);
-    if (slots % 8 == 0 && (long long)a.total >= 2 * slots) a.persist = (int)slots;
-  }
   return ATTN_OK;
 }
 
@@ -361,6 +353,14 @@ int run_prefill(const void *q, const void *k, const void *v, void *out, float *l
     char *base = static_cast<char *>(mem);
     a.part_lse = reinterpret_cast<float *>(base);
     a.part_o = reinterpret_cast<float *>(base + prefill_lse_bytes(a));
+  }
+  if (a.nsplit == 1 && attn::prefill_can_persist(D)) {
+    // large grids: one resident workgroup per slot, several work items each
+    int cus = 0, occ = 0;
+    if (device_cus(&cus) != ATTN_OK) return ATTN_ERR_HIP;
+    if (attn::prefill_wgs_per_cu(D, &occ) != hipSuccess) return ATTN_ERR_HIP;
+    const long long slots = (long long)cus * (occ > 0 ? occ : 1);
+    if (slots % 8 == 0 && (long long)a.total >= 2 * slots) a.persist = (int)slots;
   }
   hipError_t e = attn::launch_prefill(a, D, s);
   if (owned) {
