@@ -3,7 +3,10 @@
 One step = one causal prefill of a Qwen3-8B-shaped layer at 16,384 tokens
 (B=1, Hq=32, Hkv=8, D=128) followed by one ragged GQA decode over 64 cached
 sequences (lengths uniform in [1024, 32768], same heads).  Inputs are
-synthetic, seeded, and resident in HBM before timing starts.
+synthetic, seeded, and resident in HBM before timing starts.  Before the
+warmup steps, untimed steps run for at least --prewarm-ms of wall time: the
+device's clock takes about that long to settle, and the timed steps then see
+its steady state (the per-configuration records are taken the same way).
 
 Printed: one JSON line.  `value` is the prefill's causal TFLOP/s (FLOPs =
 4*B*Hq*D*visible (query, key) pairs of the bottom-right mask, divided by the
@@ -41,6 +44,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--prewarm-ms", type=float, default=150.0,
+                   help="untimed steps for at least this long before the warmup steps (the device's clock "
+                        "settles over its first ~100 ms of work)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU seconds per oracle sample")
     p.add_argument("--all-configs", action="store_true",
@@ -525,6 +531,14 @@ def main():
         if evs:
             evs[3].record(stream)
 
+    # untimed: steps for at least prewarm_ms of wall time, then the warmup steps
+    t_pre = time.perf_counter()
+    n_pre = 0
+    while (time.perf_counter() - t_pre) * 1e3 < args.prewarm_ms:
+        step(n_pre)
+        n_pre += 1
+        if n_pre % 8 == 0:
+            torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -551,6 +565,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prewarm_ms": args.prewarm_ms,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -58,10 +58,10 @@
 //  ATTN_PF_PV_AHEAD     V^T operand reads issued this many MFMAs ahead
 //  ATTN_PF_QK_AHEAD     K operand reads issued this many MFMAs ahead
 #ifndef ATTN_PF_PV_AHEAD
-#define ATTN_PF_PV_AHEAD 3
+#define ATTN_PF_PV_AHEAD 2
 #endif
 #ifndef ATTN_PF_QK_AHEAD
-#define ATTN_PF_QK_AHEAD 4
+#define ATTN_PF_QK_AHEAD 2
 #endif
 //  ATTN_PF_IW           head dims that use prefill_iw_kernel (in-wave pipelined)
 //                       rather than the two-group ping-pong prefill_kernel, as a
@@ -115,6 +115,17 @@
 #ifndef ATTN_PF_PIPE
 #define ATTN_PF_PIPE 1
 #endif
+//  ATTN_PF_PRIO         wave priority in prefill_kernel's phases: 1 = the matrix
+//                       phase raised, 2 = the softmax phase raised, 0 = neither
+#ifndef ATTN_PF_PRIO
+#define ATTN_PF_PRIO 1
+#endif
+//  ATTN_PF_ALT          prefill_kernel alternates the accumulators of consecutive
+//                       MFMAs (key blocks of S^T, value blocks of O^T); the
+//                       products into each accumulator keep their order
+#ifndef ATTN_PF_ALT
+#define ATTN_PF_ALT 1
+#endif
 //  ATTN_PF_BK128        key-tile size for D = 128
 #ifndef ATTN_PF_BK128
 #define ATTN_PF_BK128 64
@@ -132,6 +143,11 @@ namespace attn {
 #ifndef ATTN_PF_BK256
 #define ATTN_PF_BK256 64
 #endif
+
+// prefill_kernel's MFMA order: consecutive MFMAs into different accumulators
+constexpr bool kPfAlt = ATTN_PF_ALT != 0;
+constexpr int kPrioGemm = ATTN_PF_PRIO == 1 ? 1 : 0;
+constexpr int kPrioSoft = ATTN_PF_PRIO == 2 ? 1 : 0;
 
 template <int D>
 constexpr int kPfThreads = (D == 256 ? ATTN_PF_NW256 : 8) * 64;
@@ -312,7 +328,7 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
     constexpr int N = (D / 32) * (BK / 16);
     constexpr int A = ATTN_PF_PV_AHEAD;
     auto vread = [&](int i) __attribute__((always_inline)) {
-      const int db = i / (BK / 16), kb = i % (BK / 16);
+      const int db = kPfAlt ? i % (D / 32) : i / (BK / 16), kb = kPfAlt ? i / (D / 32) : i % (BK / 16);
       const uint16_t *vp = vs_ + 16 * kb * D + voff(db);
       const bf16x4 lo = lds_tr16(vp);
       const bf16x4 hi = lds_tr16(vp + 8 * D);
@@ -329,7 +345,7 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
       for (int i = 0; i < N; ++i) {
         if (i + A < N) vr[(i + A) % (A + 1)] = vread(i + A);
         __builtin_amdgcn_sched_barrier(0);
-        const int db = i / (BK / 16), kb = i % (BK / 16);
+        const int db = kPfAlt ? i % (D / 32) : i / (BK / 16), kb = kPfAlt ? i / (D / 32) : i % (BK / 16);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[i % (A + 1)], pb[kb], o[db], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -337,7 +353,7 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int db = i / (BK / 16), kb = i % (BK / 16);
+      const int db = kPfAlt ? i % (D / 32) : i / (BK / 16), kb = kPfAlt ? i / (D / 32) : i % (BK / 16);
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(i), pb[kb], o[db], 0, 0, 0);
     }
     // keep the transposing reads ATTN_PF_PV_AHEAD MFMAs ahead of their use
@@ -480,9 +496,9 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
     constexpr int NLD = decltype(nld)::value;
     constexpr int N = (BK / 32) * (D / 16);
     constexpr int A = ATTN_PF_QK_AHEAD;
-    constexpr int SP = NLD > 0 && N / NLD > 0 ? N / NLD : 1;
+    constexpr int SP = NLD > 0 && N / (NLD > 0 ? NLD : 1) > 0 ? N / (NLD > 0 ? NLD : 1) : 1;
     auto kread = [&](int i) __attribute__((always_inline)) {
-      const int rb = i / (D / 16), ks = i % (D / 16);
+      const int rb = kPfAlt ? i % (BK / 32) : i / (D / 16), ks = kPfAlt ? i / (BK / 32) : i % (D / 16);
       return ld16(ks_ + 32 * rb * D + koff(ks));
     };
 #pragma unroll
@@ -497,7 +513,7 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
       for (int i = 0; i < N; ++i) {
         if (i + A < N) kr[(i + A) % (A + 1)] = kread(i + A);
         __builtin_amdgcn_sched_barrier(0);
-        const int rb = i / (D / 16), ks = i % (D / 16);
+        const int rb = kPfAlt ? i % (BK / 32) : i / (D / 16), ks = kPfAlt ? i / (BK / 32) : i % (D / 16);
         s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[i % (A + 1)]), qf[ks], s[rb], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         if (NLD > 0 && i % SP == 0 && i / SP < NLD) {
@@ -509,7 +525,7 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int rb = i / (D / 16), ks = i % (D / 16);
+      const int rb = kPfAlt ? i % (BK / 32) : i / (D / 16), ks = kPfAlt ? i / (BK / 32) : i % (D / 16);
       s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kread(i)), qf[ks], s[rb], 0, 0, 0);
     }
 #pragma unroll
@@ -558,7 +574,7 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
     auto none = [](int) __attribute__((always_inline)) {};
     constexpr auto n0 = std::integral_constant<int, 0>{};
     if (grpA) {
-      __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_s_setprio(kPrioGemm);
       // K(j+1) and V(j) among the QK MFMAs (past the last tile: a repeat of
       // it, never read)
 #if ATTN_DEVICE_PASS
@@ -571,14 +587,15 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_kernel(PrefillArgs a) {
 #else
       gemm(j, kcur, vprev, none, std::integral_constant<int, 4 * C::DPW>{});
 #endif
-      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_s_setprio(kPrioSoft);
       soft(j);
     } else {
+      __builtin_amdgcn_s_setprio(kPrioSoft);
       soft(j - 1);
-      __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_s_setprio(kPrioGemm);
       gemm(j, kcur, vprev, none, n0);
-      __builtin_amdgcn_s_setprio(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     ATTN_WAIT_VMEM();
     __syncthreads();
   };
@@ -1063,9 +1080,14 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a, lon
   if (a.lse != nullptr && lane == 0) a.lse[row] = mx + __logf(den);
 }
 
+// whether head dim D runs on prefill_iw_kernel (else prefill_kernel); only
+// the kernel a head dim uses is instantiated
+template <int D>
+constexpr bool kUseIw = (ATTN_PF_IW & (D == 64 ? 1 : D == 128 ? 2 : 4)) != 0;
+
 template <int D, int BK>
 static hipError_t launch_t(const PrefillArgs &a, hipStream_t s) {
-  if (ATTN_PF_IW & (D == 64 ? 1 : D == 128 ? 2 : 4))
+  if constexpr (kUseIw<D>)
     hipLaunchKernelGGL((prefill_iw_kernel<D, BK>), dim3(a.total), dim3(PrefillCfg<D, BK>::NT), 0, s, a);
   else
     hipLaunchKernelGGL((prefill_kernel<D, BK>), dim3(a.persist > 0 ? a.persist : a.total),
@@ -1078,7 +1100,12 @@ static hipError_t launch_t(const PrefillArgs &a, hipStream_t s) {
 }
 
 bool prefill_can_persist(int D) {
-  return ATTN_PF_PERSIST && !(ATTN_PF_IW & (D == 64 ? 1 : D == 128 ? 2 : 4));
+  switch (D) {
+    case 64: return ATTN_PF_PERSIST && !kUseIw<64>;
+    case 128: return ATTN_PF_PERSIST && !kUseIw<128>;
+    case 256: return ATTN_PF_PERSIST && !kUseIw<256>;
+    default: return false;
+  }
 }
 
 int prefill_tile_keys(int D) { return D == 256 ? ATTN_PF_BK256 : (D == 128 ? ATTN_PF_BK128 : 64); }
@@ -1106,8 +1133,9 @@ bool prefill_plan(PrefillArgs &a, int D) {
 
 template <int D, int BK>
 static hipError_t wgs_per_cu_t(int *out) {
-  const void *f = (ATTN_PF_IW & (D == 64 ? 1 : D == 128 ? 2 : 4)) ? (const void *)&prefill_iw_kernel<D, BK>
-                                                                  : (const void *)&prefill_kernel<D, BK>;
+  const void *f;
+  if constexpr (kUseIw<D>) f = (const void *)&prefill_iw_kernel<D, BK>;
+  else f = (const void *)&prefill_kernel<D, BK>;
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, f, PrefillCfg<D, BK>::NT, 0);
 }
 
