@@ -126,6 +126,9 @@
 #ifndef ATTN_PF_ALT
 #define ATTN_PF_ALT 1
 #endif
+#ifndef ATTN_PF_IW_ALT
+#define ATTN_PF_IW_ALT 1
+#endif
 //  ATTN_PF_BK128        key-tile size for D = 128
 #ifndef ATTN_PF_BK128
 #define ATTN_PF_BK128 64
@@ -146,6 +149,8 @@ namespace attn {
 
 // prefill_kernel's MFMA order: consecutive MFMAs into different accumulators
 constexpr bool kPfAlt = ATTN_PF_ALT != 0;
+// the same for prefill_iw_kernel
+constexpr bool kIwAlt = ATTN_PF_IW_ALT != 0;
 constexpr int kPrioGemm = ATTN_PF_PRIO == 1 ? 1 : 0;
 constexpr int kPrioSoft = ATTN_PF_PRIO == 2 ? 1 : 0;
 
@@ -772,7 +777,7 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_iw_kernel(PrefillArgs a
     for (int rb = 0; rb < BK / 32; ++rb) s[rb] = f32x16{};
 #pragma unroll
     for (int i = 0; i < (BK / 32) * (D / 16); ++i) {
-      const int rb = i / (D / 16), ks = i % (D / 16);
+      const int rb = kIwAlt ? i % (BK / 32) : i / (D / 16), ks = kIwAlt ? i / (BK / 32) : i % (D / 16);
       s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(ks_ + 32 * rb * D + koff(ks))), qf[ks], s[rb],
                                                       0, 0, 0);
     }
@@ -780,7 +785,7 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_iw_kernel(PrefillArgs a
   auto pv_ops = [&](const uint16_t *vs_) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < (D / 32) * (BK / 16); ++i) {
-      const int db = i / (BK / 16), kb = i % (BK / 16);
+      const int db = kIwAlt ? i % (D / 32) : i / (BK / 16), kb = kIwAlt ? i / (D / 32) : i % (BK / 16);
       const uint16_t *vp = vs_ + 16 * kb * D + voff(db);
       const bf16x4 lo = lds_tr16(vp);
       const bf16x4 hi = lds_tr16(vp + 8 * D);
