@@ -138,6 +138,42 @@ def test_prefill_gsweep_sampled(attn, G):
     run_sampled(attn, ai.gsweep_prefill(G))
 
 
+# Grids of two or more device rounds run on resident workgroups that each take
+# several work items (32-row query blocks here: G = 8 packs one head per wave).
+# 514 and 513 items are not multiples of the 8 XCDs, so the leftover items go
+# one each to the first workgroups; one row of every item is checked (causal)
+# or every row (full attention over a short key range).
+RESIDENT_CASES = [
+    ai.PrefillCase("resident_causal_G8_L16432_D128", 75, B=1, Hq=8, Hkv=1, Lq=16432, Lk=16432, D=128),
+    ai.PrefillCase("resident_full_G8_Lq16400_Lk300_D128", 76, B=1, Hq=8, Hkv=1, Lq=16400, Lk=300, D=128,
+                   causal=False),
+]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("case", RESIDENT_CASES, ids=lambda c: c.name)
+def test_prefill_resident_workgroups_leftover_items(attn, case):
+    assert attn.prefill_splits(case.B, case.Hq, case.Hkv, case.Lq, case.Lk, case.D, case.causal, 0) == 1
+    d = PrefillData(case)
+    out, lse = attn.prefill(d.q, d.k, d.v, causal=case.causal, scale=case.scale)
+    torch.cuda.synchronize()
+    q, k, v = d.f64()
+    go, gl = to_np(out), to_np(lse)
+    if not case.causal:
+        ro, rl = oracle.attention(q, k, v, False, case.scale)
+        check_out(go, ro, case.name)
+        check_lse(gl, rl, case.name)
+        return
+    nblk = (case.Lq + 31) // 32
+    rows1 = np.minimum(np.arange(nblk) * 32 + np.arange(nblk) % 32, case.Lq - 1)
+    rows = np.broadcast_to(rows1, (case.B, case.Hq, nblk))
+    ro, rl = oracle.attention_rows(q, k, v, rows, True, case.scale)
+    bi = np.arange(case.B)[:, None, None]
+    hi = np.arange(case.Hq)[None, :, None]
+    check_out(go[bi, hi, rows], ro, case.name)
+    check_lse(gl[bi, hi, rows], rl, case.name)
+
+
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_prefill_scale_zero_closed_form(attn, D):
     # zero scores: lse_i = ln(#visible keys) and out_i = mean of the visible V rows
