@@ -150,6 +150,20 @@ ATTN_DEV void sched_interleave() {
 #ifndef ATTN_BWD_TR_AHEAD
 #define ATTN_BWD_TR_AHEAD 4
 #endif
+//  ATTN_BWD_XPIPE256   bwd_dkdv_kernel at D = 256: the S and dP MFMAs take their
+//                      operand reads ATTN_BWD_XAHEAD MFMAs ahead, in explicit
+//                      program order held by scheduling fences (the scheduler had
+//                      put every read right before its MFMA); the same for the
+//                      dV/dK products spills 16 registers, so those stay as they are
+#ifndef ATTN_BWD_XPIPE256
+#define ATTN_BWD_XPIPE256 1
+#endif
+#ifndef ATTN_BWD_XAHEAD
+#define ATTN_BWD_XAHEAD 2
+#endif
+template <int D>
+constexpr bool kBwdXPipeS = D == 256 && ATTN_BWD_XPIPE256 != 0;
+constexpr int kBwdXAhead = ATTN_BWD_XAHEAD;
 // D = 256 leaves fewer registers for reads in flight
 template <int D>
 constexpr int kQkAhead = D == 256 ? 2 : ATTN_BWD_QK_AHEAD;
@@ -273,19 +287,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   // per-lane LDS offsets: b128 operand (row ql, chunk 2 ks + hh) and the
   // transposed operand (rows 4 hh + (j16 >> 2) [+8], 4 columns at
   // 32 db + 16 (g16 & 1) + 4 (j16 & 3)); a 16-row step adds 16 D.
-  int roff[D / 16];
+  // the swizzle touches only the low 4 bits of a chunk index, so from 16
+  // chunks on the offsets repeat 128 elements further: 8 (and 4 + 4) of them
+  // are kept, the rest is an immediate offset of the read
+  constexpr int NRO = D / 16 < 8 ? D / 16 : 8, NTO = D / 32 < 4 ? D / 32 : 4;
+  int roff8[NRO];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) roff[ks] = toff<D>(ql, 2 * ks + hh);
-  int tlo[D / 32], thi[D / 32];
+  for (int ks = 0; ks < NRO; ++ks) roff8[ks] = toff<D>(ql, 2 * ks + hh);
+  int tlo4[NTO], thi4[NTO];
   {
     const int r = 4 * hh + (j16 >> 2);
     const int c = 2 * (g16 & 1) + ((j16 & 3) >> 1);
 #pragma unroll
-    for (int dd = 0; dd < D / 32; ++dd) {
-      tlo[dd] = toff<D>(r, 4 * dd + c) + 4 * (j16 & 1);
-      thi[dd] = toff<D>(r + 8, 4 * dd + c) + 4 * (j16 & 1);
+    for (int dd = 0; dd < NTO; ++dd) {
+      tlo4[dd] = toff<D>(r, 4 * dd + c) + 4 * (j16 & 1);
+      thi4[dd] = toff<D>(r + 8, 4 * dd + c) + 4 * (j16 & 1);
     }
   }
+  auto roff = [&](int ks) __attribute__((always_inline)) { return roff8[ks % NRO] + (ks / NRO) * 128; };
+  auto tlo = [&](int dd) __attribute__((always_inline)) { return tlo4[dd % NTO] + (dd / NTO) * 128; };
+  auto thi = [&](int dd) __attribute__((always_inline)) { return thi4[dd % NTO] + (dd / NTO) * 128; };
 
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
@@ -345,10 +366,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
   auto sdp = [&](const uint16_t *qt, const uint16_t *dt, f32x16 &s, f32x16 &dp) __attribute__((always_inline)) {
     s = f32x16{};
     dp = f32x16{};
+    if constexpr (kBwdXPipeS<D>) {
+      // operand reads A MFMAs ahead in a ring of A + 1, S and dP alternating
+      constexpr int N = 2 * (D / 16), A = kBwdXAhead;
+      auto rd = [&](int i) __attribute__((always_inline)) { return ld16((i & 1 ? dt : qt) + roff(i >> 1)); };
+      u32x4 r[A + 1];
+#pragma unroll
+      for (int i = 0; i < A; ++i) r[i] = rd(i);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        if (i + A < N) r[(i + A) % (A + 1)] = rd(i + A);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i & 1) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(r[i % (A + 1)]), vf[i >> 1], dp, 0, 0, 0);
+        else s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(r[i % (A + 1)]), kf[i >> 1], s, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return;
+    }
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(qt + roff[ks])), kf[ks], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(dt + roff[ks])), vf[ks], dp, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(qt + roff(ks))), kf[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(dt + roff(ks))), vf[ks], dp, 0, 0, 0);
     }
   };
   // p and ds of one half as bf16 B operands; this lane: key column `key`,
@@ -385,9 +423,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void b
 #pragma unroll
       for (int qh = 0; qh < 2; ++qh) {
         dv[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            tr_operand(dt + 16 * qh * D + tlo[dd], dt + 16 * qh * D + thi[dd]), pb[qh], dv[dd], 0, 0, 0);
+            tr_operand(dt + 16 * qh * D + tlo(dd), dt + 16 * qh * D + thi(dd)), pb[qh], dv[dd], 0, 0, 0);
         dk[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            tr_operand(qt + 16 * qh * D + tlo[dd], qt + 16 * qh * D + thi[dd]), sb[qh], dk[dd], 0, 0, 0);
+            tr_operand(qt + 16 * qh * D + tlo(dd), qt + 16 * qh * D + thi(dd)), sb[qh], dk[dd], 0, 0, 0);
       }
     }
   };
@@ -1163,7 +1201,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
     loads();
     constexpr int N = 2 * (D / 16);
     constexpr int AH = kQkAhead<D>;
-    constexpr int SP = NLD > 0 && N / NLD > 0 ? N / NLD : 1;
+    constexpr int SP = NLD > 0 && N / (NLD > 0 ? NLD : 1) > 0 ? N / (NLD > 0 ? NLD : 1) : 1;
     __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
