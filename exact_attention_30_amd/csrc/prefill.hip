@@ -104,11 +104,12 @@
 #ifndef ATTN_PF_LAZYMAX
 #define ATTN_PF_LAZYMAX 1
 #endif
-//  ATTN_PF_PERSIST      prefill_kernel runs as one resident workgroup per slot,
-//                       each taking several work items, when the grid would
-//                       fill two or more rounds of the device
+//  ATTN_PF_PERSIST      head dims (bit mask as for ATTN_PF_IW) whose prefill runs
+//                       as one resident workgroup per slot, each taking several
+//                       work items, when the grid would fill two or more rounds
+//                       of the device
 #ifndef ATTN_PF_PERSIST
-#define ATTN_PF_PERSIST 1
+#define ATTN_PF_PERSIST 3
 #endif
 //  ATTN_PF_PIPE         prefill_kernel issues its MFMA operand reads ahead in
 //                       explicit program order held by scheduling fences
@@ -147,6 +148,11 @@ namespace attn {
 #define ATTN_PF_BK256 64
 #endif
 
+// whether head dim D runs on resident workgroups (ATTN_PF_PERSIST); the
+// one-item form of prefill_iw_kernel is kept straight-line for the others
+// (at D = 256 the item loop costs registers: 29 SGPRs spilled, -30%)
+template <int D>
+constexpr bool kPersist = (ATTN_PF_PERSIST & (D == 64 ? 1 : D == 128 ? 2 : 4)) != 0;
 // prefill_kernel's MFMA order: consecutive MFMAs into different accumulators
 constexpr bool kPfAlt = ATTN_PF_ALT != 0;
 // the same for prefill_iw_kernel
@@ -671,11 +677,11 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_iw_kernel(PrefillArgs a
   __shared__ __attribute__((aligned(1024))) uint16_t vb0[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t vb1[C::TILE];
 
-  // ---- which tile: XCD-grouped, heaviest q-block first -------------------
-  const int bid = blockIdx.x;
-  int t = bid;
+  // ---- which tile: XCD-grouped, heaviest q-block first; one work item per
+  // workgroup or, for head dims built with resident workgroups and
+  // a.persist > 0, several per workgroup (as in prefill_kernel) ------------
   const int tf = a.total & ~7;
-  if (bid < tf) t = (bid & 7) * (tf >> 3) + (bid >> 3);
+  auto item = [&](int t) __attribute__((always_inline)) {
   const int sp = t % a.nsplit;
   t /= a.nsplit;
   int unit = t / a.n_qblk;
@@ -1026,6 +1032,35 @@ __global__ __launch_bounds__(kPfThreads<D>) void prefill_iw_kernel(PrefillArgs a
     }
     if (hh == 0) a.part_lse[row * a.nsplit + sp] = lt > 0.f ? m_run * ATTN_LN2 + __logf(lt) : -__builtin_inff();
   }
+  };
+  if constexpr (kPersist<D>) {
+    const int per_x = tf >> 3, q8 = a.persist >> 3;
+    const int px = blockIdx.x & 7, pi = blockIdx.x >> 3;
+    bool tail_done = false;
+    for (int it = 0;; ++it) {
+      int t;
+      if (a.persist == 0) {
+        if (it > 0) break;
+        t = blockIdx.x;
+        if (t < tf) t = (t & 7) * per_x + (t >> 3);
+      } else {
+        const int kx = it * q8 + ((it & 1) ? q8 - 1 - pi : pi);
+        if (kx < per_x) {
+          t = px * per_x + kx;
+        } else if (!tail_done && (int)blockIdx.x < a.total - tf) {
+          t = tf + blockIdx.x;
+          tail_done = true;
+        } else {
+          break;
+        }
+      }
+      item(t);
+    }
+  } else {
+    int t = blockIdx.x;
+    if (t < tf) t = (t & 7) * (tf >> 3) + (t >> 3);
+    item(t);
+  }
 }
 
 // Merge of the key ranges of one query row (one wave per row, nsplit <= 64):
@@ -1093,7 +1128,8 @@ constexpr bool kUseIw = (ATTN_PF_IW & (D == 64 ? 1 : D == 128 ? 2 : 4)) != 0;
 template <int D, int BK>
 static hipError_t launch_t(const PrefillArgs &a, hipStream_t s) {
   if constexpr (kUseIw<D>)
-    hipLaunchKernelGGL((prefill_iw_kernel<D, BK>), dim3(a.total), dim3(PrefillCfg<D, BK>::NT), 0, s, a);
+    hipLaunchKernelGGL((prefill_iw_kernel<D, BK>), dim3(a.persist > 0 ? a.persist : a.total),
+                       dim3(PrefillCfg<D, BK>::NT), 0, s, a);
   else
     hipLaunchKernelGGL((prefill_kernel<D, BK>), dim3(a.persist > 0 ? a.persist : a.total),
                        dim3(PrefillCfg<D, BK>::NT), 0, s, a);
@@ -1106,9 +1142,9 @@ static hipError_t launch_t(const PrefillArgs &a, hipStream_t s) {
 
 bool prefill_can_persist(int D) {
   switch (D) {
-    case 64: return ATTN_PF_PERSIST && !kUseIw<64>;
-    case 128: return ATTN_PF_PERSIST && !kUseIw<128>;
-    case 256: return ATTN_PF_PERSIST && !kUseIw<256>;
+    case 64: return kPersist<64>;
+    case 128: return kPersist<128>;
+    case 256: return kPersist<256>;
     default: return false;
   }
 }

@@ -139,7 +139,8 @@ def test_prefill_gsweep_sampled(attn, G):
 
 
 # Grids of two or more device rounds run on resident workgroups that each take
-# several work items (32-row query blocks here: G = 8 packs one head per wave).
+# several work items (32-row query blocks here: G = 8 packs one head per wave;
+# D = 128 on the two-group kernel, D = 64 on the in-wave kernel).
 # 514 and 513 items are not multiples of the 8 XCDs, so the leftover items go
 # one each to the first workgroups; one row of every item is checked (causal)
 # or every row (full attention over a short key range).
@@ -147,6 +148,7 @@ RESIDENT_CASES = [
     ai.PrefillCase("resident_causal_G8_L16432_D128", 75, B=1, Hq=8, Hkv=1, Lq=16432, Lk=16432, D=128),
     ai.PrefillCase("resident_full_G8_Lq16400_Lk300_D128", 76, B=1, Hq=8, Hkv=1, Lq=16400, Lk=300, D=128,
                    causal=False),
+    ai.PrefillCase("resident_causal_G8_L16432_D64", 77, B=1, Hq=8, Hkv=1, Lq=16432, Lk=16432, D=64),
 ]
 
 
