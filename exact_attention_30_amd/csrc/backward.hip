@@ -655,11 +655,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
       r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(xt + roff[ks])), kvf[ks], r, 0, 0, 0);
   };
   // acc^T += X^T Y (k = the half's 32 rows), X^T read transposed from LDS
+  // (the half's two 16-row steps outermost, so that consecutive MFMAs go to
+  // different accumulators; each accumulator keeps its order)
   auto colprod = [&](const uint16_t *xt, const bf16x8(&y)[2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int dd = 0; dd < D / 32; ++dd)
+    for (int qh = 0; qh < 2; ++qh)
 #pragma unroll
-      for (int qh = 0; qh < 2; ++qh)
+      for (int dd = 0; dd < D / 32; ++dd)
         acc[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             tr_operand(xt + 16 * qh * D + tlo[dd], xt + 16 * qh * D + thi[dd]), y[qh], acc[dd], 0, 0, 0);
   };
@@ -1179,9 +1181,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   // dQ^T += K^T dS^T of the tile in stage kp (K^T read transposed)
   auto dq_part = [&](const uint16_t *kp, const bf16x8(&sb)[2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int dd = 0; dd < D / 32; ++dd)
+    for (int kc2 = 0; kc2 < BK / 16; ++kc2)
 #pragma unroll
-      for (int kc2 = 0; kc2 < BK / 16; ++kc2)
+      for (int dd = 0; dd < D / 32; ++dd)
         dq[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             tr_operand(kp + 16 * kc2 * D + tlo[dd], kp + 16 * kc2 * D + thi[dd]), sb[kc2], dq[dd], 0, 0, 0);
     sched_reads_ahead<(D / 32) * (BK / 16), 2, kTrAhead<D>>();
